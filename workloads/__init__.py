@@ -1,0 +1,10 @@
+"""Seeded synthetic workloads shared by the tests, the benchmark and the smoke check.
+
+This package holds no step of the attention method: it only names the
+problem shapes and draws random inputs.  Both the HIP path and the CPU oracle
+consume what it returns.
+"""
+from .configs import CONFIGS, Config, SWEEP_SHAPES
+from .gen import Inputs, make_inputs
+
+__all__ = ["CONFIGS", "Config", "SWEEP_SHAPES", "Inputs", "make_inputs"]
