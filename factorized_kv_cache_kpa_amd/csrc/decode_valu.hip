@@ -1,0 +1,203 @@
+// General-shape split-KV decode on the vector ALUs (any split/rank within the
+// kpa.h limits, float32 or bfloat16 factors, one or many queries).  Used for
+// float32 caches, for the TPA-degenerate split and for shapes the matrix-core
+// kernels do not cover.
+//
+// Per (chunk of the cache, query, sequence) one workgroup:
+//   1. rotates the query with R_KPA(q_pos) and folds in log2(e)/(R_K sqrt(d_h))
+//      ([KPA] Def. 2.3, §2.3);
+//   2. per 32-slot tile, scores every (head, slot) in factor space: the query
+//      is contracted with B~^K over j2, then with A^K over j1 and summed over
+//      the rank ([KPA] Prop. 2.2 / Eq. (6) with a dense query);
+//   3. keeps an online softmax per head (running max and sum, rescaling the
+//      accumulators when the max grows -- the blocked online log-sum-exp of
+//      FlashTPA decoding, "Tensor Product Attention Is All You Need" summary
+//      page);
+//   4. accumulates sum_s p_s v_{s,i} with v rebuilt element by element from
+//      A^V, B^V ([KPA] Eq. (4)); K and V are never stored;
+//   5. writes either the final output or a partial (m, l, o) for the merge.
+// [KPA] = "Kronecker Product Attention: Memory-Efficient KV Compression via
+// Structured Factorization".
+#include "kpa_common.hpp"
+
+namespace kpa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxPerThread = KPA_MAX_HD / kThreads;  // output elements per thread
+
+template <bool kF32>
+__device__ __forceinline__ float load_factor(const uint8_t* p) {
+    if constexpr (kF32) return *reinterpret_cast<const float*>(p);
+    else return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+}
+
+template <bool kF32>
+__global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P) {
+    extern __shared__ float smem[];
+    const kpa_dims& d = P.d;
+    const Layout& L = P.L;
+    const int h = d.p1 * d.p2, dh = d.q1 * d.q2;
+    const int split = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+
+    float* qr = smem;                      // [h][dh] rotated, scaled query
+    float* zs = qr + h * dh;               // [h][32] scores, then probabilities
+    float* m_run = zs + h * kTileSlots;    // [h] running max (log2 units)
+    float* l_run = m_run + h;              // [h] running sum
+    float* alpha = l_run + h;              // [h] rescale factor of this tile
+    float* cs = alpha + h;                 // [q2/2][2] cos, sin
+
+    const int vis = visible_slots(P, b, n);
+    const int first = split * P.chunk_tiles * kTileSlots;
+    int last = first + P.chunk_tiles * kTileSlots;
+    if (last > vis) last = vis;
+
+    // 1. rotate the query ---------------------------------------------------
+    const int qp = P.q_pos[(int64_t)b * P.n_q + n];
+    const int half = d.q2 / 2;
+    if (tid < half) {
+        const double theta = exp2(-(2.0 * tid / d.q2) * log2((double)d.rope_base));
+        double sn, c;
+        sincos((double)qp * theta, &sn, &c);
+        cs[2 * tid] = (float)c;
+        cs[2 * tid + 1] = (float)sn;
+    }
+    for (int i = tid; i < h; i += kThreads) {
+        m_run[i] = -INFINITY;
+        l_run[i] = 0.f;
+    }
+    __syncthreads();
+    const float* qg = P.q + ((int64_t)b * P.n_q + n) * h * dh;
+    for (int pr = tid; pr < h * dh / 2; pr += kThreads) {
+        const int e = 2 * pr;
+        const int m = (e % d.q2) / 2;
+        const float x0 = qg[e], x1 = qg[e + 1];
+        const float c = cs[2 * m], sn = cs[2 * m + 1];
+        qr[e] = (x0 * c - x1 * sn) * P.q_scale;
+        qr[e + 1] = (x0 * sn + x1 * c) * P.q_scale;
+    }
+
+    float acc[kMaxPerThread];
+#pragma unroll
+    for (int k = 0; k < kMaxPerThread; ++k) acc[k] = 0.f;
+    __syncthreads();
+
+    const uint8_t* seq_base = P.cache + (int64_t)b * L.n_tiles * L.tile_bytes;
+    const int es = L.elem_bytes;
+    for (int s0 = first; s0 < last; s0 += kTileSlots) {
+        const uint8_t* tile = seq_base + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
+        const int valid = (last - s0) < kTileSlots ? (last - s0) : kTileSlots;
+
+        // 2. factor-space scores for every (head, slot) -------------------------
+        for (int pi = tid; pi < h * kTileSlots; pi += kThreads) {
+            const int i = pi / kTileSlots, t = pi % kTileSlots;
+            float z = -INFINITY;
+            if (t < valid) {
+                const int i1 = i / d.p2, i2 = i % d.p2;
+                const float* qi = qr + i * dh;
+                z = 0.f;
+                for (int r = 0; r < d.r_k; ++r) {
+                    const int bk_row = (r * d.p2 + i2) * d.q2;
+                    const int ak_row = (r * d.p1 + i1) * d.q1;
+                    for (int j1 = 0; j1 < d.q1; ++j1) {
+                        float w = 0.f;  // sum_j2 q'[i, j1, j2] B~^K_r[i2, j2]
+                        for (int j2 = 0; j2 < d.q2; ++j2)
+                            w += qi[j1 * d.q2 + j2] * load_factor<kF32>(tile + elem_offset(L, 1, bk_row + j2, t));
+                        z += load_factor<kF32>(tile + elem_offset(L, 0, ak_row + j1, t)) * w;
+                    }
+                }
+            }
+            zs[i * kTileSlots + t] = z;
+        }
+        __syncthreads();
+
+        // 3. online softmax per head ---------------------------------------------
+        for (int i = tid; i < h; i += kThreads) {
+            float* zi = zs + i * kTileSlots;
+            float mx = -INFINITY;
+            for (int t = 0; t < kTileSlots; ++t) mx = fmaxf(mx, zi[t]);
+            const float m_old = m_run[i];
+            const float m_new = fmaxf(m_old, mx);
+            const float a = (m_new == -INFINITY) ? 1.f : exp2f(m_old - m_new);
+            float sum = 0.f;
+            for (int t = 0; t < kTileSlots; ++t) {
+                const float p = (zi[t] == -INFINITY) ? 0.f : exp2f(zi[t] - m_new);
+                zi[t] = p;
+                sum += p;
+            }
+            alpha[i] = a;
+            m_run[i] = m_new;
+            l_run[i] = l_run[i] * a + sum;
+        }
+        __syncthreads();
+
+        // 4. value accumulation in factor space ---------------------------------
+#pragma unroll
+        for (int k = 0; k < kMaxPerThread; ++k) {
+            const int o = tid + k * kThreads;
+            if (o < h * dh) {
+                const int i = o / dh, j = o % dh;
+                const int i1 = i / d.p2, i2 = i % d.p2;
+                const int j1 = j / d.q2, j2 = j % d.q2;
+                const float* pi = zs + i * kTileSlots;
+                float sum = 0.f;
+                for (int r = 0; r < d.r_v; ++r) {
+                    const uint8_t* av = tile + elem_offset(L, 2, (r * d.p1 + i1) * d.q1 + j1, 0);
+                    const uint8_t* bv = tile + elem_offset(L, 3, (r * d.p2 + i2) * d.q2 + j2, 0);
+                    for (int t = 0; t < valid; ++t)
+                        sum += pi[t] * load_factor<kF32>(av + t * es) * load_factor<kF32>(bv + t * es);
+                }
+                acc[k] = acc[k] * alpha[i] + sum;
+            }
+        }
+        __syncthreads();
+    }
+
+    // 5. write out -------------------------------------------------------------
+    const int64_t row = ((int64_t)b * P.n_q + n);
+    if (P.n_split == 1) {
+#pragma unroll
+        for (int k = 0; k < kMaxPerThread; ++k) {
+            const int o = tid + k * kThreads;
+            if (o < h * dh) {
+                const int i = o / dh;
+                const float l = l_run[i];
+                P.out[row * h * dh + o] = l > 0.f ? acc[k] * P.v_scale / l : 0.f;
+            }
+        }
+        if (P.lse)
+            for (int i = tid; i < h; i += kThreads)
+                P.lse[row * h + i] = l_run[i] > 0.f ? (m_run[i] + log2f(l_run[i])) * 0.69314718055994531f : -INFINITY;
+    } else {
+        const int64_t prow = row * P.n_split + split;
+#pragma unroll
+        for (int k = 0; k < kMaxPerThread; ++k) {
+            const int o = tid + k * kThreads;
+            if (o < h * dh) P.part_o[prow * h * dh + o] = acc[k] * P.v_scale;
+        }
+        for (int i = tid; i < h; i += kThreads) {
+            P.part_ml[(prow * h + i) * 2] = m_run[i];
+            P.part_ml[(prow * h + i) * 2 + 1] = l_run[i];
+        }
+    }
+}
+
+}  // namespace
+
+size_t decode_valu_smem(const kpa_dims& d) {
+    const int h = d.p1 * d.p2, dh = d.q1 * d.q2;
+    return sizeof(float) * ((size_t)h * dh + (size_t)h * kTileSlots + 3 * (size_t)h + d.q2);
+}
+
+hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s) {
+    dim3 grid(P.n_split, P.n_q, P.batch);
+    const size_t smem = decode_valu_smem(P.d);
+    if (P.d.dtype == KPA_F32)
+        hipLaunchKernelGGL(decode_valu_kernel<true>, grid, dim3(kThreads), smem, s, P);
+    else
+        hipLaunchKernelGGL(decode_valu_kernel<false>, grid, dim3(kThreads), smem, s, P);
+    return hipGetLastError();
+}
+
+}  // namespace kpa

@@ -1,0 +1,206 @@
+// libkpa C ABI: argument checks, split-KV planning and kernel dispatch.
+// Declarations and the contract of every entry point are in include/kpa.h.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "kpa_common.hpp"
+#include "kpa_dispatch.hpp"
+
+using namespace kpa;
+
+namespace {
+
+bool dims_ok(const kpa_dims* d) {
+    if (d->p1 <= 0 || d->p2 <= 0 || d->q1 <= 0 || d->q2 <= 0 || d->r_k <= 0 || d->r_v <= 0) return false;
+    if (d->q2 % 2) return false;
+    const int64_t h = (int64_t)d->p1 * d->p2, dh = (int64_t)d->q1 * d->q2;
+    if (h > KPA_MAX_HEADS || dh > KPA_MAX_HEAD_DIM || h * dh > KPA_MAX_HD) return false;
+    if (d->r_k > KPA_MAX_RANK || d->r_v > KPA_MAX_RANK) return false;
+    if (!(d->rope_base > 0.f) || !isfinite(d->rope_base)) return false;
+    return true;
+}
+
+int check_dims(const kpa_dims* d) {
+    if (!d) return KPA_ERR_NULL_PTR;
+    if (d->dtype != KPA_F32 && d->dtype != KPA_BF16) return KPA_ERR_DTYPE;
+    if (!dims_ok(d)) return KPA_ERR_INVALID_DIMS;
+    return KPA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Compute units of the current device, looked up once per device.
+int num_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+int check_decode_args(const kpa_dims* d, int32_t batch, int32_t capacity, int32_t max_ctx, int32_t n_q) {
+    int st = check_dims(d);
+    if (st != KPA_OK) return st;
+    if (batch < 0 || capacity < 0 || max_ctx < 0 || max_ctx > capacity) return KPA_ERR_INVALID_ARG;
+    if (n_q < 1 || n_q > KPA_MAX_NQ) return KPA_ERR_INVALID_ARG;
+    if ((int64_t)batch * n_q > 65535) return KPA_ERR_INVALID_ARG;
+    return KPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kpa_cache_layout(const kpa_dims* dims, int32_t batch, int32_t capacity, kpa_layout_info* out) {
+    int st = check_dims(dims);
+    if (st != KPA_OK) return st;
+    if (!out) return KPA_ERR_NULL_PTR;
+    if (batch < 0 || capacity < 0) return KPA_ERR_INVALID_ARG;
+    Layout L = make_layout(*dims, batch, capacity);
+    out->version = KPA_LAYOUT_VERSION;
+    out->tile_slots = kTileSlots;
+    out->elem_bytes = L.elem_bytes;
+    out->n_tiles = L.n_tiles;
+    out->tile_bytes = L.tile_bytes;
+    for (int c = 0; c < 4; ++c) {
+        out->comp_offset[c] = L.off[c];
+        out->comp_elems[c] = L.elems[c];
+    }
+    out->positions_offset = L.positions_off;
+    out->total_bytes = L.total_bytes;
+    return KPA_OK;
+}
+
+size_t kpa_cache_bytes(const kpa_dims* dims, int32_t batch, int32_t capacity) {
+    kpa_layout_info info;
+    if (kpa_cache_layout(dims, batch, capacity, &info) != KPA_OK) return 0;
+    return (size_t)info.total_bytes;
+}
+
+int kpa_cache_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t capacity,
+                     const void* a_k, const void* b_k, const void* a_v, const void* b_v,
+                     const int32_t* positions, const int32_t* slot0, int32_t n_new,
+                     uint32_t* dev_status, void* stream) {
+    int st = check_dims(dims);
+    if (st != KPA_OK) return st;
+    if (batch < 0 || capacity < 0 || n_new < 0 || batch > 65535) return KPA_ERR_INVALID_ARG;
+    if (batch == 0 || n_new == 0) return KPA_OK;
+    if (!cache || !a_k || !b_k || !a_v || !b_v || !positions || !slot0) return KPA_ERR_NULL_PTR;
+    if (!aligned(cache, 16)) return KPA_ERR_INVALID_ARG;
+    AppendParams P{};
+    P.d = *dims;
+    P.L = make_layout(*dims, batch, capacity);
+    P.cache = static_cast<uint8_t*>(cache);
+    P.batch = batch;
+    P.capacity = capacity;
+    P.n_new = n_new;
+    P.a_k = a_k;
+    P.b_k = b_k;
+    P.a_v = a_v;
+    P.b_v = b_v;
+    P.positions = positions;
+    P.slot0 = slot0;
+    P.dev_status = dev_status;
+    return launch_append(P, static_cast<hipStream_t>(stream)) == hipSuccess ? KPA_OK : KPA_ERR_HIP;
+}
+
+size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t max_ctx, int32_t n_q,
+                                  int32_t num_splits) {
+    if (check_decode_args(dims, batch, max_ctx, max_ctx, n_q) != KPA_OK) return 0;
+    Plan plan = plan_decode(*dims, batch, max_ctx, n_q, num_splits, num_cus());
+    return plan.workspace_bytes;
+}
+
+static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch, int32_t capacity,
+                         const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
+                         const float* q, const int32_t* q_pos, float* out, float* lse,
+                         void* workspace, size_t workspace_bytes, int32_t num_splits,
+                         uint32_t* dev_status, void* stream) {
+    int st = check_decode_args(dims, batch, capacity, max_ctx, n_q);
+    if (st != KPA_OK) return st;
+    if (batch == 0) return KPA_OK;
+    if (!cache || !ctx_len || !q || !q_pos || !out) return KPA_ERR_NULL_PTR;
+    if (!aligned(cache, 16) || !aligned(q, 16) || !aligned(out, 16)) return KPA_ERR_INVALID_ARG;
+    Plan plan = plan_decode(*dims, batch, max_ctx, n_q, num_splits, num_cus());
+    if (plan.path == Path::kUnsupported) return KPA_ERR_UNSUPPORTED;
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.workspace_bytes) return KPA_ERR_WORKSPACE;
+        if (!aligned(workspace, 16)) return KPA_ERR_INVALID_ARG;
+    }
+    DecodeParams P{};
+    P.d = *dims;
+    P.L = make_layout(*dims, batch, capacity);
+    P.cache = static_cast<const uint8_t*>(cache);
+    P.batch = batch;
+    P.capacity = capacity;
+    P.max_ctx = max_ctx;
+    P.n_q = n_q;
+    P.causal = causal ? 1 : 0;
+    P.ctx_len = ctx_len;
+    P.q = q;
+    P.q_pos = q_pos;
+    P.out = out;
+    P.lse = lse;
+    P.dev_status = dev_status;
+    P.n_split = plan.n_split;
+    P.chunk_tiles = plan.chunk_tiles;
+    const int h = dims->p1 * dims->p2, dh = dims->q1 * dims->q2;
+    if (plan.n_split > 1) {
+        P.part_o = static_cast<float*>(workspace);
+        P.part_ml = P.part_o + (size_t)batch * n_q * plan.n_split * h * dh;
+    }
+    P.q_scale = (float)(1.4426950408889634 / (dims->r_k * sqrt((double)dh)));
+    P.v_scale = (float)(1.0 / dims->r_v);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_plan(plan, P, s);
+    if (e != hipSuccess) return KPA_ERR_HIP;
+    if (plan.n_split > 1 && launch_merge(P, s) != hipSuccess) return KPA_ERR_HIP;
+    return KPA_OK;
+}
+
+int kpa_decode(const kpa_dims* dims, const void* cache, int32_t batch, int32_t capacity,
+               const int32_t* ctx_len, int32_t max_ctx, const float* q, const int32_t* q_pos,
+               float* out, float* lse, void* workspace, size_t workspace_bytes,
+               int32_t num_splits, uint32_t* dev_status, void* stream) {
+    return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, 1, 0, q, q_pos, out, lse,
+                         workspace, workspace_bytes, num_splits, dev_status, stream);
+}
+
+int kpa_decode_multiq(const kpa_dims* dims, const void* cache, int32_t batch, int32_t capacity,
+                      const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
+                      const float* q, const int32_t* q_pos, float* out, float* lse,
+                      void* workspace, size_t workspace_bytes, int32_t num_splits,
+                      uint32_t* dev_status, void* stream) {
+    return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causal, q, q_pos, out,
+                         lse, workspace, workspace_bytes, num_splits, dev_status, stream);
+}
+
+const char* kpa_status_string(int status) {
+    switch (status) {
+        case KPA_OK: return "ok";
+        case KPA_ERR_INVALID_DIMS: return "invalid dims (non-positive split or rank, odd q2, or above the build limits)";
+        case KPA_ERR_NULL_PTR: return "a required pointer is NULL";
+        case KPA_ERR_DTYPE: return "unknown cache element type";
+        case KPA_ERR_WORKSPACE: return "workspace missing or smaller than kpa_decode_workspace_bytes()";
+        case KPA_ERR_UNSUPPORTED: return "shape not supported by any kernel in this build";
+        case KPA_ERR_HIP: return "HIP runtime error";
+        case KPA_ERR_INVALID_ARG: return "argument out of range or misaligned pointer";
+        default: return "unknown status";
+    }
+}
+
+const char* kpa_decode_path(const kpa_dims* dims, int32_t n_q) {
+    if (check_dims(dims) != KPA_OK || n_q < 1 || n_q > KPA_MAX_NQ) return "";
+    return path_name(select_path(*dims, n_q));
+}
+
+}  // extern "C"

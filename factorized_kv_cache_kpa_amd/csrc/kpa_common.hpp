@@ -1,0 +1,139 @@
+// Shared host/device definitions of libkpa: cache layout arithmetic, the
+// launch-parameter structs and small device helpers.
+//
+// [KPA] "Kronecker Product Attention: Memory-Efficient KV Compression via
+//       Structured Factorization" (arXiv 2610.12657).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kpa.h"
+
+namespace kpa {
+
+constexpr int kTileSlots = 32;   // slots per cache tile
+constexpr int kChunkBytes = 16;  // key sets are cut into 16-byte chunks
+constexpr int kTileAlign = 128;  // tiles are padded to 128 bytes
+
+// Cache layout (the KPA_LAYOUT_VERSION 1 description in kpa.h).
+struct Layout {
+    int32_t elem_bytes;
+    int32_t n_tiles;       // per sequence
+    int64_t tile_bytes;
+    int64_t off[4];        // A^K, B~^K, A^V, B^V inside a tile
+    int32_t elems[4];      // elements per token of each set
+    int64_t positions_off; // start of the int32 positions array
+    int64_t total_bytes;
+};
+
+inline __host__ __device__ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Host-side construction; assumes dims already validated.
+inline Layout make_layout(const kpa_dims& d, int32_t batch, int32_t capacity) {
+    Layout L{};
+    L.elem_bytes = d.dtype == KPA_F32 ? 4 : 2;
+    L.n_tiles = (capacity + kTileSlots - 1) / kTileSlots;
+    L.elems[0] = d.r_k * d.p1 * d.q1;
+    L.elems[1] = d.r_k * d.p2 * d.q2;
+    L.elems[2] = d.r_v * d.p1 * d.q1;
+    L.elems[3] = d.r_v * d.p2 * d.q2;
+    int64_t off = 0;
+    for (int c = 0; c < 4; ++c) {
+        L.off[c] = off;
+        int64_t bytes;
+        if (c < 2)  // feature-chunk: whole 16-byte chunks per slot
+            bytes = round_up((int64_t)L.elems[c] * L.elem_bytes, kChunkBytes) * kTileSlots;
+        else        // token-major
+            bytes = (int64_t)L.elems[c] * L.elem_bytes * kTileSlots;
+        off += bytes;
+    }
+    L.tile_bytes = round_up(off, kTileAlign);
+    L.positions_off = (int64_t)batch * L.n_tiles * L.tile_bytes;
+    L.total_bytes = L.positions_off + (int64_t)batch * L.n_tiles * kTileSlots * 4;
+    return L;
+}
+
+// Byte offset of element e of set c for slot t inside a tile.
+inline __host__ __device__ int64_t elem_offset(const Layout& L, int c, int64_t e, int t) {
+    if (c < 2) {
+        const int per_chunk = kChunkBytes / L.elem_bytes;
+        return L.off[c] + (e / per_chunk) * (kTileSlots * kChunkBytes) + (int64_t)t * kChunkBytes +
+               (e % per_chunk) * L.elem_bytes;
+    }
+    return L.off[c] + (e * kTileSlots + t) * L.elem_bytes;
+}
+
+// ---------------------------------------------------------------------------
+// Element conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float64 -> bfloat16, one rounding to nearest even.  Round to float with
+// round-to-odd (truncate, then force the last bit when inexact), then round
+// that float to bf16: float keeps 16 more bits than bf16, so the second
+// rounding cannot double-round.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+    float t = __double2float_rz(x);
+    uint32_t u = __float_as_uint(t);
+    if ((double)t != x) u |= 1u;
+    if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)(u >> 16);  // inf / nan
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Launch parameters
+// ---------------------------------------------------------------------------
+struct AppendParams {
+    kpa_dims d;
+    Layout L;
+    uint8_t* cache;
+    int32_t batch, capacity, n_new;
+    const void *a_k, *b_k, *a_v, *b_v;
+    const int32_t* positions;
+    const int32_t* slot0;
+    uint32_t* dev_status;
+};
+
+struct DecodeParams {
+    kpa_dims d;
+    Layout L;
+    const uint8_t* cache;
+    int32_t batch, capacity, max_ctx;
+    int32_t n_q, causal;
+    const int32_t* ctx_len;
+    const float* q;
+    const int32_t* q_pos;
+    float* out;
+    float* lse;
+    uint32_t* dev_status;
+    // split-KV
+    int32_t n_split;      // chunks per (sequence, query)
+    int32_t chunk_tiles;  // tiles per chunk
+    float* part_o;        // [batch][n_q][n_split][h][d_h]  (unnormalised sum p v)
+    float* part_ml;       // [batch][n_q][n_split][h][2]   (running max in log2 units, sum p)
+    float q_scale;        // log2(e) / (R_K sqrt(d_h))
+    float v_scale;        // 1 / R_V
+};
+
+// Visible slots of query n of sequence b (causal: the n_q newest slots hold
+// the queries' own tokens).  Out-of-range ctx_len is clamped and flagged.
+__device__ __forceinline__ int visible_slots(const DecodeParams& P, int b, int n) {
+    int ctx = P.ctx_len[b];
+    if (ctx < 0 || ctx > P.max_ctx) {
+        if (P.dev_status && n == 0 && threadIdx.x == 0) atomicOr(P.dev_status, (uint32_t)KPA_DEV_CTX_OUT_OF_RANGE);
+        ctx = ctx < 0 ? 0 : P.max_ctx;
+    }
+    int vis = P.causal ? ctx - P.n_q + n + 1 : ctx;
+    if (vis > ctx) vis = ctx;
+    if (vis < 0) vis = 0;
+    return vis;
+}
+
+// Launchers (one per translation unit).
+hipError_t launch_append(const AppendParams& P, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s);
+hipError_t launch_merge(const DecodeParams& P, hipStream_t s);
+
+}  // namespace kpa

@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/kpa.h declares, reports the documented cache
+layout, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import factorized_kv_cache_kpa_amd as kpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # non-null, aligned; only reached by calls that must fail before any launch
+
+
+def _declared_symbols():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(kpa_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = kpa.load()
+    declared = _declared_symbols()
+    assert {"kpa_cache_append", "kpa_decode", "kpa_decode_multiq"} <= declared
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+
+
+def _layout_by_hand(p1, p2, q1, q2, r_k, r_v, es, batch, capacity):
+    """The cache layout written out from its description in kpa.h."""
+    T = 32
+    elems = [r_k * p1 * q1, r_k * p2 * q2, r_v * p1 * q1, r_v * p2 * q2]
+    sizes = [-(-elems[0] * es // 16) * 16 * T, -(-elems[1] * es // 16) * 16 * T,
+             elems[2] * es * T, elems[3] * es * T]
+    offs = [0, sizes[0], sizes[0] + sizes[1], sizes[0] + sizes[1] + sizes[2]]
+    tile = -(-sum(sizes) // 128) * 128
+    n_tiles = -(-capacity // T)
+    pos_off = batch * n_tiles * tile
+    return dict(tile_bytes=tile, comp_offset=offs, comp_elems=elems, n_tiles=n_tiles,
+                positions_offset=pos_off, total_bytes=pos_off + batch * n_tiles * T * 4)
+
+
+@pytest.mark.parametrize("shape", [(2, 2, 4, 4, 2, 2, "f32"), (12, 1, 1, 64, 2, 2, "bf16"),
+                                   (4, 4, 8, 16, 2, 2, "bf16"), (8, 4, 8, 16, 2, 4, "bf16"),
+                                   (4, 8, 16, 8, 4, 4, "bf16"), (3, 5, 3, 6, 3, 1, "bf16")])
+@pytest.mark.parametrize("batch,capacity", [(1, 256), (3, 1000), (2, 31), (1, 0)])
+def test_layout_matches_description(shape, batch, capacity):
+    *dd, dt = shape
+    dims = kpa.make_dims(*dd, dtype=dt)
+    got = kpa.kpa_cache_layout(dims, batch, capacity)
+    want = _layout_by_hand(*dd, 4 if dt == "f32" else 2, batch, capacity)
+    for k, v in want.items():
+        assert got[k] == v, (k, got[k], v)
+    assert got["version"] == 1 and got["tile_slots"] == 32
+    assert kpa.kpa_cache_bytes(dims, batch, capacity) == want["total_bytes"]
+    # per-token factor bytes without padding: (R_K + R_V)(p1 q1 + p2 q2) * elem bytes
+    p1, p2, q1, q2, r_k, r_v = dd
+    assert sum(got["comp_elems"]) == (r_k + r_v) * (p1 * q1 + p2 * q2)
+
+
+def test_layout_has_no_per_token_padding_for_the_configs():
+    from workloads import CONFIGS
+    for cfg in CONFIGS.values():
+        dims = kpa.make_dims(cfg.p1, cfg.p2, cfg.q1, cfg.q2, cfg.r_k, cfg.r_v, dtype=cfg.dtype)
+        lay = kpa.kpa_cache_layout(dims, 1, 32)
+        assert lay["tile_bytes"] == 32 * cfg.bytes_per_token, cfg.name
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q2=5), -1), (dict(p1=0), -1), (dict(r_k=0), -1), (dict(r_v=17), -1),
+    (dict(p1=16, p2=16), -1), (dict(q1=32, q2=16), -1), (dict(rope_base=0.0), -1), (dict(dtype=7), -3),
+])
+def test_invalid_dims_rejected(bad, code):
+    base = dict(p1=4, p2=4, q1=8, q2=16, r_k=2, r_v=2, dtype=1, rope_base=10000.0)
+    base.update(bad)
+    dims = kpa.kpa_dims(**base)
+    lib = kpa.load()
+    info = kpa.kpa_layout_info()
+    assert lib.kpa_cache_layout(ctypes.byref(dims), 1, 64, ctypes.byref(info)) == code
+    assert lib.kpa_cache_bytes(ctypes.byref(dims), 1, 64) == 0
+    assert lib.kpa_cache_append(ctypes.byref(dims), FAKE, 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                1, None, None) == code
+    assert lib.kpa_decode(ctypes.byref(dims), FAKE, 1, 64, FAKE, 64, FAKE, FAKE, FAKE, None,
+                          FAKE, 1 << 30, 0, None, None) == code
+    assert kpa.kpa_decode_path(dims) == ""
+
+
+def test_null_and_range_errors_return_before_launch():
+    lib = kpa.load()
+    dims = kpa.make_dims(4, 4, 8, 16, 2, 2)
+    d = ctypes.byref(dims)
+    assert lib.kpa_cache_layout(None, 1, 1, None) == -2
+    assert lib.kpa_cache_append(d, None, 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, None) == -2
+    assert lib.kpa_cache_append(d, FAKE, -1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, None) == -7
+    assert lib.kpa_cache_append(d, FAKE + 4, 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, None) == -7
+    # nothing to do: OK without touching any pointer
+    assert lib.kpa_cache_append(d, None, 0, 64, None, None, None, None, None, None, 1, None, None) == 0
+    assert lib.kpa_cache_append(d, None, 1, 64, None, None, None, None, None, None, 0, None, None) == 0
+    # decode: null pointers, max_ctx beyond capacity, bad n_q, workspace too small
+    assert lib.kpa_decode(d, None, 1, 64, FAKE, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -2
+    assert lib.kpa_decode(d, FAKE, 1, 64, FAKE, 65, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -7
+    assert lib.kpa_decode_multiq(d, FAKE, 1, 64, FAKE, 64, 0, 1, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0,
+                                 None, None) == -7
+    assert lib.kpa_decode_multiq(d, FAKE, 1, 64, FAKE, 64, 65, 1, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0,
+                                 None, None) == -7
+    need = lib.kpa_decode_workspace_bytes(d, 4, 4096, 1, 8)
+    assert need > 0
+    assert lib.kpa_decode(d, FAKE, 4, 4096, FAKE, 4096, FAKE, FAKE, FAKE, None, FAKE, need - 1, 8,
+                          None, None) == -4
+    assert lib.kpa_decode(d, FAKE, 4, 4096, FAKE, 4096, FAKE, FAKE, FAKE, None, None, need, 8,
+                          None, None) == -4
+    assert lib.kpa_decode(d, None, 0, 4096, None, 4096, None, None, None, None, None, 0, 0, None, None) == 0
+
+
+def test_workspace_sizes_follow_the_split_count():
+    dims = kpa.make_dims(4, 4, 8, 16, 2, 2)
+    h, dh = 16, 128
+    assert kpa.kpa_decode_workspace_bytes(dims, 2, 4096, 1, 1) == 0
+    assert kpa.kpa_decode_workspace_bytes(dims, 2, 4096, 1, 8) == 2 * 8 * h * (dh + 2) * 4
+    # a forced count above the number of 32-slot tiles is clamped
+    assert kpa.kpa_decode_workspace_bytes(dims, 1, 64, 1, 99) == 1 * 2 * h * (dh + 2) * 4
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        assert kpa.kpa_status_string(code)
+    assert kpa.kpa_status_string(-99) == "unknown status"

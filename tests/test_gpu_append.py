@@ -1,0 +1,99 @@
+"""kpa_cache_append on the GPU: bit-exact copies and positions, pre-rotated
+B^K against the oracle's float64 rotation ([KPA] Thm. 2.4, Eq. (8)), and the
+device status bits."""
+import numpy as np
+import pytest
+import torch
+
+import factorized_kv_cache_kpa_amd as kpa
+from oracle import kpa_ref
+from tests.kpa_testutil import dims_of, fill_cache
+from workloads import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def unpack(cache_np, lay, dims, batch, slots):
+    """Read the four factor sets and the positions back with the layout of kpa.h."""
+    es = lay["elem_bytes"]
+    T, tb = lay["tile_slots"], lay["tile_bytes"]
+    np_dt = np.float32 if es == 4 else np.uint16
+    out = []
+    for c in range(4):
+        n_el = lay["comp_elems"][c]
+        arr = np.zeros((batch, slots, n_el), dtype=np_dt)
+        for b in range(batch):
+            for s in range(slots):
+                base = (b * lay["n_tiles"] + s // T) * tb + lay["comp_offset"][c]
+                t = s % T
+                e = np.arange(n_el)
+                if c < 2:
+                    per = 16 // es
+                    off = base + (e // per) * (T * 16) + t * 16 + (e % per) * es
+                else:
+                    off = base + (e * T + t) * es
+                raw = np.stack([cache_np[off + k] for k in range(es)], axis=1).copy()
+                arr[b, s] = raw.view(np_dt).reshape(n_el)
+        out.append(arr)
+    pos = cache_np[lay["positions_offset"]:].view(np.int32).reshape(batch, lay["n_tiles"] * T)[:, :slots]
+    return out, pos
+
+
+def _bits(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _to_f64(x, dtype):
+    if dtype == "f32":
+        return x.astype(np.float64)
+    return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("name,batch,slots", [("tiny_f32", 1, 256), ("tpa_degenerate", 2, 70),
+                                              ("kpa_32k", 2, 45), ("long_512k", 1, 33), ("multiq_16", 2, 40)])
+def test_append_readback(gpu_lib, name, batch, slots):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, seed=3, batch=batch, ctx=slots, pos_offset=524288 - slots)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims, chunk=17)
+    lay = kpa.kpa_cache_layout(dims, batch, cap)
+    sets, pos = unpack(cache.cpu().numpy(), lay, dims, batch, slots)
+    flat = lambda t: _bits(t).reshape(batch, slots, -1)
+    # bit-exact copies and positions
+    np.testing.assert_array_equal(sets[0], flat(inp.a_k))
+    np.testing.assert_array_equal(sets[2], flat(inp.a_v))
+    np.testing.assert_array_equal(sets[3], flat(inp.b_v))
+    np.testing.assert_array_equal(pos, inp.positions.numpy())
+    # B~^K: within half an ulp of the element type of the float64 rotation
+    got = _to_f64(sets[1], cfg.dtype).reshape(inp.b_k.shape)
+    bk = inp.b_k.to(torch.float64).numpy()
+    ulp_bits = 23 if cfg.dtype == "f32" else 7
+    for b in range(batch):
+        for s in range(slots):
+            want = kpa_ref.append_rotate(bk[b, s], int(inp.positions[b, s]))
+            half_ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 1 - ulp_bits) * 0.5
+            assert np.all(np.abs(got[b, s] - want) <= half_ulp * (1 + 1e-6) + 1e-300), (b, s)
+
+
+def test_append_device_status_and_no_write(gpu_lib):
+    cfg = CONFIGS["kpa_32k"]
+    dims = dims_of(cfg)
+    nb, cap = 3, 64
+    inp = make_inputs(cfg, seed=4, batch=nb, ctx=2)
+    cache = kpa.alloc_cache(dims, nb, cap)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pos = inp.positions.clone()
+    pos[1, 0] = -5                                           # negative position
+    slot0 = torch.tensor([0, 10, cap - 1], dtype=torch.int32)  # sequence 2's second token overflows
+    kpa.kpa_cache_append(dims, cache, nb, cap, inp.a_k.cuda(), inp.b_k.cuda(), inp.a_v.cuda(),
+                         inp.b_v.cuda(), pos.cuda(), slot0.cuda(), n_new=2, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kpa.KPA_DEV_SLOT_OUT_OF_RANGE | kpa.KPA_DEV_NEGATIVE_POSITION
+    lay = kpa.kpa_cache_layout(dims, nb, cap)
+    sets, positions = unpack(cache.cpu().numpy(), lay, dims, nb, cap)
+    # the rejected token (sequence 1, slot 10) was not written; its neighbour was
+    assert np.all(sets[0][1, 10] == 0) and positions[1, 10] == 0
+    assert positions[1, 11] == int(pos[1, 1])
+    assert positions[2, cap - 1] == int(pos[2, 0])

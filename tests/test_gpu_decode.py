@@ -1,0 +1,135 @@
+"""GPU decode parity against the float64 oracle, through the C ABI.
+
+Small cases compare every output element with the oracle; they span several
+32-slot tiles, a ragged tail, ragged per-sequence contexts and several KV
+chunks.  Full-size cases (every config at its real shape, in the launch
+configuration the benchmark times) compare a seeded sample of (sequence,
+query, head) rows, which the streaming oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import factorized_kv_cache_kpa_amd as kpa
+from oracle import kpa_oracle
+from tests.kpa_testutil import assert_close, dims_of, fill_cache, rel_err, run_decode
+from workloads import CONFIGS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(inp, causal=True, items=None):
+    return kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
+                             inp.q, inp.q_pos, causal=causal, items=items)
+
+
+SMALL = [
+    # name, batch, ctx, n_q, ragged, q_scale
+    ("tiny_f32", 1, 256, 1, False, 1.0),
+    ("tiny_f32", 3, 301, 1, True, 4.0),
+    ("tpa_degenerate", 4, 1000, 1, True, 1.0),
+    ("kpa_32k", 3, 2000, 1, True, 1.0),
+    ("kpa_32k", 2, 777, 1, False, 8.0),      # sharp softmax
+    ("long_512k", 1, 3000, 1, False, 1.0),
+    ("multiq_16", 2, 600, 16, True, 1.0),
+    ("multiq_16", 1, 16, 16, False, 2.0),    # the chunk is the whole context
+]
+
+
+@pytest.mark.parametrize("name,batch,ctx,n_q,ragged,q_scale", SMALL)
+def test_decode_matches_oracle_small(gpu_lib, name, batch, ctx, n_q, ragged, q_scale):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, seed=11, batch=batch, ctx=ctx, n_q=n_q, ragged=ragged, q_scale=q_scale)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    go, gl = run_decode(inp, dims, cache, cap)
+    ro, rl = _oracle(inp)
+    assert_close(go, gl, ro, rl, cfg.dtype, f"{name} b{batch} ctx{ctx}")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "kpa_32k", "multiq_16"])
+def test_split_count_invariance(gpu_lib, name):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, seed=5, batch=2, ctx=900, ragged=True)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    base_o, base_l = run_decode(inp, dims, cache, cap, num_splits=1)
+    for s in (2, 7, 29, 0):
+        o, l = run_decode(inp, dims, cache, cap, num_splits=s)
+        assert rel_err(o, base_o).max() <= 1e-5, s
+        assert np.allclose(l, base_l, atol=1e-5), s
+
+
+def test_non_causal_multi_query(gpu_lib):
+    cfg = CONFIGS["multiq_16"]
+    inp = make_inputs(cfg, seed=6, batch=2, ctx=300, n_q=5)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    go, gl = run_decode(inp, dims, cache, cap, causal=False)
+    ro, rl = _oracle(inp, causal=False)
+    assert_close(go, gl, ro, rl, cfg.dtype, "non-causal")
+
+
+def test_multi_query_row_equals_truncated_single_query(gpu_lib):
+    cfg = CONFIGS["multiq_16"]
+    inp = make_inputs(cfg, seed=8, batch=2, ctx=200, n_q=4)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    go, gl = run_decode(inp, dims, cache, cap)
+    for n in range(4):
+        sub = make_inputs(cfg, seed=8, batch=2, ctx=200, n_q=4)
+        sub.q = inp.q[:, n:n + 1].contiguous()
+        sub.q_pos = inp.q_pos[:, n:n + 1].contiguous()
+        sub.ctx_len = inp.ctx_len - 4 + n + 1
+        o1, l1 = run_decode(sub, dims, cache, cap)
+        assert rel_err(go[:, n], o1[:, 0]).max() <= 1e-5
+
+
+def test_empty_context_and_zero_batch(gpu_lib):
+    cfg = CONFIGS["kpa_32k"]
+    inp = make_inputs(cfg, seed=9, batch=3, ctx=100)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    inp.ctx_len[1] = 0
+    go, gl = run_decode(inp, dims, cache, cap, num_splits=3)
+    assert np.all(go[1] == 0) and np.all(np.isneginf(gl[1]))
+    ro, rl = _oracle(inp)
+    assert_close(go, gl, ro, rl, cfg.dtype, "ragged with empty")
+    # every sequence empty, max_ctx = 0
+    inp.ctx_len[:] = 0
+    go, gl = run_decode(inp, dims, cache, cap, max_ctx=0)
+    assert np.all(go == 0) and np.all(np.isneginf(gl))
+
+
+def test_ctx_len_above_max_ctx_is_flagged(gpu_lib):
+    cfg = CONFIGS["kpa_32k"]
+    inp = make_inputs(cfg, seed=10, batch=2, ctx=64)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((2, dims.h, dims.d_h), device="cuda")
+    ctx = torch.tensor([64, 40], dtype=torch.int32, device="cuda")
+    ws = kpa.alloc_workspace(dims, 2, 40)
+    kpa.kpa_decode(dims, cache, 2, cap, ctx, 40, inp.q.cuda().view(2, dims.h, dims.d_h),
+                   inp.q_pos.cuda().view(2), out, None, ws, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kpa.KPA_DEV_CTX_OUT_OF_RANGE
+
+
+def _sample_items(rng, batch, n_q, h, k):
+    idx = rng.choice(batch * n_q * h, size=min(k, batch * n_q * h), replace=False)
+    return np.stack([idx // (n_q * h), (idx // h) % n_q, idx % h], axis=1).astype(np.int32)
+
+
+@pytest.mark.parametrize("name,k", [("tpa_degenerate", 48), ("kpa_32k", 32), ("long_512k", 8), ("multiq_16", 32)])
+def test_decode_full_size_sampled(gpu_lib, name, k):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, seed=0)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    go, gl = run_decode(inp, dims, cache, cap)
+    items = _sample_items(np.random.default_rng(0), inp.batch, inp.q.shape[1], cfg.h, k)
+    ro, rl = _oracle(inp, items=items)
+    got_o = np.stack([go[b, n, hd] for b, n, hd in items])
+    got_l = np.array([gl[b, n, hd] for b, n, hd in items])
+    assert_close(got_o, got_l, ro, rl, cfg.dtype, f"{name} full size")
