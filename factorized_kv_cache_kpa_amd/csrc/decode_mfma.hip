@@ -1,0 +1,351 @@
+// Single-query split-KV decode on the bf16 matrix cores (gfx950 MFMA).
+//
+// Math ([KPA] = "Kronecker Product Attention: Memory-Efficient KV Compression
+// via Structured Factorization"; [TPA] = "Tensor Product Attention Is All You
+// Need", summary page):
+//   K_s = (1/R_K) sum_r A^K_r (x) B~^K_r, V_s likewise      ([KPA] Eqs. (3)-(4))
+//   z_{i,s} = q'_i . k_{s,i} / sqrt(d_h), q' = R_KPA(q_pos) q  ([KPA] §2.3, Def. 2.3)
+// Written with the two factors of a head: call F the factor whose feature
+// dimension is 16 (it is contracted on the matrix cores) and G the other one.
+// Head i = (iG, iF), feature j = (jG, jF) in the block order of the Kronecker
+// product ([KPA] Def. 2.1).  Then, per rank r and cached slot s,
+//   W_r[(iG,jG), s] = sum_jF q'[iG,iF,jG,jF] F_r[s,iF,jF]      (MFMA 32x32x16:
+//        M = (iG,jG), N = 32 slots, K = jF -- the query is the stationary
+//        operand, exactly as a grouped-query decode shares K across heads)
+//   z[iG,iF,s] = sum_r sum_jG G_r[s,iG,jG] W_r[(iG,jG),s]       (VALU, in lane)
+// which is [KPA] Prop. 2.2 / Eq. (6) with a dense query: contract with one
+// factor, then the other; K is never rebuilt.  The value side, per iF,
+//   O[(iG,jG), jF] += sum_{r,s} (p[iG,iF,s] G^V_r[s,iG,jG]) F^V_r[s,iF,jF]
+// is a GEMM over slots (MFMA 16x16x32: M = (iG,jG), N = jF, K = 32 slots),
+// with the softmax weight folded into the G factor on the VALU.  The online
+// softmax (running max and sum per head, rescaling O when the max grows) is
+// the blocked online log-sum-exp of FlashTPA decoding ([TPA]).
+//
+// Work split: one wave per (sequence, KV chunk, iF).  The PF waves of a
+// workgroup share the G factors through L1; each wave reads only its own F
+// slice, so every cache byte crosses HBM once.  No cross-wave reduction: the
+// heads (., iF) of a wave are its own.
+//
+// Precision: bf16 factors exactly; the rotated, scaled query is split into
+// bf16 hi + lo parts (two MFMAs) so it carries ~16 bits; the value operand
+// p * G^V is formed in fp32 and rounded once to bf16 (relative 2^-9 per
+// term, unbiased); the normaliser sums the fp32 weights; all accumulation is
+// fp32.  Because each KV chunk rounds against its own running max, results
+// for different chunk counts agree to that bf16 rounding, not bit for bit.
+#include "kpa_common.hpp"
+#include "kpa_mfma.hpp"
+
+namespace kpa {
+namespace {
+
+template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B>
+struct Shape {
+    static constexpr int PG_ = PG, QG_ = QG, PF_ = PF, QF_ = QF;
+    static constexpr int M = PG * QG;  // rows (iG, jG)
+    static constexpr int MB32 = M / 32;
+    static constexpr int MB16 = M / 16;
+    static constexpr int H = PG * PF;
+    static constexpr int DH = QG * QF;
+    static constexpr int GROUPS = 64 / PG;      // softmax: lanes per head
+    static constexpr int TPG = 32 / GROUPS;     // softmax: slots per lane
+    // cache sets
+    static constexpr int SET_GK = F_IS_B ? 0 : 1;
+    static constexpr int SET_FK = F_IS_B ? 1 : 0;
+    static constexpr int SET_GV = F_IS_B ? 2 : 3;
+    static constexpr int SET_FV = F_IS_B ? 3 : 2;
+    static_assert(QF == 16, "the MFMA-side feature dimension must be 16");
+    static_assert(M % 32 == 0, "rows (iG, jG) must fill 32-row MFMA blocks");
+    static_assert(QG == 4 || QG == 8 || QG == 16, "G-side feature dimension 4, 8 or 16");
+    static_assert(64 % PG == 0 && PG >= 2, "PG must divide 64");
+    static_assert(RK <= 4 && RV <= 4, "ranks up to 4");
+    __device__ static int head(int iG, int iF) { return F_IS_B ? iG * PF + iF : iF * PG + iG; }
+    __device__ static int feat(int jG, int jF) { return F_IS_B ? jG * QF + jF : jF * QG + jG; }
+};
+
+// Per-wave LDS scratch.
+template <class S>
+struct alignas(16) WaveScratch {
+    float z[S::PG_][32];
+    float p[S::PG_][32];
+    float alpha[S::PG_];
+    float m_fin[S::PG_];
+    float l_fin[S::PG_];
+};
+
+template <class S>
+__global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P) {
+    constexpr int PG = S::PG_, QG = S::QG_, PF = S::PF_, QF = S::QF_, RK = S::RK_, RV = S::RV_;
+    constexpr int M = S::M, MB32 = S::MB32, MB16 = S::MB16;
+    __shared__ WaveScratch<S> scratch[PF];
+    __shared__ float cs_tab[16][2];
+
+    const int lane = threadIdx.x & 63;
+    const int iF = threadIdx.x >> 6;
+    const int half = lane >> 5;
+    const int s = lane & 31;       // slot within the tile for the score side
+    const int l16 = lane & 15;
+    const int g16 = lane >> 4;     // 8-slot group for the value side
+    const int split = blockIdx.x, b = blockIdx.y;
+    WaveScratch<S>& ws = scratch[iF];
+    const Layout& L = P.L;
+
+    // ---- rotated, scaled query as MFMA A operands (hi + lo bf16) ------------
+    const int qp = P.q_pos[b];
+    constexpr int QROT = S::F_IS_B_ ? QF : QG;  // rotary pairs live in B's feature dim
+    if (threadIdx.x < QROT / 2) {
+        const double theta = exp2(-(2.0 * threadIdx.x / QROT) * log2((double)P.d.rope_base));
+        double sn, c;
+        sincos((double)qp * theta, &sn, &c);
+        cs_tab[threadIdx.x][0] = (float)c;
+        cs_tab[threadIdx.x][1] = (float)sn;
+    }
+    __syncthreads();
+    bf16x8 q_hi[MB32], q_lo[MB32];
+    {
+        const float* qg = P.q + (int64_t)b * S::H * S::DH;
+#pragma unroll
+        for (int mb = 0; mb < MB32; ++mb) {
+            const int R = mb * 32 + s;
+            const int iG = R / QG, jG = R % QG;
+            const float* qi = qg + (int64_t)S::head(iG, iF) * S::DH;
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int jF = 8 * half + k;
+                float x, y;  // this element and its rotary partner
+                int m, first;
+                if constexpr (S::F_IS_B_) {
+                    x = qi[S::feat(jG, jF)];
+                    y = qi[S::feat(jG, jF ^ 1)];
+                    m = jF >> 1;
+                    first = !(jF & 1);
+                } else {
+                    x = qi[S::feat(jG, jF)];
+                    y = qi[S::feat(jG ^ 1, jF)];
+                    m = jG >> 1;
+                    first = !(jG & 1);
+                }
+                const float c = cs_tab[m][0], sn = cs_tab[m][1];
+                // (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
+                v[k] = (first ? (x * c - y * sn) : (y * sn + x * c)) * P.q_scale;
+            }
+            split_bf16x8(v, q_hi[mb], q_lo[mb]);
+        }
+    }
+
+    f32x4 o_acc[MB16];
+#pragma unroll
+    for (int k = 0; k < MB16; ++k) o_acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // softmax state for head (iG = lane % PG, iF); l is this lane's partial sum
+    const int sm_iG = lane % PG, sm_g = lane / PG;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int vis = visible_slots(P, b, 0);
+    const int first = split * P.chunk_tiles * kTileSlots;
+    int last = first + P.chunk_tiles * kTileSlots;
+    if (last > vis) last = vis;
+    const uint8_t* seq = P.cache + (int64_t)b * L.n_tiles * L.tile_bytes;
+    const int64_t offFK = L.off[S::SET_FK], offGK = L.off[S::SET_GK];
+    const int64_t offFV = L.off[S::SET_FV], offGV = L.off[S::SET_GV];
+
+    for (int s0 = first; s0 < last; s0 += kTileSlots) {
+        const uint8_t* tile = seq + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
+        const int valid = min(kTileSlots, last - s0);
+
+        // ---- loads (all coalesced: 512 B or 1 KB contiguous per wave) ------
+        bf16x8 fk[RK];
+        uint2 gk[RK][MB32][4];
+        bf16x8 gv[RV][MB16], fv[RV];
+#pragma unroll
+        for (int r = 0; r < RK; ++r)
+            fk[r] = ld16<bf16x8>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + half) * 512 + s * 16);
+#pragma unroll
+        for (int r = 0; r < RK; ++r)
+#pragma unroll
+            for (int mb = 0; mb < MB32; ++mb)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    gk[r][mb][a] = ld8(tile + offGK + (int64_t)(r * (M / 8) + mb * 4 + a) * 512 + s * 16 + half * 8);
+#pragma unroll
+        for (int r = 0; r < RV; ++r) {
+#pragma unroll
+            for (int mb = 0; mb < MB16; ++mb)
+                gv[r][mb] = ld16<bf16x8>(tile + offGV + ((int64_t)(r * M + mb * 16 + l16) * 32 + 8 * g16) * 2);
+            fv[r] = ld16<bf16x8>(tile + offFV + ((int64_t)((r * PF + iF) * QF + l16) * 32 + 8 * g16) * 2);
+        }
+
+        // ---- scores: W = q' F (MFMA), z = sum G W (VALU) --------------------
+#pragma unroll
+        for (int mb = 0; mb < MB32; ++mb) {
+            float zp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < RK; ++r) {
+                f32x16 w = f32x16{};
+                w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_hi[mb], fk[r], w, 0, 0, 0);
+                w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_lo[mb], fk[r], w, 0, 0, 0);
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    float g0, g1, g2, g3;
+                    unpack_bf16x4(gk[r][mb][a], g0, g1, g2, g3);
+                    zp[a] += w[a * 4 + 0] * g0 + w[a * 4 + 1] * g1 + w[a * 4 + 2] * g2 + w[a * 4 + 3] * g3;
+                }
+            }
+            const bool ok = s < valid;
+            if constexpr (QG == 4) {
+                // rows 8a + 4half + b: iG = mb*8 + 2a + half, jG = b -- complete in lane
+#pragma unroll
+                for (int a = 0; a < 4; ++a) ws.z[mb * 8 + 2 * a + half][s] = ok ? zp[a] : -INFINITY;
+            } else if constexpr (QG == 8) {
+                // iG = mb*4 + a, jG = 4half + b: add the other half
+#pragma unroll
+                for (int a = 0; a < 4; ++a) zp[a] = sum_halves(zp[a]);
+                ws.z[mb * 4 + 2 * half + 0][s] = ok ? zp[2 * half + 0] : -INFINITY;
+                ws.z[mb * 4 + 2 * half + 1][s] = ok ? zp[2 * half + 1] : -INFINITY;
+            } else {
+                // QG == 16: iG = mb*2 + a/2, jG = 8(a%2) + 4half + b
+                float z0 = zp[0] + zp[1], z1 = zp[2] + zp[3];
+                z0 = sum_halves(z0);
+                z1 = sum_halves(z1);
+                ws.z[mb * 2 + half][s] = ok ? (half ? z1 : z0) : -INFINITY;
+            }
+        }
+        __syncthreads();
+
+        // ---- online softmax for the wave's PG heads --------------------------
+        {
+            float zl[S::TPG];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < S::TPG; ++u) {
+                zl[u] = ws.z[sm_iG][sm_g * S::TPG + u];
+                mt = fmaxf(mt, zl[u]);
+            }
+#pragma unroll
+            for (int x = PG; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x));
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+            float lsum = 0.f;
+#pragma unroll
+            for (int u = 0; u < S::TPG; ++u) {
+                const float p = (zl[u] == -INFINITY) ? 0.f : exp2f(zl[u] - m_new);
+                ws.p[sm_iG][sm_g * S::TPG + u] = p;
+                lsum += p;
+            }
+            l_run = l_run * alpha + lsum;
+            m_run = m_new;
+            if (sm_g == 0) ws.alpha[sm_iG] = alpha;
+        }
+        __syncthreads();
+
+        // ---- values: O = alpha O + (p G^V) F^V (MFMA over slots) -------------
+        if (valid < kTileSlots) {  // slots past the end: zero both operands
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                if (8 * g16 + k >= valid) {
+#pragma unroll
+                    for (int r = 0; r < RV; ++r) {
+                        fv[r][k] = (__bf16)0.f;
+#pragma unroll
+                        for (int mb = 0; mb < MB16; ++mb) gv[r][mb][k] = (__bf16)0.f;
+                    }
+                }
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB16; ++mb) {
+            const int iG_out = (mb * 16 + 4 * g16) / QG;  // rows of this lane's accumulator
+            const float a = ws.alpha[iG_out];
+            o_acc[mb] *= a;
+            const int iG_row = (mb * 16 + l16) / QG;      // row of this lane's A operand
+            float p[8];
+            ld_lds32(&ws.p[iG_row][8 * g16], p);
+#pragma unroll
+            for (int r = 0; r < RV; ++r) {
+                float gvf[8];
+                unpack_bf16x8(gv[r][mb], gvf);
+                float prod[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) prod[k] = p[k] * gvf[k];
+                o_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack_bf16x8(prod), fv[r], o_acc[mb], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- finish: full sums per head, then write -----------------------------
+#pragma unroll
+    for (int x = PG; x < 64; x <<= 1) l_run += __shfl_xor(l_run, x);
+    if (sm_g == 0) {
+        ws.m_fin[sm_iG] = m_run;
+        ws.l_fin[sm_iG] = l_run;
+    }
+    __syncthreads();
+    const int64_t row = b;  // single query
+    const int H = S::H, DH = S::DH;
+#pragma unroll
+    for (int mb = 0; mb < MB16; ++mb) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int R = mb * 16 + 4 * g16 + c;
+            const int iG = R / QG, jG = R % QG;
+            const int i = S::head(iG, iF), j = S::feat(jG, l16);
+            const float v = o_acc[mb][c] * P.v_scale;
+            if (P.n_split == 1) {
+                const float l = ws.l_fin[iG];
+                P.out[(row * H + i) * DH + j] = l > 0.f ? v / l : 0.f;
+            } else {
+                P.part_o[((row * P.n_split + split) * H + i) * DH + j] = v;
+            }
+        }
+    }
+    if (lane < PG) {
+        const int i = S::head(lane, iF);
+        const float m = ws.m_fin[lane], l = ws.l_fin[lane];
+        if (P.n_split == 1) {
+            if (P.lse) P.lse[row * H + i] = l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+        } else {
+            float* ml = P.part_ml + ((row * P.n_split + split) * H + i) * 2;
+            ml[0] = m;
+            ml[1] = l;
+        }
+    }
+}
+
+template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B>
+struct Cfg : Shape<PG, QG, PF, QF, RK, RV, F_IS_B> {
+    static constexpr int RK_ = RK, RV_ = RV;
+    static constexpr bool F_IS_B_ = F_IS_B;
+};
+
+template <class C>
+hipError_t launch_one(const DecodeParams& P, hipStream_t s) {
+    dim3 grid(P.n_split, P.batch);
+    hipLaunchKernelGGL(decode_mfma_kernel<C>, grid, dim3(C::PF_ * 64), 0, s, P);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Shapes with a matrix-core instantiation; the dispatcher asks here first.
+bool decode_mfma_supported(const kpa_dims& d, int n_q) {
+    if (d.dtype != KPA_BF16 || n_q != 1) return false;
+    const int k[6] = {d.p1, d.p2, d.q1, d.q2, d.r_k, d.r_v};
+    auto is = [&](int a, int b, int c, int e, int f, int g) {
+        return k[0] == a && k[1] == b && k[2] == c && k[3] == e && k[4] == f && k[5] == g;
+    };
+    return is(4, 4, 8, 16, 2, 2) || is(8, 4, 8, 16, 2, 4) || is(4, 8, 16, 8, 4, 4) || is(4, 4, 8, 16, 1, 1);
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s) {
+    const kpa_dims& d = P.d;
+    // F is the factor with feature dimension 16.
+    if (d.p1 == 4 && d.p2 == 4 && d.q1 == 8 && d.q2 == 16 && d.r_k == 2 && d.r_v == 2)
+        return launch_one<Cfg<4, 8, 4, 16, 2, 2, true>>(P, s);
+    if (d.p1 == 4 && d.p2 == 4 && d.q1 == 8 && d.q2 == 16 && d.r_k == 1 && d.r_v == 1)
+        return launch_one<Cfg<4, 8, 4, 16, 1, 1, true>>(P, s);
+    if (d.p1 == 8 && d.p2 == 4 && d.q1 == 8 && d.q2 == 16 && d.r_k == 2 && d.r_v == 4)
+        return launch_one<Cfg<8, 8, 4, 16, 2, 4, true>>(P, s);
+    if (d.p1 == 4 && d.p2 == 8 && d.q1 == 16 && d.q2 == 8 && d.r_k == 4 && d.r_v == 4)
+        return launch_one<Cfg<8, 8, 4, 16, 4, 4, false>>(P, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kpa

@@ -135,5 +135,7 @@ __device__ __forceinline__ int visible_slots(const DecodeParams& P, int b, int n
 hipError_t launch_append(const AppendParams& P, hipStream_t s);
 hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s);
 hipError_t launch_merge(const DecodeParams& P, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s);
+bool decode_mfma_supported(const kpa_dims& d, int n_q);
 
 }  // namespace kpa

@@ -5,7 +5,7 @@
 
 namespace kpa {
 
-enum class Path { kUnsupported, kValu };
+enum class Path { kUnsupported, kValu, kMfmaSq };
 
 struct Plan {
     Path path;
@@ -17,12 +17,13 @@ struct Plan {
 inline const char* path_name(Path p) {
     switch (p) {
         case Path::kValu: return "valu";
+        case Path::kMfmaSq: return "mfma_bf16";
         default: return "";
     }
 }
 
-inline Path select_path(const kpa_dims& d, int32_t /*n_q*/) {
-    (void)d;
+inline Path select_path(const kpa_dims& d, int32_t n_q) {
+    if (decode_mfma_supported(d, n_q)) return Path::kMfmaSq;
     return Path::kValu;
 }
 
@@ -38,7 +39,9 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
     if (num_splits > 0) {
         s = num_splits;
     } else {
-        const int64_t target = 4LL * cus;
+        // workgroups in flight: the VALU kernel is one 256-thread group per
+        // chunk; the matrix-core kernel one wave per (chunk, iF)
+        const int64_t target = (p.path == Path::kMfmaSq ? 2LL : 4LL) * cus;
         s = rows > 0 ? (target + rows - 1) / rows : 1;
         const int64_t min_tiles_per_chunk = 2;
         const int64_t cap = (tiles + min_tiles_per_chunk - 1) / min_tiles_per_chunk;
@@ -62,6 +65,7 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
 inline hipError_t launch_plan(const Plan& plan, const DecodeParams& P, hipStream_t s) {
     switch (plan.path) {
         case Path::kValu: return launch_decode_valu(P, s);
+        case Path::kMfmaSq: return launch_decode_mfma(P, s);
         default: return hipErrorInvalidValue;
     }
 }

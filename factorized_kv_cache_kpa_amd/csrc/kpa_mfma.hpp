@@ -1,0 +1,95 @@
+// Register types and small helpers for the gfx950 matrix-core kernels.
+//
+// Operand layouts of the bf16 MFMA instructions used here (wave of 64 lanes):
+//   v_mfma_f32_32x32x16_bf16: A[m][k] is element k%8 of lane m + 32*(k/8);
+//     B[k][n] is element k%8 of lane n + 32*(k/8); D[m][n] is register
+//     (m/8)*4 + m%4 of lane n + 32*((m/4)%2).
+//   v_mfma_f32_16x16x32_bf16: A[m][k] is element k%8 of lane m + 16*(k/8);
+//     B[k][n] is element k%8 of lane n + 16*(k/8); D[m][n] is register m%4
+//     of lane n + 16*(m/4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kpa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+template <typename T>
+__device__ __forceinline__ T ld16(const uint8_t* p) {
+    return __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+
+__device__ __forceinline__ bf16x8 ld_lds16(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void ld_lds32(const float* p, float* out) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        out[k] = a[k];
+        out[4 + k] = b[k];
+    }
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ void unpack_bf16x4(uint2 u, float& a, float& b, float& c, float& d) {
+    a = __uint_as_float(u.x << 16);
+    b = __uint_as_float(u.x & 0xffff0000u);
+    c = __uint_as_float(u.y << 16);
+    d = __uint_as_float(u.y & 0xffff0000u);
+}
+
+__device__ __forceinline__ void unpack_bf16x8(bf16x8 v, float* out) {
+    const u32x4 u = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        out[2 * k] = __uint_as_float(u[k] << 16);
+        out[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+    }
+}
+
+// Round 8 floats to bf16 (nearest even).
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
+    bf16x8 r;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) r[k] = (__bf16)v[k];
+    return r;
+}
+
+// v = hi + lo with hi = bf16(v) and lo = bf16(v - hi).
+__device__ __forceinline__ void split_bf16x8(const float* v, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const __bf16 h = (__bf16)v[k];
+        hi[k] = h;
+        lo[k] = (__bf16)(v[k] - (float)h);
+    }
+}
+
+// The value of lane l ^ 32 (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    // r[0] holds the lower half's value in every lane, r[1] the upper half's.
+    return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
+}
+
+// x(l) + x(l ^ 32) in every lane.
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace kpa

@@ -13,50 +13,43 @@
 namespace kpa {
 namespace {
 
-constexpr int kThreads = 256;
-
-__global__ void __launch_bounds__(kThreads) merge_kernel(DecodeParams P) {
-    extern __shared__ float smem[];
+// One block per (sequence, query, head); threads over the head dimension.
+__global__ void __launch_bounds__(256) merge_kernel(DecodeParams P) {
     const int h = P.d.p1 * P.d.p2, dh = P.d.q1 * P.d.q2;
     const int64_t row = blockIdx.x;  // (b, n)
+    const int i = blockIdx.y;        // head
     const int S = P.n_split;
-    float* big_m = smem;       // [h]
-    float* inv_l = smem + h;   // [h]
     const float* ml = P.part_ml + row * S * h * 2;
     const float* po = P.part_o + row * S * h * dh;
 
-    for (int i = threadIdx.x; i < h; i += kThreads) {
-        float M = -INFINITY;
-        for (int k = 0; k < S; ++k) M = fmaxf(M, ml[(k * h + i) * 2]);
-        float l = 0.f;
-        if (M != -INFINITY)
-            for (int k = 0; k < S; ++k) {
-                const float mk = ml[(k * h + i) * 2];
-                if (mk != -INFINITY) l += exp2f(mk - M) * ml[(k * h + i) * 2 + 1];
-            }
-        big_m[i] = M;
-        inv_l[i] = l > 0.f ? 1.f / l : 0.f;
-        if (P.lse) P.lse[row * h + i] = l > 0.f ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
-    }
-    __syncthreads();
-    for (int o = threadIdx.x; o < h * dh; o += kThreads) {
-        const int i = o / dh;
-        const float M = big_m[i];
+    float M = -INFINITY;
+    for (int k = 0; k < S; ++k) M = fmaxf(M, ml[(k * h + i) * 2]);
+    float l = 0.f;
+    if (M != -INFINITY)
+        for (int k = 0; k < S; ++k) {
+            const float mk = ml[(k * h + i) * 2];
+            if (mk != -INFINITY) l += exp2f(mk - M) * ml[(k * h + i) * 2 + 1];
+        }
+    const float inv_l = l > 0.f ? 1.f / l : 0.f;
+    if (P.lse && threadIdx.x == 0)
+        P.lse[row * h + i] = l > 0.f ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    for (int j = threadIdx.x; j < dh; j += blockDim.x) {
         float acc = 0.f;
         if (M != -INFINITY)
             for (int k = 0; k < S; ++k) {
                 const float mk = ml[(k * h + i) * 2];
-                if (mk != -INFINITY) acc += exp2f(mk - M) * po[(int64_t)k * h * dh + o];
+                if (mk != -INFINITY) acc += exp2f(mk - M) * po[((int64_t)k * h + i) * dh + j];
             }
-        P.out[row * h * dh + o] = acc * inv_l[i];
+        P.out[(row * h + i) * dh + j] = acc * inv_l;
     }
 }
 
 }  // namespace
 
 hipError_t launch_merge(const DecodeParams& P, hipStream_t s) {
-    const int h = P.d.p1 * P.d.p2;
-    hipLaunchKernelGGL(merge_kernel, dim3(P.batch * P.n_q), dim3(kThreads), 2 * h * sizeof(float), s, P);
+    const int h = P.d.p1 * P.d.p2, dh = P.d.q1 * P.d.q2;
+    const int threads = dh <= 64 ? 64 : (dh <= 128 ? 128 : 256);
+    hipLaunchKernelGGL(merge_kernel, dim3(P.batch * P.n_q, h), dim3(threads), 0, s, P);
     return hipGetLastError();
 }
 

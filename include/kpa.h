@@ -177,7 +177,9 @@ size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t m
  *   workspace: device, >= kpa_decode_workspace_bytes(dims, batch, max_ctx, 1, num_splits).
  *   num_splits: 0 picks the number of KV chunks per sequence from max_ctx and
  *       the CU count; > 0 forces it (clamped to [1, ceil(max_ctx / 32)]).
- *       Results agree across split counts up to float32 rounding.
+ *       Results agree across split counts up to rounding: float32 rounding on
+ *       the vector-ALU path, the bf16 rounding of the softmax-weighted value
+ *       operand (relative 2^-9 per term) on the matrix-core path.
  *   dev_status: as for kpa_cache_append (KPA_DEV_CTX_OUT_OF_RANGE), or NULL.
  * ctx_len[b] = 0 gives out = 0 and lse = -inf.
  */

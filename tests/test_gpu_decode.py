@@ -33,7 +33,35 @@ SMALL = [
     ("long_512k", 1, 3000, 1, False, 1.0),
     ("multiq_16", 2, 600, 16, True, 1.0),
     ("multiq_16", 1, 16, 16, False, 2.0),    # the chunk is the whole context
+    ("multiq_16", 2, 500, 1, True, 3.0),     # one query on the multi-query shape (F = A orientation)
+    ("long_512k", 2, 45, 1, True, 1.0),      # contexts shorter than two tiles
 ]
+
+
+def test_decode_rank_one_kpa(gpu_lib):
+    cfg = CONFIGS["kpa_32k"].scaled(r_k=1, r_v=1)
+    inp = make_inputs(cfg, seed=12, batch=2, ctx=333, ragged=True, q_scale=2.0)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    go, gl = run_decode(inp, dims, cache, cap)
+    ro, rl = _oracle(inp)
+    assert_close(go, gl, ro, rl, cfg.dtype, "rank one")
+
+
+def test_garbage_past_the_context_is_ignored(gpu_lib):
+    # slots past ctx_len hold NaN bit patterns; the result must not see them
+    cfg = CONFIGS["kpa_32k"]
+    inp = make_inputs(cfg, seed=13, batch=2, ctx=100)
+    dims = dims_of(cfg)
+    cap = 128
+    nan_cache = kpa.alloc_cache(dims, 2, cap)
+    nan_cache.fill_(0xFF)
+    kpa.kpa_cache_append(dims, nan_cache, 2, cap, inp.a_k.cuda(), inp.b_k.cuda(), inp.a_v.cuda(), inp.b_v.cuda(),
+                         inp.positions.cuda(), torch.zeros(2, dtype=torch.int32, device="cuda"), n_new=100)
+    torch.cuda.synchronize()
+    go, gl = run_decode(inp, dims, nan_cache, cap, max_ctx=cap)
+    ro, rl = _oracle(inp)
+    assert_close(go, gl, ro, rl, cfg.dtype, "NaN past the context")
 
 
 @pytest.mark.parametrize("name,batch,ctx,n_q,ragged,q_scale", SMALL)
@@ -53,11 +81,17 @@ def test_split_count_invariance(gpu_lib, name):
     inp = make_inputs(cfg, seed=5, batch=2, ctx=900, ragged=True)
     dims = dims_of(cfg)
     cache, cap = fill_cache(inp, dims)
+    # the matrix-core path rounds the weighted value operand to bf16 against each
+    # chunk's own running max, so chunkings agree to that rounding (2^-9 per term)
+    path = kpa.kpa_decode_path(dims, inp.q.shape[1])
+    tol = 1e-5 if path == "valu" else 1e-2
+    ro, rl = _oracle(inp)
     base_o, base_l = run_decode(inp, dims, cache, cap, num_splits=1)
     for s in (2, 7, 29, 0):
         o, l = run_decode(inp, dims, cache, cap, num_splits=s)
-        assert rel_err(o, base_o).max() <= 1e-5, s
+        assert rel_err(o, base_o).max() <= tol, s
         assert np.allclose(l, base_l, atol=1e-5), s
+        assert_close(o, l, ro, rl, cfg.dtype, f"splits={s}")
 
 
 def test_non_causal_multi_query(gpu_lib):
@@ -82,7 +116,11 @@ def test_multi_query_row_equals_truncated_single_query(gpu_lib):
         sub.q_pos = inp.q_pos[:, n:n + 1].contiguous()
         sub.ctx_len = inp.ctx_len - 4 + n + 1
         o1, l1 = run_decode(sub, dims, cache, cap)
-        assert rel_err(go[:, n], o1[:, 0]).max() <= 1e-5
+        # the two calls may take different kernel paths; the matrix-core path
+        # rounds the weighted value operand to bf16 (2^-9 per term)
+        paths = {kpa.kpa_decode_path(dims, 4), kpa.kpa_decode_path(dims, 1)}
+        tol = 1e-5 if paths == {"valu"} else 1e-2
+        assert rel_err(go[:, n], o1[:, 0]).max() <= tol
 
 
 def test_empty_context_and_zero_batch(gpu_lib):
