@@ -73,7 +73,7 @@ struct alignas(16) WaveScratch {
 };
 
 template <class S>
-__global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P) {
+__global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(DecodeParams P) {
     constexpr int PG = S::PG_, QG = S::QG_, PF = S::PF_, QF = S::QF_, RK = S::RK_, RV = S::RV_;
     constexpr int M = S::M, MB32 = S::MB32, MB16 = S::MB16;
     __shared__ WaveScratch<S> scratch[PF];
@@ -140,6 +140,7 @@ __global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P
     const int sm_iG = lane % PG, sm_g = lane / PG;
     float m_run = -INFINITY, l_run = 0.f;
 
+    clear_merge_counters(P, b, split);
     const int vis = visible_slots(P, b, 0);
     const int first = split * P.chunk_tiles * kTileSlots;
     int last = first + P.chunk_tiles * kTileSlots;
@@ -148,14 +149,14 @@ __global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P
     const int64_t offFK = L.off[S::SET_FK], offGK = L.off[S::SET_GK];
     const int64_t offFV = L.off[S::SET_FV], offGV = L.off[S::SET_GV];
 
-    for (int s0 = first; s0 < last; s0 += kTileSlots) {
-        const uint8_t* tile = seq + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
-        const int valid = min(kTileSlots, last - s0);
-
-        // ---- loads (all coalesced: 512 B or 1 KB contiguous per wave) ------
-        bf16x8 fk[RK];
-        uint2 gk[RK][MB32][4];
-        bf16x8 gv[RV][MB16], fv[RV];
+    // Loads are skewed by half a tile: the value-side operands of tile t are
+    // requested before its score phase, the key-side operands of tile t+1
+    // before the value phase of tile t, so every load has a phase of work to
+    // hide behind without doubling the registers.
+    bf16x8 fk[RK];
+    uint2 gk[RK][MB32][4];
+    bf16x8 gv[RV][MB16], fv[RV];
+    auto load_key_side = [&](const uint8_t* tile) {
 #pragma unroll
         for (int r = 0; r < RK; ++r)
             fk[r] = ld16<bf16x8>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + half) * 512 + s * 16);
@@ -166,6 +167,8 @@ __global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
                     gk[r][mb][a] = ld8(tile + offGK + (int64_t)(r * (M / 8) + mb * 4 + a) * 512 + s * 16 + half * 8);
+    };
+    auto load_value_side = [&](const uint8_t* tile) {
 #pragma unroll
         for (int r = 0; r < RV; ++r) {
 #pragma unroll
@@ -173,6 +176,13 @@ __global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P
                 gv[r][mb] = ld16<bf16x8>(tile + offGV + ((int64_t)(r * M + mb * 16 + l16) * 32 + 8 * g16) * 2);
             fv[r] = ld16<bf16x8>(tile + offFV + ((int64_t)((r * PF + iF) * QF + l16) * 32 + 8 * g16) * 2);
         }
+    };
+    if (first < last) load_key_side(seq + (int64_t)(first / kTileSlots) * L.tile_bytes);
+
+    for (int s0 = first; s0 < last; s0 += kTileSlots) {
+        const uint8_t* tile = seq + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
+        const int valid = min(kTileSlots, last - s0);
+        load_value_side(tile);
 
         // ---- scores: W = q' F (MFMA), z = sum G W (VALU) --------------------
 #pragma unroll
@@ -209,7 +219,7 @@ __global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P
                 ws.z[mb * 2 + half][s] = ok ? (half ? z1 : z0) : -INFINITY;
             }
         }
-        __syncthreads();
+        wave_lds_sync();
 
         // ---- online softmax for the wave's PG heads --------------------------
         {
@@ -235,7 +245,9 @@ __global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P
             m_run = m_new;
             if (sm_g == 0) ws.alpha[sm_iG] = alpha;
         }
-        __syncthreads();
+        wave_lds_sync();
+
+        if (s0 + kTileSlots < last) load_key_side(tile + L.tile_bytes);
 
         // ---- values: O = alpha O + (p G^V) F^V (MFMA over slots) -------------
         if (valid < kTileSlots) {  // slots past the end: zero both operands
@@ -277,7 +289,7 @@ __global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P
         ws.m_fin[sm_iG] = m_run;
         ws.l_fin[sm_iG] = l_run;
     }
-    __syncthreads();
+    wave_lds_sync();
     const int64_t row = b;  // single query
     const int H = S::H, DH = S::DH;
 #pragma unroll
@@ -309,10 +321,11 @@ __global__ void __launch_bounds__(S::PF_ * 64) decode_mfma_kernel(DecodeParams P
     }
 }
 
-template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B>
+template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int MW = 2>
 struct Cfg : Shape<PG, QG, PF, QF, RK, RV, F_IS_B> {
     static constexpr int RK_ = RK, RV_ = RV;
     static constexpr bool F_IS_B_ = F_IS_B;
+    static constexpr int MIN_WAVES = MW;  // waves per SIMD the register budget must allow
 };
 
 template <class C>
@@ -344,7 +357,7 @@ hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s) {
     if (d.p1 == 8 && d.p2 == 4 && d.q1 == 8 && d.q2 == 16 && d.r_k == 2 && d.r_v == 4)
         return launch_one<Cfg<8, 8, 4, 16, 2, 4, true>>(P, s);
     if (d.p1 == 4 && d.p2 == 8 && d.q1 == 16 && d.q2 == 8 && d.r_k == 4 && d.r_v == 4)
-        return launch_one<Cfg<8, 8, 4, 16, 4, 4, false>>(P, s);
+        return launch_one<Cfg<8, 8, 4, 16, 4, 4, false, 1>>(P, s);
     return hipErrorInvalidValue;
 }
 

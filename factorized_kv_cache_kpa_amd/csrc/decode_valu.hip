@@ -48,6 +48,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P) {
     float* alpha = l_run + h;              // [h] rescale factor of this tile
     float* cs = alpha + h;                 // [q2/2][2] cos, sin
 
+    clear_merge_counters(P, (int64_t)b * P.n_q + n, split);
     const int vis = visible_slots(P, b, n);
     const int first = split * P.chunk_tiles * kTileSlots;
     int last = first + P.chunk_tiles * kTileSlots;

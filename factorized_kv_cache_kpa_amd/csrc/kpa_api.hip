@@ -154,9 +154,16 @@ static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch,
     P.n_split = plan.n_split;
     P.chunk_tiles = plan.chunk_tiles;
     const int h = dims->p1 * dims->p2, dh = dims->q1 * dims->q2;
+    P.n_group = plan.n_group;
     if (plan.n_split > 1) {
-        P.part_o = static_cast<float*>(workspace);
+        float* ws = static_cast<float*>(workspace);
+        P.part_o = ws;
         P.part_ml = P.part_o + (size_t)batch * n_q * plan.n_split * h * dh;
+        if (plan.n_group > 1) {
+            P.part2_o = ws + plan.part_floats;
+            P.part2_ml = P.part2_o + (size_t)batch * n_q * plan.n_group * h * dh;
+            P.merge_count = reinterpret_cast<uint32_t*>(ws + plan.part_floats + plan.part2_floats);
+        }
     }
     P.q_scale = (float)(1.4426950408889634 / (dims->r_k * sqrt((double)dh)));
     P.v_scale = (float)(1.0 / dims->r_v);

@@ -113,6 +113,10 @@ struct DecodeParams {
     int32_t chunk_tiles;  // tiles per chunk
     float* part_o;        // [batch][n_q][n_split][h][d_h]  (unnormalised sum p v)
     float* part_ml;       // [batch][n_q][n_split][h][2]   (running max in log2 units, sum p)
+    int32_t n_group;      // merge groups per (row, head); > 1 adds a second level
+    float* part2_o;       // [batch][n_q][n_group][h][d_h]
+    float* part2_ml;      // [batch][n_q][n_group][h][2]
+    uint32_t* merge_count; // [batch][n_q][h] arrival counters of the second level
     float q_scale;        // log2(e) / (R_K sqrt(d_h))
     float v_scale;        // 1 / R_V
 };
@@ -129,6 +133,15 @@ __device__ __forceinline__ int visible_slots(const DecodeParams& P, int b, int n
     if (vis > ctx) vis = ctx;
     if (vis < 0) vis = 0;
     return vis;
+}
+
+// The chunk-0 workgroup of a row clears that row's merge counters; the merge
+// kernel runs after the decode kernel on the same stream and leaves them at 0.
+__device__ __forceinline__ void clear_merge_counters(const DecodeParams& P, int64_t row, int split) {
+    if (P.merge_count && split == 0) {
+        const int h = P.d.p1 * P.d.p2;
+        for (int i = threadIdx.x; i < h; i += blockDim.x) P.merge_count[row * h + i] = 0u;
+    }
 }
 
 // Launchers (one per translation unit).

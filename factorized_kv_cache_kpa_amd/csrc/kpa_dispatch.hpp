@@ -11,8 +11,14 @@ struct Plan {
     Path path;
     int32_t n_split;
     int32_t chunk_tiles;
+    int32_t n_group;        // merge groups (level-2 partials) per (row, head); 1 = single level
+    size_t part_floats;     // level-1 partials
+    size_t part2_floats;    // level-2 partials
     size_t workspace_bytes;
 };
+
+// Splits merged by one merge block; more splits go through a second level.
+constexpr int kMergeGroup = 32;
 
 inline const char* path_name(Path p) {
     switch (p) {
@@ -58,7 +64,11 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
     p.n_split = (int32_t)s;
     p.chunk_tiles = (int32_t)chunk;
     const int64_t h = (int64_t)d.p1 * d.p2, dh = (int64_t)d.q1 * d.q2;
-    p.workspace_bytes = s > 1 ? (size_t)(rows * s * h * (dh + 2) * sizeof(float)) : 0;
+    p.n_group = s > 1 ? (int32_t)((s + kMergeGroup - 1) / kMergeGroup) : 1;
+    p.part_floats = s > 1 ? (size_t)(rows * s * h * (dh + 2)) : 0;
+    p.part2_floats = p.n_group > 1 ? (size_t)(rows * p.n_group * h * (dh + 2)) : 0;
+    const size_t counters = p.n_group > 1 ? (size_t)(rows * h) : 0;
+    p.workspace_bytes = (p.part_floats + p.part2_floats + counters) * sizeof(float);
     return p;
 }
 

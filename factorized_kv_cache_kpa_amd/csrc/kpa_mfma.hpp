@@ -86,6 +86,16 @@ __device__ __forceinline__ float swap_halves(float x) {
     return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
 
+// Make this wave's LDS writes visible to its other lanes (the wave's LDS
+// operations complete in order; the fences keep the compiler from moving
+// LDS accesses across this point).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // x(l) + x(l ^ 32) in every lane.
 __device__ __forceinline__ float sum_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
