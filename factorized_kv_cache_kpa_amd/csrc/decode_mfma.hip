@@ -32,6 +32,9 @@
 // term, unbiased); the normaliser sums the fp32 weights; all accumulation is
 // fp32.  Because each KV chunk rounds against its own running max, results
 // for different chunk counts agree to that bf16 rounding, not bit for bit.
+#include <atomic>
+#include <type_traits>
+
 #include "kpa_common.hpp"
 #include "kpa_mfma.hpp"
 
@@ -46,6 +49,10 @@ struct Shape {
     static constexpr int MB16 = M / 16;
     static constexpr int H = PG * PF;
     static constexpr int DH = QG * QF;
+    // G factors of one tile in 1 KB blocks: key set R_K*M elements in 16-byte
+    // chunks (M/8 chunks of 512 B per rank), value set R_V*M elements x 32 slots
+    static constexpr int GK_BLOCKS = RK * M * 64 / 1024;
+    static constexpr int G_BLOCKS = (RK + RV) * M * 64 / 1024;
     static constexpr int GROUPS = 64 / PG;      // softmax: lanes per head
     static constexpr int TPG = 32 / GROUPS;     // softmax: slots per lane
     // cache sets
@@ -78,6 +85,10 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
     constexpr int M = S::M, MB32 = S::MB32, MB16 = S::MB16;
     __shared__ WaveScratch<S> scratch[PF];
     __shared__ float cs_tab[16][2];
+    // two separate LDS objects (not one 2-D array) so the compiler can tell the
+    // buffer being filled by DMA from the one being read
+    __shared__ __attribute__((aligned(1024))) uint8_t gbuf_a[S::G_BLOCKS * 1024];
+    __shared__ __attribute__((aligned(1024))) uint8_t gbuf_b[S::G_BLOCKS * 1024];
 
     const int lane = threadIdx.x & 63;
     const int iF = threadIdx.x >> 6;
@@ -149,41 +160,36 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
     const int64_t offFK = L.off[S::SET_FK], offGK = L.off[S::SET_GK];
     const int64_t offFV = L.off[S::SET_FV], offGV = L.off[S::SET_GV];
 
-    // Loads are skewed by half a tile: the value-side operands of tile t are
-    // requested before its score phase, the key-side operands of tile t+1
-    // before the value phase of tile t, so every load has a phase of work to
-    // hide behind without doubling the registers.
-    bf16x8 fk[RK];
-    uint2 gk[RK][MB32][4];
-    bf16x8 gv[RV][MB16], fv[RV];
-    auto load_key_side = [&](const uint8_t* tile) {
-#pragma unroll
-        for (int r = 0; r < RK; ++r)
-            fk[r] = ld16<bf16x8>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + half) * 512 + s * 16);
-#pragma unroll
-        for (int r = 0; r < RK; ++r)
-#pragma unroll
-            for (int mb = 0; mb < MB32; ++mb)
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    gk[r][mb][a] = ld8(tile + offGK + (int64_t)(r * (M / 8) + mb * 4 + a) * 512 + s * 16 + half * 8);
+    // Pipeline, one tile ahead for every byte:
+    //  * G factors (shared by the PF waves): HBM -> LDS by direct DMA
+    //    (global_load_lds_dwordx4), double-buffered, each wave copying 1 KB
+    //    blocks.  The DMA is issued from inline asm so the compiler does not
+    //    make every LDS read wait for it; the explicit vmcnt(0) below is the
+    //    only wait it needs;
+    //  * the wave's own F slice: HBM -> registers, double-buffered.
+    // At the top of each tile one wait for everything issued a tile earlier
+    // and one barrier (all G blocks landed; the other buffer is free).
+    constexpr int KB = S::GK_BLOCKS, NBLK = S::G_BLOCKS;
+    struct FRegs {
+        bf16x8 fk[RK];
+        bf16x8 fv[RV];
     };
-    auto load_value_side = [&](const uint8_t* tile) {
+    auto issue = [&](const uint8_t* tile, uint8_t* gdst, FRegs& f) {
 #pragma unroll
-        for (int r = 0; r < RV; ++r) {
-#pragma unroll
-            for (int mb = 0; mb < MB16; ++mb)
-                gv[r][mb] = ld16<bf16x8>(tile + offGV + ((int64_t)(r * M + mb * 16 + l16) * 32 + 8 * g16) * 2);
-            fv[r] = ld16<bf16x8>(tile + offFV + ((int64_t)((r * PF + iF) * QF + l16) * 32 + 8 * g16) * 2);
+        for (int k = iF; k < NBLK; k += PF) {
+            const uint8_t* src = k < KB ? tile + offGK + k * 1024 : tile + offGV + (k - KB) * 1024;
+            dma_to_lds16(src + lane * 16, lds_addr(gdst + k * 1024));
         }
+#pragma unroll
+        for (int r = 0; r < RK; ++r)
+            f.fk[r] = ld16<bf16x8>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + half) * 512 + s * 16);
+#pragma unroll
+        for (int r = 0; r < RV; ++r)
+            f.fv[r] = ld16<bf16x8>(tile + offFV + ((int64_t)((r * PF + iF) * QF + l16) * 32 + 8 * g16) * 2);
     };
-    if (first < last) load_key_side(seq + (int64_t)(first / kTileSlots) * L.tile_bytes);
 
-    for (int s0 = first; s0 < last; s0 += kTileSlots) {
-        const uint8_t* tile = seq + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
+    auto process = [&](int s0, const uint8_t* gcur, FRegs& f) {
         const int valid = min(kTileSlots, last - s0);
-        load_value_side(tile);
-
         // ---- scores: W = q' F (MFMA), z = sum G W (VALU) --------------------
 #pragma unroll
         for (int mb = 0; mb < MB32; ++mb) {
@@ -191,12 +197,13 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
 #pragma unroll
             for (int r = 0; r < RK; ++r) {
                 f32x16 w = f32x16{};
-                w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_hi[mb], fk[r], w, 0, 0, 0);
-                w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_lo[mb], fk[r], w, 0, 0, 0);
+                w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_hi[mb], f.fk[r], w, 0, 0, 0);
+                w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_lo[mb], f.fk[r], w, 0, 0, 0);
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
+                    const uint2 gk = *reinterpret_cast<const uint2*>(gcur + (r * (M / 8) + mb * 4 + a) * 512 + s * 16 + half * 8);
                     float g0, g1, g2, g3;
-                    unpack_bf16x4(gk[r][mb][a], g0, g1, g2, g3);
+                    unpack_bf16x4(gk, g0, g1, g2, g3);
                     zp[a] += w[a * 4 + 0] * g0 + w[a * 4 + 1] * g1 + w[a * 4 + 2] * g2 + w[a * 4 + 3] * g3;
                 }
             }
@@ -209,8 +216,11 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
                 // iG = mb*4 + a, jG = 4half + b: add the other half
 #pragma unroll
                 for (int a = 0; a < 4; ++a) zp[a] = sum_halves(zp[a]);
-                ws.z[mb * 4 + 2 * half + 0][s] = ok ? zp[2 * half + 0] : -INFINITY;
-                ws.z[mb * 4 + 2 * half + 1][s] = ok ? zp[2 * half + 1] : -INFINITY;
+                // selects, not a lane-dependent array index (which would go to scratch)
+                const float za = half ? zp[2] : zp[0];
+                const float zb = half ? zp[3] : zp[1];
+                ws.z[mb * 4 + 2 * half + 0][s] = ok ? za : -INFINITY;
+                ws.z[mb * 4 + 2 * half + 1][s] = ok ? zb : -INFINITY;
             } else {
                 // QG == 16: iG = mb*2 + a/2, jG = 8(a%2) + 4half + b
                 float z0 = zp[0] + zp[1], z1 = zp[2] + zp[3];
@@ -233,11 +243,13 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
 #pragma unroll
             for (int x = PG; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x));
             const float m_new = fmaxf(m_run, mt);
-            const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+            // with no slot seen yet (m = -inf) every weight is 0 and alpha 1
+            const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+            const float alpha = fast_exp2(m_run - m_ref);
             float lsum = 0.f;
 #pragma unroll
             for (int u = 0; u < S::TPG; ++u) {
-                const float p = (zl[u] == -INFINITY) ? 0.f : exp2f(zl[u] - m_new);
+                const float p = fast_exp2(zl[u] - m_ref);  // masked slots: 2^-inf = 0
                 ws.p[sm_iG][sm_g * S::TPG + u] = p;
                 lsum += p;
             }
@@ -247,39 +259,61 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
         }
         wave_lds_sync();
 
-        if (s0 + kTileSlots < last) load_key_side(tile + L.tile_bytes);
-
         // ---- values: O = alpha O + (p G^V) F^V (MFMA over slots) -------------
-        if (valid < kTileSlots) {  // slots past the end: zero both operands
+        const uint8_t* gvbase = gcur + KB * 1024;
+        auto values = [&](auto partial_tag) {
+            constexpr bool kPartial = decltype(partial_tag)::value;
+            if constexpr (kPartial) {
+                // slots past the end: zero both operands (the cache may hold NaNs there)
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                if (8 * g16 + k >= valid) {
+                for (int k = 0; k < 8; ++k)
+                    if (8 * g16 + k >= valid)
 #pragma unroll
-                    for (int r = 0; r < RV; ++r) {
-                        fv[r][k] = (__bf16)0.f;
-#pragma unroll
-                        for (int mb = 0; mb < MB16; ++mb) gv[r][mb][k] = (__bf16)0.f;
-                    }
-                }
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB16; ++mb) {
-            const int iG_out = (mb * 16 + 4 * g16) / QG;  // rows of this lane's accumulator
-            const float a = ws.alpha[iG_out];
-            o_acc[mb] *= a;
-            const int iG_row = (mb * 16 + l16) / QG;      // row of this lane's A operand
-            float p[8];
-            ld_lds32(&ws.p[iG_row][8 * g16], p);
-#pragma unroll
-            for (int r = 0; r < RV; ++r) {
-                float gvf[8];
-                unpack_bf16x8(gv[r][mb], gvf);
-                float prod[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) prod[k] = p[k] * gvf[k];
-                o_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack_bf16x8(prod), fv[r], o_acc[mb], 0, 0, 0);
+                        for (int r = 0; r < RV; ++r) f.fv[r][k] = (__bf16)0.f;
             }
-        }
+#pragma unroll
+            for (int mb = 0; mb < MB16; ++mb) {
+                const int iG_out = (mb * 16 + 4 * g16) / QG;  // rows of this lane's accumulator
+                o_acc[mb] *= ws.alpha[iG_out];
+                const int iG_row = (mb * 16 + l16) / QG;      // row of this lane's A operand
+                float p[8];
+                ld_lds32(&ws.p[iG_row][8 * g16], p);
+#pragma unroll
+                for (int r = 0; r < RV; ++r) {
+                    float gvf[8];
+                    unpack_bf16x8(*reinterpret_cast<const bf16x8*>(gvbase + ((r * M + mb * 16 + l16) * 32 + 8 * g16) * 2), gvf);
+                    float prod[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        prod[k] = p[k] * gvf[k];
+                        if constexpr (kPartial) prod[k] = (8 * g16 + k >= valid) ? 0.f : prod[k];
+                    }
+                    o_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack_bf16x8(prod), f.fv[r], o_acc[mb], 0, 0, 0);
+                }
+            }
+        };
+        if (valid < kTileSlots) values(std::true_type{});
+        else values(std::false_type{});
+    };
+
+    FRegs fa, fb;
+    const uint8_t* t0 = seq + (int64_t)(first / kTileSlots) * L.tile_bytes;
+    if (first < last) issue(t0, gbuf_a, fa);
+    for (int s0 = first; s0 < last; s0 += 2 * kTileSlots) {
+        // tile s0: data in gbuf_a and fa
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the DMA and loads issued one tile ago
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const uint8_t* tile = seq + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
+        if (s0 + kTileSlots < last) issue(tile + L.tile_bytes, gbuf_b, fb);
+        process(s0, gbuf_a, fa);
+        if (s0 + kTileSlots >= last) break;
+        // tile s0 + 32: data in gbuf_b and fb
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (s0 + 2 * kTileSlots < last) issue(tile + 2 * L.tile_bytes, gbuf_a, fa);
+        process(s0 + kTileSlots, gbuf_b, fb);
     }
 
     // ---- finish: full sums per head, then write -----------------------------
@@ -329,36 +363,62 @@ struct Cfg : Shape<PG, QG, PF, QF, RK, RV, F_IS_B> {
 };
 
 template <class C>
-hipError_t launch_one(const DecodeParams& P, hipStream_t s) {
-    dim3 grid(P.n_split, P.batch);
-    hipLaunchKernelGGL(decode_mfma_kernel<C>, grid, dim3(C::PF_ * 64), 0, s, P);
-    return hipGetLastError();
+struct Entry {
+    static hipError_t launch(const DecodeParams& P, hipStream_t s) {
+        dim3 grid(P.n_split, P.batch);
+        hipLaunchKernelGGL(decode_mfma_kernel<C>, grid, dim3(C::PF_ * 64), 0, s, P);
+        return hipGetLastError();
+    }
+    // Workgroups of this kernel one CU holds at once (registers and LDS).
+    static int blocks_per_cu() {
+        static std::atomic<int> cached{0};
+        int v = cached.load(std::memory_order_relaxed);
+        if (v > 0) return v;
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<C>, C::PF_ * 64, 0) != hipSuccess ||
+            n <= 0)
+            n = 1;
+        cached.store(n, std::memory_order_relaxed);
+        return n;
+    }
+};
+
+struct MfmaKernel {
+    int p1, p2, q1, q2, r_k, r_v;
+    hipError_t (*launch)(const DecodeParams&, hipStream_t);
+    int (*blocks_per_cu)();
+};
+
+// Shapes with a matrix-core instantiation.  F is the factor whose feature
+// dimension is 16 (B for the first three, A for the last).
+const MfmaKernel kKernels[] = {
+    {4, 4, 8, 16, 2, 2, Entry<Cfg<4, 8, 4, 16, 2, 2, true, 3>>::launch, Entry<Cfg<4, 8, 4, 16, 2, 2, true, 3>>::blocks_per_cu},
+    {4, 4, 8, 16, 1, 1, Entry<Cfg<4, 8, 4, 16, 1, 1, true>>::launch, Entry<Cfg<4, 8, 4, 16, 1, 1, true>>::blocks_per_cu},
+    {8, 4, 8, 16, 2, 4, Entry<Cfg<8, 8, 4, 16, 2, 4, true>>::launch, Entry<Cfg<8, 8, 4, 16, 2, 4, true>>::blocks_per_cu},
+    {4, 8, 16, 8, 4, 4, Entry<Cfg<8, 8, 4, 16, 4, 4, false, 1>>::launch,
+     Entry<Cfg<8, 8, 4, 16, 4, 4, false, 1>>::blocks_per_cu},
+};
+
+const MfmaKernel* find_kernel(const kpa_dims& d, int n_q) {
+    if (d.dtype != KPA_BF16 || n_q != 1) return nullptr;
+    for (const MfmaKernel& k : kKernels)
+        if (k.p1 == d.p1 && k.p2 == d.p2 && k.q1 == d.q1 && k.q2 == d.q2 && k.r_k == d.r_k && k.r_v == d.r_v)
+            return &k;
+    return nullptr;
 }
 
 }  // namespace
 
-// Shapes with a matrix-core instantiation; the dispatcher asks here first.
-bool decode_mfma_supported(const kpa_dims& d, int n_q) {
-    if (d.dtype != KPA_BF16 || n_q != 1) return false;
-    const int k[6] = {d.p1, d.p2, d.q1, d.q2, d.r_k, d.r_v};
-    auto is = [&](int a, int b, int c, int e, int f, int g) {
-        return k[0] == a && k[1] == b && k[2] == c && k[3] == e && k[4] == f && k[5] == g;
-    };
-    return is(4, 4, 8, 16, 2, 2) || is(8, 4, 8, 16, 2, 4) || is(4, 8, 16, 8, 4, 4) || is(4, 4, 8, 16, 1, 1);
+bool decode_mfma_supported(const kpa_dims& d, int n_q) { return find_kernel(d, n_q) != nullptr; }
+
+int decode_mfma_blocks_per_cu(const kpa_dims& d) {
+    const MfmaKernel* k = find_kernel(d, 1);
+    return k ? k->blocks_per_cu() : 1;
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s) {
-    const kpa_dims& d = P.d;
-    // F is the factor with feature dimension 16.
-    if (d.p1 == 4 && d.p2 == 4 && d.q1 == 8 && d.q2 == 16 && d.r_k == 2 && d.r_v == 2)
-        return launch_one<Cfg<4, 8, 4, 16, 2, 2, true>>(P, s);
-    if (d.p1 == 4 && d.p2 == 4 && d.q1 == 8 && d.q2 == 16 && d.r_k == 1 && d.r_v == 1)
-        return launch_one<Cfg<4, 8, 4, 16, 1, 1, true>>(P, s);
-    if (d.p1 == 8 && d.p2 == 4 && d.q1 == 8 && d.q2 == 16 && d.r_k == 2 && d.r_v == 4)
-        return launch_one<Cfg<8, 8, 4, 16, 2, 4, true>>(P, s);
-    if (d.p1 == 4 && d.p2 == 8 && d.q1 == 16 && d.q2 == 8 && d.r_k == 4 && d.r_v == 4)
-        return launch_one<Cfg<8, 8, 4, 16, 4, 4, false, 1>>(P, s);
-    return hipErrorInvalidValue;
+    const MfmaKernel* k = find_kernel(P.d, P.n_q);
+    return k ? k->launch(P, s) : hipErrorInvalidValue;
 }
 
 }  // namespace kpa

@@ -18,7 +18,7 @@ struct Plan {
 };
 
 // Splits merged by one merge block; more splits go through a second level.
-constexpr int kMergeGroup = 32;
+constexpr int kMergeGroup = 64;
 
 inline const char* path_name(Path p) {
     switch (p) {
@@ -45,9 +45,11 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
     if (num_splits > 0) {
         s = num_splits;
     } else {
-        // workgroups in flight: the VALU kernel is one 256-thread group per
-        // chunk; the matrix-core kernel one wave per (chunk, iF)
-        const int64_t target = (p.path == Path::kMfmaSq ? 2LL : 4LL) * cus;
+        // one full round of workgroups: as many as the CUs hold at once (the
+        // matrix-core kernel's occupancy from its registers and LDS; the VALU
+        // kernel, a fallback, four per CU)
+        const int64_t per_cu = p.path == Path::kMfmaSq ? decode_mfma_blocks_per_cu(d) : 4;
+        const int64_t target = per_cu * cus;
         s = rows > 0 ? (target + rows - 1) / rows : 1;
         const int64_t min_tiles_per_chunk = 2;
         const int64_t cap = (tiles + min_tiles_per_chunk - 1) / min_tiles_per_chunk;
@@ -57,8 +59,9 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
     if (s < 1) s = 1;
     int64_t chunk = tiles > 0 ? (tiles + s - 1) / s : 1;
     s = tiles > 0 ? (tiles + chunk - 1) / chunk : 1;
-    if (s > 65535) {  // grid.x limit; widen the chunks
-        chunk = (tiles + 65535 - 1) / 65535;
+    const int64_t s_max = (int64_t)kMergeGroup * kMergeGroup;  // two merge levels
+    if (s > s_max) {  // widen the chunks
+        chunk = (tiles + s_max - 1) / s_max;
         s = (tiles + chunk - 1) / chunk;
     }
     p.n_split = (int32_t)s;

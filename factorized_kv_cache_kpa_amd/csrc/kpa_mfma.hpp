@@ -19,6 +19,8 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 template <typename T>
 __device__ __forceinline__ T ld16(const uint8_t* p) {
@@ -61,13 +63,19 @@ __device__ __forceinline__ void unpack_bf16x8(bf16x8 v, float* out) {
     }
 }
 
-// Round 8 floats to bf16 (nearest even).
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// Round 8 floats to bf16 (nearest even), two per v_cvt_pk_bf16_f32.
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
-    bf16x8 r;
+    u32x4 r;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = (__bf16)v[k];
-    return r;
+    for (int k = 0; k < 4; ++k)
+        r[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2 * k], v[2 * k + 1]}, bf16x2));
+    return __builtin_bit_cast(bf16x8, r);
 }
+
+// 2^x on the hardware exp unit (x <= 0 here; results below 2^-126 flush to 0).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // v = hi + lo with hi = bf16(v) and lo = bf16(v - hi).
 __device__ __forceinline__ void split_bf16x8(const float* v, bf16x8& hi, bf16x8& lo) {
@@ -85,6 +93,23 @@ __device__ __forceinline__ float swap_halves(float x) {
     // r[0] holds the lower half's value in every lane, r[1] the upper half's.
     return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
+
+// LDS byte address of a __shared__ pointer, as a wave-uniform value.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+// One wave copies 64 x 16 B from global memory (each lane its own address)
+// into LDS at [lds, lds + 1 KB) without passing through registers
+// (global_load_lds_dwordx4; M0 holds the LDS base).  Completion is tracked by
+// vmcnt; the caller waits with s_waitcnt vmcnt before reading the LDS bytes.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_to_lds16(const void* gaddr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gaddr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // Make this wave's LDS writes visible to its other lanes (the wave's LDS
 // operations complete in order; the fences keep the compiler from moving

@@ -13,7 +13,8 @@
 // chunks (a long single sequence split over the whole chip) the blocks of a
 // (row, head) each write a second-level partial (M_g, L_g, O_g) -- the same
 // triple, so the same rule combines them -- and the last block to arrive
-// (an arrival counter, cleared by the decode kernel) merges those.
+// (an arrival counter, cleared by the decode kernel) merges those.  The
+// planner keeps the chunk count <= kMergeGroup^2.
 #include "kpa_common.hpp"
 #include "kpa_dispatch.hpp"
 
@@ -22,54 +23,58 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Combine n (max, sum) pairs into weights w[k] = 2^(m_k - M) (0 for empty
-// chunks); returns M and L = sum_k w_k l_k through LDS.  Block-wide.
-__device__ void merge_weights(const float* ml, int stride, int n, float* w, float* red, float& M_out,
-                              float& L_out) {
-    float m = -INFINITY;
-    for (int k = threadIdx.x; k < n; k += blockDim.x) m = fmaxf(m, ml[(int64_t)k * stride]);
-    for (int x = 32; x > 0; x >>= 1) m = fmaxf(m, __shfl_xor(m, x));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    float M = -INFINITY;
-    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) M = fmaxf(M, red[k]);
-    __syncthreads();
-    float l = 0.f;
-    for (int k = threadIdx.x; k < n; k += blockDim.x) {
-        const float mk = ml[(int64_t)k * stride];
-        const float wk = (mk == -INFINITY) ? 0.f : exp2f(mk - M);
-        w[k] = wk;
-        l += wk * ml[(int64_t)k * stride + 1];
-    }
-    for (int x = 32; x > 0; x >>= 1) l += __shfl_xor(l, x);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = l;
-    __syncthreads();
-    float L = 0.f;
-    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) L += red[k];
-    M_out = M;
-    L_out = L;
-    __syncthreads();
-}
+// One (row, head) over n <= kMergeGroup chunks, for the thread's output
+// element j (j < dh).  Every load -- the chunk maxima, sums and outputs -- is
+// issued up front; the weights need only a block-wide max, so the whole merge
+// costs one memory round trip.  Returns (M, L) and the unnormalised sum.
+struct MergeOut {
+    float M, L, acc;
+};
 
-// sum_k w[k] * o[k * stride + j] with several loads in flight.
-__device__ __forceinline__ float weighted_sum(const float* w, const float* o, int64_t stride, int n) {
-    float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-    int k = 0;
-    for (; k + 4 <= n; k += 4) {
-        acc0 += w[k] * o[k * stride];
-        acc1 += w[k + 1] * o[(k + 1) * stride];
-        acc2 += w[k + 2] * o[(k + 2) * stride];
-        acc3 += w[k + 3] * o[(k + 3) * stride];
+__device__ MergeOut merge_group(const float* ml, int ml_stride, const float* o, int64_t o_stride, int n,
+                                int j, bool has_j, float* red) {
+    float m = -INFINITY, l = 0.f;
+    if ((int)threadIdx.x < n) {  // one chunk's (max, sum) per thread
+        m = ml[(int64_t)threadIdx.x * ml_stride];
+        l = ml[(int64_t)threadIdx.x * ml_stride + 1];
     }
-    for (; k < n; ++k) acc0 += w[k] * o[k * stride];
-    return (acc0 + acc1) + (acc2 + acc3);
+    // block max of the chunk maxima
+    float M = m;
+    for (int x = 32; x > 0; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = M;
+    __syncthreads();
+    M = -INFINITY;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) M = fmaxf(M, red[k]);
+    // this thread's chunk weight, the weighted sum of sums, and every weight in LDS
+    const float wk = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    float L = wk * l;
+    for (int x = 32; x > 0; x >>= 1) L += __shfl_xor(L, x);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = L;
+    red[4 + threadIdx.x] = wk;  // red[4 .. 4 + blockDim)
+    __syncthreads();
+    L = 0.f;
+    for (int k = 0; k < (int)(blockDim.x >> 6); ++k) L += red[k];
+    float acc = 0.f;
+    if (has_j) {
+        const float* oj = o + j;
+        int k = 0;
+        for (; k + 8 <= n; k += 8) {  // eight loads in flight
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = oj[(k + u) * o_stride];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += red[4 + k + u] * v[u];
+        }
+        for (; k < n; ++k) acc += red[4 + k] * oj[k * o_stride];
+    }
+    __syncthreads();
+    return {M, L, acc};
 }
 
 __global__ void __launch_bounds__(256) merge_kernel(DecodeParams P) {
-    __shared__ float w[kMergeGroup];
-    __shared__ float red[4];
+    __shared__ float red[4 + 256];
     __shared__ int is_last;
-    extern __shared__ float w2[];  // [n_group] second-level weights
     const int h = P.d.p1 * P.d.p2, dh = P.d.q1 * P.d.q2;
     const int64_t row = blockIdx.x / h;  // (b, n)
     const int i = blockIdx.x % h;
@@ -77,30 +82,24 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeParams P) {
     const int S = P.n_split, G = P.n_group;
     const int k0 = g * kMergeGroup;
     const int n = min(S - k0, kMergeGroup);
+    const int j = threadIdx.x;  // blockDim.x >= dh and >= kMergeGroup
+    const bool has_j = j < dh;
 
-    const float* ml = P.part_ml + ((row * S + k0) * h + i) * 2;
-    const float* po = P.part_o + ((row * S + k0) * h + i) * (int64_t)dh;
-    float M, L;
-    merge_weights(ml, h * 2, n, w, red, M, L);
-    float acc[2];
-    int nj = 0;
-    for (int j = threadIdx.x; j < dh; j += blockDim.x) acc[nj++] = weighted_sum(w, po + j, (int64_t)h * dh, n);
-
+    MergeOut r = merge_group(P.part_ml + ((row * S + k0) * h + i) * 2, h * 2,
+                             P.part_o + ((row * S + k0) * h + i) * (int64_t)dh, (int64_t)h * dh, n, j, has_j, red);
     if (G == 1) {
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        nj = 0;
-        for (int j = threadIdx.x; j < dh; j += blockDim.x) P.out[(row * h + i) * dh + j] = acc[nj++] * inv;
-        if (P.lse && threadIdx.x == 0) P.lse[row * h + i] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+        const float inv = r.L > 0.f ? 1.f / r.L : 0.f;
+        if (has_j) P.out[(row * h + i) * dh + j] = r.acc * inv;
+        if (P.lse && threadIdx.x == 0) P.lse[row * h + i] = r.L > 0.f ? (r.M + log2f(r.L)) * kLn2 : -INFINITY;
         return;
     }
 
     // second level: publish this group's triple, the last block merges all groups
     const int64_t prow = (row * G + g) * h + i;
-    nj = 0;
-    for (int j = threadIdx.x; j < dh; j += blockDim.x) P.part2_o[prow * dh + j] = acc[nj++];
+    if (has_j) P.part2_o[prow * dh + j] = r.acc;
     if (threadIdx.x == 0) {
-        P.part2_ml[prow * 2] = M;
-        P.part2_ml[prow * 2 + 1] = L;
+        P.part2_ml[prow * 2] = r.M;
+        P.part2_ml[prow * 2 + 1] = r.L;
     }
     __threadfence();
     __syncthreads();
@@ -108,14 +107,13 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeParams P) {
     __syncthreads();
     if (!is_last) return;
     __threadfence();
-    const float* ml2 = P.part2_ml + (row * G * h + i) * 2;
-    const float* po2 = P.part2_o + (row * G * h + i) * (int64_t)dh;
-    merge_weights(ml2, h * 2, G, w2, red, M, L);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int j = threadIdx.x; j < dh; j += blockDim.x)
-        P.out[(row * h + i) * dh + j] = weighted_sum(w2, po2 + j, (int64_t)h * dh, G) * inv;
+    // G <= kMergeGroup (the planner caps the chunk count)
+    r = merge_group(P.part2_ml + (row * G * h + i) * 2, h * 2, P.part2_o + (row * G * h + i) * (int64_t)dh,
+                    (int64_t)h * dh, G, j, has_j, red);
+    const float inv = r.L > 0.f ? 1.f / r.L : 0.f;
+    if (has_j) P.out[(row * h + i) * dh + j] = r.acc * inv;
     if (threadIdx.x == 0) {
-        if (P.lse) P.lse[row * h + i] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+        if (P.lse) P.lse[row * h + i] = r.L > 0.f ? (r.M + log2f(r.L)) * kLn2 : -INFINITY;
         P.merge_count[row * h + i] = 0u;
     }
 }
@@ -124,9 +122,8 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeParams P) {
 
 hipError_t launch_merge(const DecodeParams& P, hipStream_t s) {
     const int h = P.d.p1 * P.d.p2, dh = P.d.q1 * P.d.q2;
-    const int threads = dh <= 64 ? 64 : (dh <= 128 ? 128 : 256);
-    const size_t smem = P.n_group > 1 ? P.n_group * sizeof(float) : 0;
-    hipLaunchKernelGGL(merge_kernel, dim3(P.batch * P.n_q * h, P.n_group), dim3(threads), smem, s, P);
+    const int threads = dh <= 64 ? 64 : (dh <= 128 ? 128 : 256);  // >= kMergeGroup as well
+    hipLaunchKernelGGL(merge_kernel, dim3(P.batch * P.n_q * h, P.n_group), dim3(threads), 0, s, P);
     return hipGetLastError();
 }
 
