@@ -1,4 +1,5 @@
-// Single-query split-KV decode on the bf16 matrix cores (gfx950 MFMA).
+// Split-KV decode on the bf16 matrix cores (gfx950 MFMA), one query or a
+// causal chunk of queries per sequence.
 //
 // Math ([KPA] = "Kronecker Product Attention: Memory-Efficient KV Compression
 // via Structured Factorization"; [TPA] = "Tensor Product Attention Is All You
@@ -8,23 +9,27 @@
 // Written with the two factors of a head: call F the factor whose feature
 // dimension is 16 (it is contracted on the matrix cores) and G the other one.
 // Head i = (iG, iF), feature j = (jG, jF) in the block order of the Kronecker
-// product ([KPA] Def. 2.1).  Then, per rank r and cached slot s,
-//   W_r[(iG,jG), s] = sum_jF q'[iG,iF,jG,jF] F_r[s,iF,jF]      (MFMA 32x32x16:
-//        M = (iG,jG), N = 32 slots, K = jF -- the query is the stationary
-//        operand, exactly as a grouped-query decode shares K across heads)
-//   z[iG,iF,s] = sum_r sum_jG G_r[s,iG,jG] W_r[(iG,jG),s]       (VALU, in lane)
+// product ([KPA] Def. 2.1).  Then, per query n, rank r and cached slot s,
+//   W_r[(n,iG,jG), s] = sum_jF q'[n,iG,iF,jG,jF] F_r[s,iF,jF]   (MFMA 32x32x16:
+//        M = (n,iG,jG), N = 32 slots, K = jF -- the queries are the
+//        stationary operand, as a grouped-query decode shares K across heads)
+//   z[n,iG,iF,s] = sum_r sum_jG G_r[s,iG,jG] W_r[(n,iG,jG),s]   (VALU, in lane)
 // which is [KPA] Prop. 2.2 / Eq. (6) with a dense query: contract with one
 // factor, then the other; K is never rebuilt.  The value side, per iF,
-//   O[(iG,jG), jF] += sum_{r,s} (p[iG,iF,s] G^V_r[s,iG,jG]) F^V_r[s,iF,jF]
+//   O[(n,iG,jG), jF] += sum_{r,s} (p[n,iG,iF,s] G^V_r[s,iG,jG]) F^V_r[s,iF,jF]
 // is a GEMM over slots (MFMA 16x16x32: M = (iG,jG), N = jF, K = 32 slots),
 // with the softmax weight folded into the G factor on the VALU.  The online
-// softmax (running max and sum per head, rescaling O when the max grows) is
-// the blocked online log-sum-exp of FlashTPA decoding ([TPA]).
+// softmax (running max and sum per (query, head), rescaling O when the max
+// grows) is the blocked online log-sum-exp of FlashTPA decoding ([TPA]).
 //
-// Work split: one wave per (sequence, KV chunk, iF).  The PF waves of a
-// workgroup share the G factors through L1; each wave reads only its own F
-// slice, so every cache byte crosses HBM once.  No cross-wave reduction: the
-// heads (., iF) of a wave are its own.
+// Work split: a workgroup owns one KV chunk of one sequence for a group of
+// queries; its waves are (iF, query subgroup).  The G factors of a tile are
+// shared by every wave of the workgroup: they go HBM -> LDS by direct DMA,
+// one tile ahead, double-buffered.  Each wave's F slice goes HBM ->
+// registers, one tile ahead.  No cross-wave reduction: the (query, head)
+// rows of a wave are its own.  With several query groups per chunk, the
+// workgroups of one chunk are placed on the same XCD so the tile is fetched
+// from HBM once and shared through that XCD's L2.
 //
 // Precision: bf16 factors exactly; the rotated, scaled query is split into
 // bf16 hi + lo parts (two MFMAs) so it carries ~16 bits; the value operand
@@ -41,10 +46,18 @@
 namespace kpa {
 namespace {
 
-template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B>
-struct Shape {
-    static constexpr int PG_ = PG, QG_ = QG, PF_ = PF, QF_ = QF;
-    static constexpr int M = PG * QG;  // rows (iG, jG)
+constexpr int kXcds = 8;  // workgroups are dealt to the 8 XCDs round-robin
+
+template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int NQW, int NQG, int MW>
+struct Cfg {
+    static constexpr int PG_ = PG, QG_ = QG, PF_ = PF, QF_ = QF, RK_ = RK, RV_ = RV;
+    static constexpr bool F_IS_B_ = F_IS_B;
+    static constexpr int NQW_ = NQW;                 // queries per wave
+    static constexpr int NQG_ = NQG;                 // query subgroups per workgroup
+    static constexpr int QPW = NQW * NQG;            // queries per workgroup
+    static constexpr int WAVES = PF * NQG;
+    static constexpr int MIN_WAVES = MW;             // waves per SIMD the registers must allow
+    static constexpr int M = PG * QG;                // rows (iG, jG) per query
     static constexpr int MB32 = M / 32;
     static constexpr int MB16 = M / 16;
     static constexpr int H = PG * PF;
@@ -53,8 +66,11 @@ struct Shape {
     // chunks (M/8 chunks of 512 B per rank), value set R_V*M elements x 32 slots
     static constexpr int GK_BLOCKS = RK * M * 64 / 1024;
     static constexpr int G_BLOCKS = (RK + RV) * M * 64 / 1024;
-    static constexpr int GROUPS = 64 / PG;      // softmax: lanes per head
-    static constexpr int TPG = 32 / GROUPS;     // softmax: slots per lane
+    // softmax: NQW*PG (query, head) rows per wave spread over 64 lanes
+    static constexpr int ROWS = NQW * PG;
+    static constexpr int GROUPS = 64 / ROWS;         // lanes per row
+    static constexpr int TPG = 32 / GROUPS;          // slots per lane
+    static constexpr int QROT = F_IS_B ? QF : QG;    // rotary pairs live in B's feature dim
     // cache sets
     static constexpr int SET_GK = F_IS_B ? 0 : 1;
     static constexpr int SET_FK = F_IS_B ? 1 : 0;
@@ -63,57 +79,72 @@ struct Shape {
     static_assert(QF == 16, "the MFMA-side feature dimension must be 16");
     static_assert(M % 32 == 0, "rows (iG, jG) must fill 32-row MFMA blocks");
     static_assert(QG == 4 || QG == 8 || QG == 16, "G-side feature dimension 4, 8 or 16");
-    static_assert(64 % PG == 0 && PG >= 2, "PG must divide 64");
+    static_assert(64 % ROWS == 0 && ROWS >= 2, "query-head rows of a wave must divide 64");
+    static_assert(QROT <= 16, "rotary table holds 8 pairs");
     static_assert(RK <= 4 && RV <= 4, "ranks up to 4");
+    static_assert(WAVES * 64 <= 1024, "at most 16 waves per workgroup");
     __device__ static int head(int iG, int iF) { return F_IS_B ? iG * PF + iF : iF * PG + iG; }
     __device__ static int feat(int jG, int jF) { return F_IS_B ? jG * QF + jF : jF * QG + jG; }
 };
 
-// Per-wave LDS scratch.
+// Per-wave LDS scratch: scores, overwritten in place by the softmax weights.
 template <class S>
 struct alignas(16) WaveScratch {
-    float z[S::PG_][32];
-    float p[S::PG_][32];
-    float alpha[S::PG_];
-    float m_fin[S::PG_];
-    float l_fin[S::PG_];
+    float zp[S::ROWS][32];
+    float alpha[S::ROWS];
+    float m_fin[S::ROWS];
+    float l_fin[S::ROWS];
 };
 
 template <class S>
-__global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(DecodeParams P) {
+__global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kernel(DecodeParams P) {
     constexpr int PG = S::PG_, QG = S::QG_, PF = S::PF_, QF = S::QF_, RK = S::RK_, RV = S::RV_;
-    constexpr int M = S::M, MB32 = S::MB32, MB16 = S::MB16;
-    __shared__ WaveScratch<S> scratch[PF];
-    __shared__ float cs_tab[16][2];
+    constexpr int M = S::M, MB32 = S::MB32, MB16 = S::MB16, NQW = S::NQW_;
+    __shared__ WaveScratch<S> scratch[S::WAVES];
+    __shared__ float cs_tab[S::QPW][8][2];
     // two separate LDS objects (not one 2-D array) so the compiler can tell the
     // buffer being filled by DMA from the one being read
     __shared__ __attribute__((aligned(1024))) uint8_t gbuf_a[S::G_BLOCKS * 1024];
     __shared__ __attribute__((aligned(1024))) uint8_t gbuf_b[S::G_BLOCKS * 1024];
 
     const int lane = threadIdx.x & 63;
-    const int iF = threadIdx.x >> 6;
+    const int wave = threadIdx.x >> 6;
+    const int iF = wave % PF;
+    const int qsub = wave / PF;
     const int half = lane >> 5;
     const int s = lane & 31;       // slot within the tile for the score side
     const int l16 = lane & 15;
     const int g16 = lane >> 4;     // 8-slot group for the value side
-    const int split = blockIdx.x, b = blockIdx.y;
-    WaveScratch<S>& ws = scratch[iF];
+    const int b = blockIdx.y;
+    // workgroup -> (chunk, query group): the query groups of a chunk share an XCD
+    const int qwg_count = (P.n_q + S::QPW - 1) / S::QPW;
+    const int bx = blockIdx.x;
+    const int split = (bx / (kXcds * qwg_count)) * kXcds + bx % kXcds;
+    const int qwg = (bx / kXcds) % qwg_count;
+    if (split >= P.n_split) return;  // padding of the grid to a multiple of the XCD count
+    WaveScratch<S>& ws = scratch[wave];
     const Layout& L = P.L;
+    const int n0 = qwg * S::QPW + qsub * NQW;  // first query of this wave
 
-    // ---- rotated, scaled query as MFMA A operands (hi + lo bf16) ------------
-    const int qp = P.q_pos[b];
-    constexpr int QROT = S::F_IS_B_ ? QF : QG;  // rotary pairs live in B's feature dim
-    if (threadIdx.x < QROT / 2) {
-        const double theta = exp2(-(2.0 * threadIdx.x / QROT) * log2((double)P.d.rope_base));
+    // ---- rotated, scaled queries as MFMA A operands (hi + lo bf16) ----------
+    for (int e = threadIdx.x; e < S::QPW * (S::QROT / 2); e += S::WAVES * 64) {
+        const int nq = e / (S::QROT / 2), m = e % (S::QROT / 2);
+        const int n = min(qwg * S::QPW + nq, P.n_q - 1);
+        const double theta = exp2(-(2.0 * m / S::QROT) * log2((double)P.d.rope_base));
         double sn, c;
-        sincos((double)qp * theta, &sn, &c);
-        cs_tab[threadIdx.x][0] = (float)c;
-        cs_tab[threadIdx.x][1] = (float)sn;
+        sincos((double)P.q_pos[(int64_t)b * P.n_q + n] * theta, &sn, &c);
+        cs_tab[nq][m][0] = (float)c;
+        cs_tab[nq][m][1] = (float)sn;
     }
+    for (int n = 0; n < S::QPW; ++n)  // every thread takes part: the clear strides over heads
+        if (qwg * S::QPW + n < P.n_q) clear_merge_counters(P, (int64_t)b * P.n_q + qwg * S::QPW + n, split);
     __syncthreads();
-    bf16x8 q_hi[MB32], q_lo[MB32];
-    {
-        const float* qg = P.q + (int64_t)b * S::H * S::DH;
+    bf16x8 q_hi[NQW][MB32], q_lo[NQW][MB32];
+#pragma unroll
+    for (int u = 0; u < NQW; ++u) {
+        const int n = min(n0 + u, P.n_q - 1);  // queries past n_q compute and are discarded
+        const float* qg = P.q + ((int64_t)b * P.n_q + n) * S::H * S::DH;
+        const int nq = qsub * NQW + u;
 #pragma unroll
         for (int mb = 0; mb < MB32; ++mb) {
             const int R = mb * 32 + s;
@@ -136,32 +167,39 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
                     m = jG >> 1;
                     first = !(jG & 1);
                 }
-                const float c = cs_tab[m][0], sn = cs_tab[m][1];
+                const float c = cs_tab[nq][m][0], sn = cs_tab[nq][m][1];
                 // (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
                 v[k] = (first ? (x * c - y * sn) : (y * sn + x * c)) * P.q_scale;
             }
-            split_bf16x8(v, q_hi[mb], q_lo[mb]);
+            split_bf16x8(v, q_hi[u][mb], q_lo[u][mb]);
         }
     }
 
-    f32x4 o_acc[MB16];
+    f32x4 o_acc[NQW][MB16];
 #pragma unroll
-    for (int k = 0; k < MB16; ++k) o_acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // softmax state for head (iG = lane % PG, iF); l is this lane's partial sum
-    const int sm_iG = lane % PG, sm_g = lane / PG;
+    for (int u = 0; u < NQW; ++u)
+#pragma unroll
+        for (int k = 0; k < MB16; ++k) o_acc[u][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // softmax state for row sm_row = (query u, head iG) of this wave; l is this
+    // lane's partial sum over its slots
+    const int sm_row = lane % S::ROWS, sm_g = lane / S::ROWS;
     float m_run = -INFINITY, l_run = 0.f;
 
-    clear_merge_counters(P, b, split);
-    const int vis = visible_slots(P, b, 0);
+    // visible slots: per query (causal), and the workgroup's furthest
+    int vis[NQW];
+#pragma unroll
+    for (int u = 0; u < NQW; ++u) vis[u] = n0 + u < P.n_q ? visible_slots(P, b, n0 + u) : 0;
+    int vis_wg = 0;
+    for (int n = qwg * S::QPW; n < min(P.n_q, (qwg + 1) * S::QPW); ++n) vis_wg = max(vis_wg, visible_slots(P, b, n));
     const int first = split * P.chunk_tiles * kTileSlots;
     int last = first + P.chunk_tiles * kTileSlots;
-    if (last > vis) last = vis;
+    if (last > vis_wg) last = vis_wg;
     const uint8_t* seq = P.cache + (int64_t)b * L.n_tiles * L.tile_bytes;
     const int64_t offFK = L.off[S::SET_FK], offGK = L.off[S::SET_GK];
     const int64_t offFV = L.off[S::SET_FV], offGV = L.off[S::SET_GV];
 
     // Pipeline, one tile ahead for every byte:
-    //  * G factors (shared by the PF waves): HBM -> LDS by direct DMA
+    //  * G factors (shared by the workgroup's waves): HBM -> LDS by direct DMA
     //    (global_load_lds_dwordx4), double-buffered, each wave copying 1 KB
     //    blocks.  The DMA is issued from inline asm so the compiler does not
     //    make every LDS read wait for it; the explicit vmcnt(0) below is the
@@ -176,7 +214,7 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
     };
     auto issue = [&](const uint8_t* tile, uint8_t* gdst, FRegs& f) {
 #pragma unroll
-        for (int k = iF; k < NBLK; k += PF) {
+        for (int k = wave; k < NBLK; k += S::WAVES) {
             const uint8_t* src = k < KB ? tile + offGK + k * 1024 : tile + offGV + (k - KB) * 1024;
             dma_to_lds16(src + lane * 16, lds_addr(gdst + k * 1024));
         }
@@ -193,69 +231,84 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
         // ---- scores: W = q' F (MFMA), z = sum G W (VALU) --------------------
 #pragma unroll
         for (int mb = 0; mb < MB32; ++mb) {
-            float zp[4] = {0.f, 0.f, 0.f, 0.f};
+            float zp[NQW][4];
+#pragma unroll
+            for (int u = 0; u < NQW; ++u)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) zp[u][a] = 0.f;
 #pragma unroll
             for (int r = 0; r < RK; ++r) {
-                f32x16 w = f32x16{};
-                w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_hi[mb], f.fk[r], w, 0, 0, 0);
-                w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_lo[mb], f.fk[r], w, 0, 0, 0);
+                // this lane's G values for rows 8a + 4half + b, shared by every query
+                float g[4][4];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     const uint2 gk = *reinterpret_cast<const uint2*>(gcur + (r * (M / 8) + mb * 4 + a) * 512 + s * 16 + half * 8);
-                    float g0, g1, g2, g3;
-                    unpack_bf16x4(gk, g0, g1, g2, g3);
-                    zp[a] += w[a * 4 + 0] * g0 + w[a * 4 + 1] * g1 + w[a * 4 + 2] * g2 + w[a * 4 + 3] * g3;
+                    unpack_bf16x4(gk, g[a][0], g[a][1], g[a][2], g[a][3]);
+                }
+#pragma unroll
+                for (int u = 0; u < NQW; ++u) {
+                    f32x16 w = f32x16{};
+                    w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_hi[u][mb], f.fk[r], w, 0, 0, 0);
+                    w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_lo[u][mb], f.fk[r], w, 0, 0, 0);
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        zp[u][a] += w[a * 4 + 0] * g[a][0] + w[a * 4 + 1] * g[a][1] + w[a * 4 + 2] * g[a][2] +
+                                    w[a * 4 + 3] * g[a][3];
                 }
             }
-            const bool ok = s < valid;
-            if constexpr (QG == 4) {
-                // rows 8a + 4half + b: iG = mb*8 + 2a + half, jG = b -- complete in lane
 #pragma unroll
-                for (int a = 0; a < 4; ++a) ws.z[mb * 8 + 2 * a + half][s] = ok ? zp[a] : -INFINITY;
-            } else if constexpr (QG == 8) {
-                // iG = mb*4 + a, jG = 4half + b: add the other half
+            for (int u = 0; u < NQW; ++u) {
+                const bool ok = s0 + s < vis[u] && s < valid;  // causal mask per query
+                float* zrow = &ws.zp[u * PG][0];
+                if constexpr (QG == 4) {
+                    // rows 8a + 4half + b: iG = mb*8 + 2a + half, jG = b -- complete in lane
 #pragma unroll
-                for (int a = 0; a < 4; ++a) zp[a] = sum_halves(zp[a]);
-                // selects, not a lane-dependent array index (which would go to scratch)
-                const float za = half ? zp[2] : zp[0];
-                const float zb = half ? zp[3] : zp[1];
-                ws.z[mb * 4 + 2 * half + 0][s] = ok ? za : -INFINITY;
-                ws.z[mb * 4 + 2 * half + 1][s] = ok ? zb : -INFINITY;
-            } else {
-                // QG == 16: iG = mb*2 + a/2, jG = 8(a%2) + 4half + b
-                float z0 = zp[0] + zp[1], z1 = zp[2] + zp[3];
-                z0 = sum_halves(z0);
-                z1 = sum_halves(z1);
-                ws.z[mb * 2 + half][s] = ok ? (half ? z1 : z0) : -INFINITY;
+                    for (int a = 0; a < 4; ++a) zrow[(mb * 8 + 2 * a + half) * 32 + s] = ok ? zp[u][a] : -INFINITY;
+                } else if constexpr (QG == 8) {
+                    // iG = mb*4 + a, jG = 4half + b: add the other half
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) zp[u][a] = sum_halves(zp[u][a]);
+                    // selects, not a lane-dependent array index (which would go to scratch)
+                    const float za = half ? zp[u][2] : zp[u][0];
+                    const float zb = half ? zp[u][3] : zp[u][1];
+                    zrow[(mb * 4 + 2 * half + 0) * 32 + s] = ok ? za : -INFINITY;
+                    zrow[(mb * 4 + 2 * half + 1) * 32 + s] = ok ? zb : -INFINITY;
+                } else {
+                    // QG == 16: iG = mb*2 + a/2, jG = 8(a%2) + 4half + b
+                    float z0 = zp[u][0] + zp[u][1], z1 = zp[u][2] + zp[u][3];
+                    z0 = sum_halves(z0);
+                    z1 = sum_halves(z1);
+                    zrow[(mb * 2 + half) * 32 + s] = ok ? (half ? z1 : z0) : -INFINITY;
+                }
             }
         }
         wave_lds_sync();
 
-        // ---- online softmax for the wave's PG heads --------------------------
+        // ---- online softmax for the wave's (query, head) rows -----------------
         {
             float zl[S::TPG];
             float mt = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < S::TPG; ++u) {
-                zl[u] = ws.z[sm_iG][sm_g * S::TPG + u];
-                mt = fmaxf(mt, zl[u]);
+            for (int t = 0; t < S::TPG; ++t) {
+                zl[t] = ws.zp[sm_row][sm_g * S::TPG + t];
+                mt = fmaxf(mt, zl[t]);
             }
 #pragma unroll
-            for (int x = PG; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x));
+            for (int x = S::ROWS; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x));
             const float m_new = fmaxf(m_run, mt);
             // with no slot seen yet (m = -inf) every weight is 0 and alpha 1
             const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
             const float alpha = fast_exp2(m_run - m_ref);
             float lsum = 0.f;
 #pragma unroll
-            for (int u = 0; u < S::TPG; ++u) {
-                const float p = fast_exp2(zl[u] - m_ref);  // masked slots: 2^-inf = 0
-                ws.p[sm_iG][sm_g * S::TPG + u] = p;
+            for (int t = 0; t < S::TPG; ++t) {
+                const float p = fast_exp2(zl[t] - m_ref);  // masked slots: 2^-inf = 0
+                ws.zp[sm_row][sm_g * S::TPG + t] = p;
                 lsum += p;
             }
             l_run = l_run * alpha + lsum;
             m_run = m_new;
-            if (sm_g == 0) ws.alpha[sm_iG] = alpha;
+            if (sm_g == 0) ws.alpha[sm_row] = alpha;
         }
         wave_lds_sync();
 
@@ -274,21 +327,27 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
 #pragma unroll
             for (int mb = 0; mb < MB16; ++mb) {
                 const int iG_out = (mb * 16 + 4 * g16) / QG;  // rows of this lane's accumulator
-                o_acc[mb] *= ws.alpha[iG_out];
                 const int iG_row = (mb * 16 + l16) / QG;      // row of this lane's A operand
-                float p[8];
-                ld_lds32(&ws.p[iG_row][8 * g16], p);
+                float p[NQW][8];
+#pragma unroll
+                for (int u = 0; u < NQW; ++u) {
+                    o_acc[u][mb] *= ws.alpha[u * PG + iG_out];
+                    ld_lds32(&ws.zp[u * PG + iG_row][8 * g16], p[u]);
+                }
 #pragma unroll
                 for (int r = 0; r < RV; ++r) {
                     float gvf[8];
                     unpack_bf16x8(*reinterpret_cast<const bf16x8*>(gvbase + ((r * M + mb * 16 + l16) * 32 + 8 * g16) * 2), gvf);
-                    float prod[8];
+                    if constexpr (kPartial)
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        prod[k] = p[k] * gvf[k];
-                        if constexpr (kPartial) prod[k] = (8 * g16 + k >= valid) ? 0.f : prod[k];
+                        for (int k = 0; k < 8; ++k) gvf[k] = (8 * g16 + k >= valid) ? 0.f : gvf[k];
+#pragma unroll
+                    for (int u = 0; u < NQW; ++u) {
+                        float prod[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) prod[k] = p[u][k] * gvf[k];
+                        o_acc[u][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack_bf16x8(prod), f.fv[r], o_acc[u][mb], 0, 0, 0);
                     }
-                    o_acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack_bf16x8(prod), f.fv[r], o_acc[mb], 0, 0, 0);
                 }
             }
         };
@@ -316,57 +375,56 @@ __global__ void __launch_bounds__(S::PF_ * 64, S::MIN_WAVES) decode_mfma_kernel(
         process(s0 + kTileSlots, gbuf_b, fb);
     }
 
-    // ---- finish: full sums per head, then write -----------------------------
+    // ---- finish: full sums per row, then write --------------------------------
 #pragma unroll
-    for (int x = PG; x < 64; x <<= 1) l_run += __shfl_xor(l_run, x);
+    for (int x = S::ROWS; x < 64; x <<= 1) l_run += __shfl_xor(l_run, x);
     if (sm_g == 0) {
-        ws.m_fin[sm_iG] = m_run;
-        ws.l_fin[sm_iG] = l_run;
+        ws.m_fin[sm_row] = m_run;
+        ws.l_fin[sm_row] = l_run;
     }
     wave_lds_sync();
-    const int64_t row = b;  // single query
     const int H = S::H, DH = S::DH;
 #pragma unroll
-    for (int mb = 0; mb < MB16; ++mb) {
+    for (int u = 0; u < NQW; ++u) {
+        if (n0 + u >= P.n_q) continue;
+        const int64_t row = (int64_t)b * P.n_q + n0 + u;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int R = mb * 16 + 4 * g16 + c;
-            const int iG = R / QG, jG = R % QG;
-            const int i = S::head(iG, iF), j = S::feat(jG, l16);
-            const float v = o_acc[mb][c] * P.v_scale;
-            if (P.n_split == 1) {
-                const float l = ws.l_fin[iG];
-                P.out[(row * H + i) * DH + j] = l > 0.f ? v / l : 0.f;
-            } else {
-                P.part_o[((row * P.n_split + split) * H + i) * DH + j] = v;
+        for (int mb = 0; mb < MB16; ++mb) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int R = mb * 16 + 4 * g16 + c;
+                const int iG = R / QG, jG = R % QG;
+                const int i = S::head(iG, iF), j = S::feat(jG, l16);
+                const float v = o_acc[u][mb][c] * P.v_scale;
+                if (P.n_split == 1) {
+                    const float l = ws.l_fin[u * PG + iG];
+                    P.out[(row * H + i) * DH + j] = l > 0.f ? v / l : 0.f;
+                } else {
+                    P.part_o[((row * P.n_split + split) * H + i) * DH + j] = v;
+                }
             }
         }
-    }
-    if (lane < PG) {
-        const int i = S::head(lane, iF);
-        const float m = ws.m_fin[lane], l = ws.l_fin[lane];
-        if (P.n_split == 1) {
-            if (P.lse) P.lse[row * H + i] = l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
-        } else {
-            float* ml = P.part_ml + ((row * P.n_split + split) * H + i) * 2;
-            ml[0] = m;
-            ml[1] = l;
+        if (lane < PG) {
+            const int i = S::head(lane, iF);
+            const float m = ws.m_fin[u * PG + lane], l = ws.l_fin[u * PG + lane];
+            if (P.n_split == 1) {
+                if (P.lse) P.lse[row * H + i] = l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
+            } else {
+                float* ml = P.part_ml + ((row * P.n_split + split) * H + i) * 2;
+                ml[0] = m;
+                ml[1] = l;
+            }
         }
     }
 }
 
-template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int MW = 2>
-struct Cfg : Shape<PG, QG, PF, QF, RK, RV, F_IS_B> {
-    static constexpr int RK_ = RK, RV_ = RV;
-    static constexpr bool F_IS_B_ = F_IS_B;
-    static constexpr int MIN_WAVES = MW;  // waves per SIMD the register budget must allow
-};
-
 template <class C>
 struct Entry {
     static hipError_t launch(const DecodeParams& P, hipStream_t s) {
-        dim3 grid(P.n_split, P.batch);
-        hipLaunchKernelGGL(decode_mfma_kernel<C>, grid, dim3(C::PF_ * 64), 0, s, P);
+        const int qwg = (P.n_q + C::QPW - 1) / C::QPW;
+        const int split_pad = (P.n_split + kXcds - 1) / kXcds * kXcds;
+        dim3 grid(split_pad * qwg, P.batch);
+        hipLaunchKernelGGL(decode_mfma_kernel<C>, grid, dim3(C::WAVES * 64), 0, s, P);
         return hipGetLastError();
     }
     // Workgroups of this kernel one CU holds at once (registers and LDS).
@@ -375,34 +433,45 @@ struct Entry {
         int v = cached.load(std::memory_order_relaxed);
         if (v > 0) return v;
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<C>, C::PF_ * 64, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<C>, C::WAVES * 64, 0) != hipSuccess ||
             n <= 0)
             n = 1;
         cached.store(n, std::memory_order_relaxed);
         return n;
     }
+    static constexpr int queries_per_group = C::QPW;
 };
 
 struct MfmaKernel {
     int p1, p2, q1, q2, r_k, r_v;
+    bool multi;  // kernel for n_q > 1
     hipError_t (*launch)(const DecodeParams&, hipStream_t);
     int (*blocks_per_cu)();
+    int queries_per_group;
 };
 
-// Shapes with a matrix-core instantiation.  F is the factor whose feature
-// dimension is 16 (B for the first three, A for the last).
+#define KPA_MFMA_ENTRY(p1, p2, q1, q2, rk, rv, multi, ...)                                               \
+    {p1, p2, q1, q2, rk, rv, multi, Entry<Cfg<__VA_ARGS__>>::launch, Entry<Cfg<__VA_ARGS__>>::blocks_per_cu, \
+     Entry<Cfg<__VA_ARGS__>>::queries_per_group}
+
+// Shapes with a matrix-core instantiation.  Cfg arguments: PG, QG, PF, QF
+// (F = the factor with feature dimension 16: B for the first three, A for the
+// last two), R_K, R_V, F is B, queries per wave, query subgroups, waves/SIMD.
 const MfmaKernel kKernels[] = {
-    {4, 4, 8, 16, 2, 2, Entry<Cfg<4, 8, 4, 16, 2, 2, true, 3>>::launch, Entry<Cfg<4, 8, 4, 16, 2, 2, true, 3>>::blocks_per_cu},
-    {4, 4, 8, 16, 1, 1, Entry<Cfg<4, 8, 4, 16, 1, 1, true>>::launch, Entry<Cfg<4, 8, 4, 16, 1, 1, true>>::blocks_per_cu},
-    {8, 4, 8, 16, 2, 4, Entry<Cfg<8, 8, 4, 16, 2, 4, true>>::launch, Entry<Cfg<8, 8, 4, 16, 2, 4, true>>::blocks_per_cu},
-    {4, 8, 16, 8, 4, 4, Entry<Cfg<8, 8, 4, 16, 4, 4, false, 1>>::launch,
-     Entry<Cfg<8, 8, 4, 16, 4, 4, false, 1>>::blocks_per_cu},
+    KPA_MFMA_ENTRY(4, 4, 8, 16, 2, 2, false, 4, 8, 4, 16, 2, 2, true, 1, 1, 3),
+    KPA_MFMA_ENTRY(4, 4, 8, 16, 1, 1, false, 4, 8, 4, 16, 1, 1, true, 1, 1, 2),
+    KPA_MFMA_ENTRY(8, 4, 8, 16, 2, 4, false, 8, 8, 4, 16, 2, 4, true, 1, 1, 2),
+    KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, false, 8, 8, 4, 16, 4, 4, false, 1, 1, 1),
+    KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, true, 8, 8, 4, 16, 4, 4, false, 2, 2, 2),
 };
+#undef KPA_MFMA_ENTRY
 
 const MfmaKernel* find_kernel(const kpa_dims& d, int n_q) {
-    if (d.dtype != KPA_BF16 || n_q != 1) return nullptr;
+    if (d.dtype != KPA_BF16) return nullptr;
+    const bool multi = n_q > 1;
     for (const MfmaKernel& k : kKernels)
-        if (k.p1 == d.p1 && k.p2 == d.p2 && k.q1 == d.q1 && k.q2 == d.q2 && k.r_k == d.r_k && k.r_v == d.r_v)
+        if (k.multi == multi && k.p1 == d.p1 && k.p2 == d.p2 && k.q1 == d.q1 && k.q2 == d.q2 && k.r_k == d.r_k &&
+            k.r_v == d.r_v)
             return &k;
     return nullptr;
 }
@@ -411,9 +480,15 @@ const MfmaKernel* find_kernel(const kpa_dims& d, int n_q) {
 
 bool decode_mfma_supported(const kpa_dims& d, int n_q) { return find_kernel(d, n_q) != nullptr; }
 
-int decode_mfma_blocks_per_cu(const kpa_dims& d) {
-    const MfmaKernel* k = find_kernel(d, 1);
+int decode_mfma_blocks_per_cu(const kpa_dims& d, int n_q) {
+    const MfmaKernel* k = find_kernel(d, n_q);
     return k ? k->blocks_per_cu() : 1;
+}
+
+// Workgroups one KV chunk needs (one per group of queries).
+int decode_mfma_query_groups(const kpa_dims& d, int n_q) {
+    const MfmaKernel* k = find_kernel(d, n_q);
+    return k ? (n_q + k->queries_per_group - 1) / k->queries_per_group : 1;
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s) {

@@ -150,6 +150,7 @@ hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s);
 hipError_t launch_merge(const DecodeParams& P, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s);
 bool decode_mfma_supported(const kpa_dims& d, int n_q);
-int decode_mfma_blocks_per_cu(const kpa_dims& d);
+int decode_mfma_blocks_per_cu(const kpa_dims& d, int n_q);
+int decode_mfma_query_groups(const kpa_dims& d, int n_q);
 
 }  // namespace kpa

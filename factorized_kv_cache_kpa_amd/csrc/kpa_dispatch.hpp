@@ -48,9 +48,12 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
         // one full round of workgroups: as many as the CUs hold at once (the
         // matrix-core kernel's occupancy from its registers and LDS; the VALU
         // kernel, a fallback, four per CU)
-        const int64_t per_cu = p.path == Path::kMfmaSq ? decode_mfma_blocks_per_cu(d) : 4;
+        const bool mfma = p.path == Path::kMfmaSq;
+        const int64_t per_cu = mfma ? decode_mfma_blocks_per_cu(d, n_q) : 4;
         const int64_t target = per_cu * cus;
-        s = rows > 0 ? (target + rows - 1) / rows : 1;
+        // workgroups per chunk: one per query group (matrix cores), one per query (VALU)
+        const int64_t wg_rows = mfma ? (int64_t)batch * decode_mfma_query_groups(d, n_q) : rows;
+        s = wg_rows > 0 ? (target + wg_rows - 1) / wg_rows : 1;
         const int64_t min_tiles_per_chunk = 2;
         const int64_t cap = (tiles + min_tiles_per_chunk - 1) / min_tiles_per_chunk;
         if (s > cap) s = cap;
