@@ -48,6 +48,8 @@ namespace {
 
 constexpr int kXcds = 8;  // workgroups are dealt to the 8 XCDs round-robin
 
+constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
+
 template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int NQW, int NQG, int MW>
 struct Cfg {
     static constexpr int PG_ = PG, QG_ = QG, PF_ = PF, QF_ = QF, RK_ = RK, RV_ = RV;
@@ -58,17 +60,24 @@ struct Cfg {
     static constexpr int WAVES = PF * NQG;
     static constexpr int MIN_WAVES = MW;             // waves per SIMD the registers must allow
     static constexpr int M = PG * QG;                // rows (iG, jG) per query
-    static constexpr int MB32 = M / 32;
-    static constexpr int MB16 = M / 16;
+    static constexpr int MB32 = (M + 31) / 32;       // score MFMA row blocks (rows past M are zero)
+    static constexpr int MB16 = (M + 15) / 16;       // value MFMA row blocks
+    static constexpr int KC = QF / 16;               // score MFMA K steps = value MFMA column blocks
     static constexpr int H = PG * PF;
     static constexpr int DH = QG * QF;
-    // G factors of one tile in 1 KB blocks: key set R_K*M elements in 16-byte
-    // chunks (M/8 chunks of 512 B per rank), value set R_V*M elements x 32 slots
-    static constexpr int GK_BLOCKS = RK * M * 64 / 1024;
-    static constexpr int G_BLOCKS = (RK + RV) * M * 64 / 1024;
-    // softmax: NQW*PG (query, head) rows per wave spread over 64 lanes
+    // G factors of one tile: key set R_K*M elements in 16-byte chunks of 8
+    // (512 B per chunk for 32 slots), value set R_V*M elements x 32 slots; in
+    // LDS each set is padded to whole 1 KB DMA blocks
+    static constexpr int GK_BYTES = (RK * M + 7) / 8 * 512;
+    static constexpr int GV_BYTES = RV * M * 64;
+    static constexpr int GK_BLOCKS = (GK_BYTES + 1023) / 1024;
+    static constexpr int GV_BLOCKS = (GV_BYTES + 1023) / 1024;
+    static constexpr int G_BLOCKS = GK_BLOCKS + GV_BLOCKS;
+    // softmax: NQW*PG (query, head) rows per wave, padded to a power of two,
+    // spread over 64 lanes
     static constexpr int ROWS = NQW * PG;
-    static constexpr int GROUPS = 64 / ROWS;         // lanes per row
+    static constexpr int ROWS_P = pow2_at_least(ROWS);
+    static constexpr int GROUPS = 64 / ROWS_P;       // lanes per row
     static constexpr int TPG = 32 / GROUPS;          // slots per lane
     static constexpr int QROT = F_IS_B ? QF : QG;    // rotary pairs live in B's feature dim
     // cache sets
@@ -76,11 +85,11 @@ struct Cfg {
     static constexpr int SET_FK = F_IS_B ? 1 : 0;
     static constexpr int SET_GV = F_IS_B ? 2 : 3;
     static constexpr int SET_FV = F_IS_B ? 3 : 2;
-    static_assert(QF == 16, "the MFMA-side feature dimension must be 16");
-    static_assert(M % 32 == 0, "rows (iG, jG) must fill 32-row MFMA blocks");
-    static_assert(QG == 4 || QG == 8 || QG == 16, "G-side feature dimension 4, 8 or 16");
-    static_assert(64 % ROWS == 0 && ROWS >= 2, "query-head rows of a wave must divide 64");
-    static_assert(QROT <= 16, "rotary table holds 8 pairs");
+    static_assert(QF == 16 || QF == 32 || QF == 64, "the MFMA-side feature dimension must be 16, 32 or 64");
+    static_assert(QG == 1 || QG == 4 || QG == 8 || QG == 16, "G-side feature dimension 1, 4, 8 or 16");
+    static_assert(M % 4 == 0, "rows (iG, jG) come in groups of four");
+    static_assert(ROWS_P <= 64 && ROWS_P >= 2, "query-head rows of a wave must fit 64 lanes");
+    static_assert(QROT <= 64, "rotary table holds 32 pairs");
     static_assert(RK <= 4 && RV <= 4, "ranks up to 4");
     static_assert(WAVES * 64 <= 1024, "at most 16 waves per workgroup");
     __device__ static int head(int iG, int iF) { return F_IS_B ? iG * PF + iF : iF * PG + iG; }
@@ -90,25 +99,27 @@ struct Cfg {
 // Per-wave LDS scratch: scores, overwritten in place by the softmax weights.
 template <class S>
 struct alignas(16) WaveScratch {
-    float zp[S::ROWS][32];
-    float alpha[S::ROWS];
-    float m_fin[S::ROWS];
-    float l_fin[S::ROWS];
+    float zp[S::ROWS_P][32];
+    float alpha[S::ROWS_P];
+    float m_fin[S::ROWS_P];
+    float l_fin[S::ROWS_P];
 };
 
 template <class S>
 __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kernel(DecodeParams P) {
     constexpr int PG = S::PG_, QG = S::QG_, PF = S::PF_, QF = S::QF_, RK = S::RK_, RV = S::RV_;
-    constexpr int M = S::M, MB32 = S::MB32, MB16 = S::MB16, NQW = S::NQW_;
+    constexpr int M = S::M, MB32 = S::MB32, MB16 = S::MB16, NQW = S::NQW_, KC = S::KC;
+    // whole row blocks: the bounds checks on rows vanish at compile time
+    constexpr bool kFull32 = M % 32 == 0, kFull16 = M % 16 == 0;
     __shared__ WaveScratch<S> scratch[S::WAVES];
-    __shared__ float cs_tab[S::QPW][8][2];
+    __shared__ float cs_tab[S::QPW][32][2];
     // two separate LDS objects (not one 2-D array) so the compiler can tell the
     // buffer being filled by DMA from the one being read
     __shared__ __attribute__((aligned(1024))) uint8_t gbuf_a[S::G_BLOCKS * 1024];
     __shared__ __attribute__((aligned(1024))) uint8_t gbuf_b[S::G_BLOCKS * 1024];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = S::WAVES == 1 ? 0 : (int)(threadIdx.x >> 6);
     const int iF = wave % PF;
     const int qsub = wave / PF;
     const int half = lane >> 5;
@@ -139,7 +150,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     for (int n = 0; n < S::QPW; ++n)  // every thread takes part: the clear strides over heads
         if (qwg * S::QPW + n < P.n_q) clear_merge_counters(P, (int64_t)b * P.n_q + qwg * S::QPW + n, split);
     __syncthreads();
-    bf16x8 q_hi[NQW][MB32], q_lo[NQW][MB32];
+    bf16x8 q_hi[NQW][MB32][KC], q_lo[NQW][MB32][KC];
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
         const int n = min(n0 + u, P.n_q - 1);  // queries past n_q compute and are discarded
@@ -148,41 +159,50 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 #pragma unroll
         for (int mb = 0; mb < MB32; ++mb) {
             const int R = mb * 32 + s;
-            const int iG = R / QG, jG = R % QG;
+            const bool row_ok = kFull32 || R < M;  // padding rows of the last block are zero
+            const int iG = row_ok ? R / QG : 0, jG = row_ok ? R % QG : 0;
             const float* qi = qg + (int64_t)S::head(iG, iF) * S::DH;
-            float v[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int jF = 8 * half + k;
-                float x, y;  // this element and its rotary partner
-                int m, first;
-                if constexpr (S::F_IS_B_) {
-                    x = qi[S::feat(jG, jF)];
-                    y = qi[S::feat(jG, jF ^ 1)];
-                    m = jF >> 1;
-                    first = !(jF & 1);
-                } else {
-                    x = qi[S::feat(jG, jF)];
-                    y = qi[S::feat(jG ^ 1, jF)];
-                    m = jG >> 1;
-                    first = !(jG & 1);
+            for (int kc = 0; kc < KC; ++kc) {
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int jF = 16 * kc + 8 * half + k;
+                    float x, y;  // this element and its rotary partner
+                    int m, first;
+                    if constexpr (S::F_IS_B_) {
+                        x = qi[S::feat(jG, jF)];
+                        y = qi[S::feat(jG, jF ^ 1)];
+                        m = jF >> 1;
+                        first = !(jF & 1);
+                    } else {
+                        x = qi[S::feat(jG, jF)];
+                        y = qi[S::feat(jG ^ 1, jF)];
+                        m = jG >> 1;
+                        first = !(jG & 1);
+                    }
+                    const float c = cs_tab[nq][m][0], sn = cs_tab[nq][m][1];
+                    // (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
+                    const float rot = first ? (x * c - y * sn) : (y * sn + x * c);
+                    v[k] = row_ok ? rot * P.q_scale : 0.f;
                 }
-                const float c = cs_tab[nq][m][0], sn = cs_tab[nq][m][1];
-                // (x0, x1) -> (x0 c - x1 s, x0 s + x1 c)
-                v[k] = (first ? (x * c - y * sn) : (y * sn + x * c)) * P.q_scale;
+                split_bf16x8(v, q_hi[u][mb][kc], q_lo[u][mb][kc]);
             }
-            split_bf16x8(v, q_hi[u][mb], q_lo[u][mb]);
         }
     }
 
-    f32x4 o_acc[NQW][MB16];
+    f32x4 o_acc[NQW][MB16][KC];
 #pragma unroll
     for (int u = 0; u < NQW; ++u)
 #pragma unroll
-        for (int k = 0; k < MB16; ++k) o_acc[u][k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < MB16; ++k)
+#pragma unroll
+            for (int nb = 0; nb < KC; ++nb) o_acc[u][k][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // padding rows of the softmax scratch never receive scores: keep them at -inf
+    for (int e = lane; e < (S::ROWS_P - S::ROWS) * 32; e += 64) ws.zp[S::ROWS + e / 32][e % 32] = -INFINITY;
     // softmax state for row sm_row = (query u, head iG) of this wave; l is this
     // lane's partial sum over its slots
-    const int sm_row = lane % S::ROWS, sm_g = lane / S::ROWS;
+    const int sm_row = lane % S::ROWS_P, sm_g = lane / S::ROWS_P;
     float m_run = -INFINITY, l_run = 0.f;
 
     // visible slots: per query (causal), and the workgroup's furthest
@@ -209,76 +229,122 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     // and one barrier (all G blocks landed; the other buffer is free).
     constexpr int KB = S::GK_BLOCKS, NBLK = S::G_BLOCKS;
     struct FRegs {
-        bf16x8 fk[RK];
-        bf16x8 fv[RV];
+        bf16x8 fk[RK][KC];
+        bf16x8 fv[RV][KC];
     };
     auto issue = [&](const uint8_t* tile, uint8_t* gdst, FRegs& f) {
 #pragma unroll
         for (int k = wave; k < NBLK; k += S::WAVES) {
-            const uint8_t* src = k < KB ? tile + offGK + k * 1024 : tile + offGV + (k - KB) * 1024;
-            dma_to_lds16(src + lane * 16, lds_addr(gdst + k * 1024));
+            // 1 KB blocks of the key set, then of the value set; a set's last
+            // block may be partial: only lanes inside the set copy
+            const bool key = k < KB;
+            const int kb = key ? k : k - KB;
+            const int left = (key ? S::GK_BYTES : S::GV_BYTES) - kb * 1024;
+            const uint8_t* src = (key ? tile + offGK : tile + offGV) + kb * 1024;
+            constexpr bool kWholeBlocks = S::GK_BYTES % 1024 == 0 && S::GV_BYTES % 1024 == 0;
+            if (kWholeBlocks || lane * 16 < left) dma_to_lds16(src + lane * 16, lds_addr(gdst + k * 1024));
         }
 #pragma unroll
         for (int r = 0; r < RK; ++r)
-            f.fk[r] = ld16<bf16x8>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + half) * 512 + s * 16);
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc)
+                f.fk[r][kc] = ld16<bf16x8>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + 2 * kc + half) * 512 + s * 16);
 #pragma unroll
         for (int r = 0; r < RV; ++r)
-            f.fv[r] = ld16<bf16x8>(tile + offFV + ((int64_t)((r * PF + iF) * QF + l16) * 32 + 8 * g16) * 2);
+#pragma unroll
+            for (int nb = 0; nb < KC; ++nb)
+                f.fv[r][nb] = ld16<bf16x8>(tile + offFV + ((int64_t)((r * PF + iF) * QF + 16 * nb + l16) * 32 + 8 * g16) * 2);
     };
 
     auto process = [&](int s0, const uint8_t* gcur, FRegs& f) {
         const int valid = min(kTileSlots, last - s0);
         // ---- scores: W = q' F (MFMA), z = sum G W (VALU) --------------------
+        // This lane holds rows R = mb*32 + 8a + 4half + b (b = 0..3) of W for slot s.
 #pragma unroll
         for (int mb = 0; mb < MB32; ++mb) {
-            float zp[NQW][4];
+            // [query][a][b]: sums over the rank, per row b (G feature dimension 1:
+            // every row is a head) or already summed over the in-lane jG
+            constexpr int ZB = QG == 1 ? 4 : 1;
+            float zp[NQW][4][ZB];
 #pragma unroll
             for (int u = 0; u < NQW; ++u)
 #pragma unroll
-                for (int a = 0; a < 4; ++a) zp[u][a] = 0.f;
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int bb = 0; bb < ZB; ++bb) zp[u][a][bb] = 0.f;
 #pragma unroll
             for (int r = 0; r < RK; ++r) {
-                // this lane's G values for rows 8a + 4half + b, shared by every query
+                // this lane's G values for its rows, shared by every query
                 float g[4][4];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const uint2 gk = *reinterpret_cast<const uint2*>(gcur + (r * (M / 8) + mb * 4 + a) * 512 + s * 16 + half * 8);
-                    unpack_bf16x4(gk, g[a][0], g[a][1], g[a][2], g[a][3]);
+                    const int R0 = mb * 32 + 8 * a + 4 * half;
+                    if (kFull32 || R0 < M) {
+                        const int e0 = r * M + R0;  // four consecutive elements in one 16-byte chunk
+                        const uint2 gk = *reinterpret_cast<const uint2*>(gcur + (e0 >> 3) * 512 + s * 16 + (e0 & 7) * 2);
+                        unpack_bf16x4(gk, g[a][0], g[a][1], g[a][2], g[a][3]);
+                    } else {
+                        g[a][0] = g[a][1] = g[a][2] = g[a][3] = 0.f;
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < NQW; ++u) {
                     f32x16 w = f32x16{};
-                    w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_hi[u][mb], f.fk[r], w, 0, 0, 0);
-                    w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_lo[u][mb], f.fk[r], w, 0, 0, 0);
 #pragma unroll
-                    for (int a = 0; a < 4; ++a)
-                        zp[u][a] += w[a * 4 + 0] * g[a][0] + w[a * 4 + 1] * g[a][1] + w[a * 4 + 2] * g[a][2] +
-                                    w[a * 4 + 3] * g[a][3];
+                    for (int kc = 0; kc < KC; ++kc) {
+                        w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_hi[u][mb][kc], f.fk[r][kc], w, 0, 0, 0);
+                        w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_lo[u][mb][kc], f.fk[r][kc], w, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        if constexpr (ZB == 4) {
+#pragma unroll
+                            for (int bb = 0; bb < 4; ++bb) zp[u][a][bb] += w[a * 4 + bb] * g[a][bb];
+                        } else {
+                            zp[u][a][0] += w[a * 4 + 0] * g[a][0] + w[a * 4 + 1] * g[a][1] + w[a * 4 + 2] * g[a][2] +
+                                           w[a * 4 + 3] * g[a][3];
+                        }
+                    }
                 }
             }
 #pragma unroll
             for (int u = 0; u < NQW; ++u) {
                 const bool ok = s0 + s < vis[u] && s < valid;  // causal mask per query
                 float* zrow = &ws.zp[u * PG][0];
-                if constexpr (QG == 4) {
-                    // rows 8a + 4half + b: iG = mb*8 + 2a + half, jG = b -- complete in lane
+                if constexpr (ZB == 4) {
+                    // every row is a head
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) zrow[(mb * 8 + 2 * a + half) * 32 + s] = ok ? zp[u][a] : -INFINITY;
-                } else if constexpr (QG == 8) {
-                    // iG = mb*4 + a, jG = 4half + b: add the other half
+                    for (int a = 0; a < 4; ++a)
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) zp[u][a] = sum_halves(zp[u][a]);
-                    // selects, not a lane-dependent array index (which would go to scratch)
-                    const float za = half ? zp[u][2] : zp[u][0];
-                    const float zb = half ? zp[u][3] : zp[u][1];
-                    zrow[(mb * 4 + 2 * half + 0) * 32 + s] = ok ? za : -INFINITY;
-                    zrow[(mb * 4 + 2 * half + 1) * 32 + s] = ok ? zb : -INFINITY;
+                        for (int bb = 0; bb < ZB; ++bb) {
+                            const int R = mb * 32 + 8 * a + 4 * half + bb;
+                            if (kFull32 || R < M) zrow[R * 32 + s] = ok ? zp[u][a][bb] : -INFINITY;
+                        }
                 } else {
-                    // QG == 16: iG = mb*2 + a/2, jG = 8(a%2) + 4half + b
-                    float z0 = zp[u][0] + zp[u][1], z1 = zp[u][2] + zp[u][3];
-                    z0 = sum_halves(z0);
-                    z1 = sum_halves(z1);
-                    zrow[(mb * 2 + half) * 32 + s] = ok ? (half ? z1 : z0) : -INFINITY;
+                    float z4[4];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) z4[a] = zp[u][a][0];
+                    if constexpr (QG == 4) {
+                        // rows 8a + 4half + b: iG = mb*8 + 2a + half, jG = b -- complete in lane
+#pragma unroll
+                        for (int a = 0; a < 4; ++a)
+                            if (kFull32 || mb * 32 + 8 * a + 4 * half < M) zrow[(mb * 8 + 2 * a + half) * 32 + s] = ok ? z4[a] : -INFINITY;
+                    } else if constexpr (QG == 8) {
+                        // iG = mb*4 + a, jG = 4half + b: add the other half
+#pragma unroll
+                        for (int a = 0; a < 4; ++a) z4[a] = sum_halves(z4[a]);
+                        // selects, not a lane-dependent array index (which would go to scratch)
+                        const float za = half ? z4[2] : z4[0];
+                        const float zb = half ? z4[3] : z4[1];
+                        if (kFull32 || mb * 32 + 16 * half < M) zrow[(mb * 4 + 2 * half + 0) * 32 + s] = ok ? za : -INFINITY;
+                        if (kFull32 || mb * 32 + 16 * half + 8 < M) zrow[(mb * 4 + 2 * half + 1) * 32 + s] = ok ? zb : -INFINITY;
+                    } else {
+                        // QG == 16: iG = mb*2 + a/2, jG = 8(a%2) + 4half + b
+                        float z0 = z4[0] + z4[1], z1 = z4[2] + z4[3];
+                        z0 = sum_halves(z0);
+                        z1 = sum_halves(z1);
+                        if (kFull32 || mb * 32 + 16 * half < M) zrow[(mb * 2 + half) * 32 + s] = ok ? (half ? z1 : z0) : -INFINITY;
+                    }
                 }
             }
         }
@@ -294,7 +360,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                 mt = fmaxf(mt, zl[t]);
             }
 #pragma unroll
-            for (int x = S::ROWS; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x));
+            for (int x = S::ROWS_P; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x));
             const float m_new = fmaxf(m_run, mt);
             // with no slot seen yet (m = -inf) every weight is 0 and alpha 1
             const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
@@ -322,22 +388,49 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                 for (int k = 0; k < 8; ++k)
                     if (8 * g16 + k >= valid)
 #pragma unroll
-                        for (int r = 0; r < RV; ++r) f.fv[r][k] = (__bf16)0.f;
+                        for (int r = 0; r < RV; ++r)
+#pragma unroll
+                            for (int nb = 0; nb < KC; ++nb) f.fv[r][nb][k] = (__bf16)0.f;
             }
 #pragma unroll
             for (int mb = 0; mb < MB16; ++mb) {
-                const int iG_out = (mb * 16 + 4 * g16) / QG;  // rows of this lane's accumulator
-                const int iG_row = (mb * 16 + l16) / QG;      // row of this lane's A operand
+                const int R_row = mb * 16 + l16;               // row of this lane's A operand
+                const bool row_ok = kFull16 || R_row < M;
+                const int iG_row = row_ok ? R_row / QG : 0;
                 float p[NQW][8];
 #pragma unroll
                 for (int u = 0; u < NQW; ++u) {
-                    o_acc[u][mb] *= ws.alpha[u * PG + iG_out];
+                    // rows of this lane's accumulators: mb*16 + 4*g16 + c
+                    if constexpr (QG % 4 == 0) {
+                        // the four rows share one head
+                        const float a = ws.alpha[u * PG + (mb * 16 + 4 * g16) / QG];
+#pragma unroll
+                        for (int nb = 0; nb < KC; ++nb)
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) o_acc[u][mb][nb][c] *= a;
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int R_out = mb * 16 + 4 * g16 + c;
+                            const float a = ws.alpha[u * PG + (kFull16 || R_out < M ? R_out / QG : 0)];
+#pragma unroll
+                            for (int nb = 0; nb < KC; ++nb) o_acc[u][mb][nb][c] *= a;
+                        }
+                    }
                     ld_lds32(&ws.zp[u * PG + iG_row][8 * g16], p[u]);
+                    if (!row_ok)
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) p[u][k] = 0.f;
                 }
 #pragma unroll
                 for (int r = 0; r < RV; ++r) {
                     float gvf[8];
-                    unpack_bf16x8(*reinterpret_cast<const bf16x8*>(gvbase + ((r * M + mb * 16 + l16) * 32 + 8 * g16) * 2), gvf);
+                    if (row_ok) {
+                        unpack_bf16x8(*reinterpret_cast<const bf16x8*>(gvbase + ((r * M + R_row) * 32 + 8 * g16) * 2), gvf);
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) gvf[k] = 0.f;
+                    }
                     if constexpr (kPartial)
 #pragma unroll
                         for (int k = 0; k < 8; ++k) gvf[k] = (8 * g16 + k >= valid) ? 0.f : gvf[k];
@@ -346,7 +439,10 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                         float prod[8];
 #pragma unroll
                         for (int k = 0; k < 8; ++k) prod[k] = p[u][k] * gvf[k];
-                        o_acc[u][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack_bf16x8(prod), f.fv[r], o_acc[u][mb], 0, 0, 0);
+                        const bf16x8 ga = pack_bf16x8(prod);
+#pragma unroll
+                        for (int nb = 0; nb < KC; ++nb)
+                            o_acc[u][mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, f.fv[r][nb], o_acc[u][mb][nb], 0, 0, 0);
                     }
                 }
             }
@@ -377,7 +473,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 
     // ---- finish: full sums per row, then write --------------------------------
 #pragma unroll
-    for (int x = S::ROWS; x < 64; x <<= 1) l_run += __shfl_xor(l_run, x);
+    for (int x = S::ROWS_P; x < 64; x <<= 1) l_run += __shfl_xor(l_run, x);
     if (sm_g == 0) {
         ws.m_fin[sm_row] = m_run;
         ws.l_fin[sm_row] = l_run;
@@ -393,14 +489,18 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int R = mb * 16 + 4 * g16 + c;
+                if (R >= M) continue;
                 const int iG = R / QG, jG = R % QG;
-                const int i = S::head(iG, iF), j = S::feat(jG, l16);
-                const float v = o_acc[u][mb][c] * P.v_scale;
-                if (P.n_split == 1) {
-                    const float l = ws.l_fin[u * PG + iG];
-                    P.out[(row * H + i) * DH + j] = l > 0.f ? v / l : 0.f;
-                } else {
-                    P.part_o[((row * P.n_split + split) * H + i) * DH + j] = v;
+                const int i = S::head(iG, iF);
+                const float l = ws.l_fin[u * PG + iG];
+#pragma unroll
+                for (int nb = 0; nb < KC; ++nb) {
+                    const int j = S::feat(jG, 16 * nb + l16);
+                    const float v = o_acc[u][mb][nb][c] * P.v_scale;
+                    if (P.n_split == 1)
+                        P.out[(row * H + i) * DH + j] = l > 0.f ? v / l : 0.f;
+                    else
+                        P.part_o[((row * P.n_split + split) * H + i) * DH + j] = v;
                 }
             }
         }
@@ -455,14 +555,17 @@ struct MfmaKernel {
      Entry<Cfg<__VA_ARGS__>>::queries_per_group}
 
 // Shapes with a matrix-core instantiation.  Cfg arguments: PG, QG, PF, QF
-// (F = the factor with feature dimension 16: B for the first three, A for the
-// last two), R_K, R_V, F is B, queries per wave, query subgroups, waves/SIMD.
+// (F = the factor with feature dimension 16, 32 or 64: B for the first three
+// and the last, A for the two multi-query shapes), R_K, R_V, F is B, queries
+// per wave, query subgroups, waves/SIMD.
 const MfmaKernel kKernels[] = {
     KPA_MFMA_ENTRY(4, 4, 8, 16, 2, 2, false, 4, 8, 4, 16, 2, 2, true, 1, 1, 3),
     KPA_MFMA_ENTRY(4, 4, 8, 16, 1, 1, false, 4, 8, 4, 16, 1, 1, true, 1, 1, 2),
     KPA_MFMA_ENTRY(8, 4, 8, 16, 2, 4, false, 8, 8, 4, 16, 2, 4, true, 1, 1, 2),
     KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, false, 8, 8, 4, 16, 4, 4, false, 1, 1, 1),
     KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, true, 8, 8, 4, 16, 4, 4, false, 2, 2, 2),
+    // TPA split (A: h x 1, B: 1 x d_h): G = A with feature dimension 1, F = B
+    KPA_MFMA_ENTRY(12, 1, 1, 64, 2, 2, false, 12, 1, 1, 64, 2, 2, true, 1, 1, 1),
 };
 #undef KPA_MFMA_ENTRY
 
