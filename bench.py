@@ -9,10 +9,20 @@ in HBM.  The default workload is 32 sequences x 32768 cached tokens,
 h = 4x4, d_h = 8x16, R_K = R_V = 2, bfloat16 factors.
 
 Prints ONE JSON line with the cached-tokens-attended rate, the roofline of
-the decode kernel (algorithmic bytes / kernel time, timed with HIP events on
-the launch stream), and the CPU oracle timed on a bounded sample.
+the split-KV decode kernel (algorithmic bytes or flops / that kernel's
+average duration, bracketed with HIP events on its own stream by the
+library's measurement hook), and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Profile summaries (text, under profiles/) are written from rocprofv3 output
+by the same file:
+
+    python bench.py --summarize-trace STATS_DIR --bench-json FILE --cmd "..."
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --copy-mib 256 --cmd "..." --cmd "..."
+
+The traffic summary carries a hash of the kernel sources; the JSON line's
+roofline.traffic is filled from it only while the sources still hash the same.
 """
 from __future__ import annotations
 
@@ -22,7 +32,11 @@ import os
 import sys
 import time
 
-HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+HBM_PEAK_GBPS = 8000.0        # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix throughput
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "factorized_kv_cache_kpa_amd", "csrc")
 METRIC = "cached tokens attended/sec (decode) + achieved HBM GB/s as % of MI355X peak"
 
 
@@ -40,11 +54,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, copy MIB MiB device-to-device 3 times (HBM counter calibration)")
+    ap.add_argument("--summarize-trace", default=None, metavar="STATS_DIR")
+    ap.add_argument("--bench-json", default=None)
+    ap.add_argument("--summarize-pmc", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--cmd", action="append", default=[], help="command recorded in a summary")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_pmc:
+        return summarize_pmc(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the decode shards by sequence with no communication; see DESIGN.md)", file=sys.stderr)
@@ -130,28 +155,45 @@ def main():
         sys.exit(1)
     log(f"warmup done ({args.warmup} steps)")
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    def timing_events(n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in ev:  # create the HIP events before the timed region
+            e0.record()
+            e1.record()
+        return ev
+
+    call_ev = timing_events(args.steps)   # the whole decode call (decode kernel + merge)
+    kern_ev = timing_events(args.steps)   # the split-KV decode kernel alone
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
-        step(events[k])
+        kpa.kpa_time_next_decode_kernel(*kern_ev[k])
+        step(call_ev[k])
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
-    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode {decode_ms * 1e3:.1f} us")
+    call_ms = np.array([a.elapsed_time(b) for a, b in call_ev])
+    kern_ms = np.array([a.elapsed_time(b) for a, b in kern_ev])
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode call {call_ms.mean() * 1e3:.1f} us, "
+        f"decode kernel {kern_ms.mean() * 1e3:.1f} us (median {np.median(kern_ms) * 1e3:.1f})")
+
+    if args.copy_calibration > 0:
+        # a plain device-to-device copy of known size, after the timed region,
+        # for scaling the HBM byte counters of a profiling pass
+        n = args.copy_calibration << 18
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration: 3 copies of {args.copy_calibration} MiB")
+        del src, dst
 
     tokens = int(inp.ctx_len.sum().item())  # cached tokens attended per step (per query)
     value = tokens / (ms_per_step / 1e3)
-    # algorithmic bytes of one decode launch: every attended token's factors
-    # once, plus the queries and outputs (no padding, no partial results)
-    alg_bytes = tokens * cfg.bytes_per_token + q.numel() * 4 + out.numel() * 4 + lse.numel() * 4
-    achieved = alg_bytes / (decode_ms / 1e3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "kpa_decode (split-KV decode + log-sum-exp merge)",
-                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
-                "alg_bytes_per_launch": alg_bytes, "launch_us": round(decode_ms * 1e3, 2)}
+    roofline = decode_roofline(cfg, tokens, q.numel() * 4 + out.numel() * 4 + lse.numel() * 4,
+                               float(kern_ms.mean()), float(call_ms.mean()), kpa.kpa_decode_path(dims, n_q))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -166,7 +208,7 @@ def main():
                    "split": [cfg.p1, cfg.p2, cfg.q1, cfg.q2], "ranks": [cfg.r_k, cfg.r_v],
                    "path": kpa.kpa_decode_path(dims, n_q), "step": "append new token(s) + decode",
                    "parallelism": "single GPU"},
-        "achieved_hbm_gbps": round(achieved, 1), "hbm_pct_of_peak": round(100 * achieved / HBM_PEAK_GBPS, 2),
+        "achieved_hbm_gbps": roofline["hbm_gbps"], "hbm_pct_of_peak": round(100 * roofline["hbm_gbps"] / HBM_PEAK_GBPS, 2),
         "roofline": roofline, "cpu_baseline": cpu,
     }
     line = json.dumps(res)
@@ -174,6 +216,193 @@ def main():
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(line + "\n")
+
+
+def alg_flops_per_query_token(cfg):
+    """Multiply-adds x 2 per (query, cached token) of the factor-space decode:
+    both contractions of the scores and of the values, (R_K + R_V) h (q1 q2 + q1)."""
+    return 2 * (cfg.r_k + cfg.r_v) * cfg.h * (cfg.q1 * cfg.q2 + cfg.q1)
+
+
+def decode_roofline(cfg, tokens, io_bytes, kern_ms, call_ms, path):
+    """Roofline of the split-KV decode kernel.  Algorithmic bytes per launch:
+    every attended token's factors once plus the queries and outputs (no tile
+    padding, no partial results); algorithmic flops: see
+    alg_flops_per_query_token.  The bound is the one the algorithmic
+    intensity selects against the MI355X ridge point."""
+    alg_bytes = tokens * cfg.bytes_per_token + io_bytes
+    alg_flops = tokens * cfg.n_q * alg_flops_per_query_token(cfg)
+    hbm_gbps = alg_bytes / (kern_ms / 1e3) / 1e9
+    tflops = alg_flops / (kern_ms / 1e3) / 1e12
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    mfma_bound = cfg.dtype == "bf16" and alg_flops / alg_bytes > ridge
+    if mfma_bound:
+        bound, achieved, peak, unit = "mfma", tflops, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", hbm_gbps, HBM_PEAK_GBPS, "GB/s"
+    r = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": None,
+         "kernel": f"split-KV decode kernel ({path})", "launch_us": round(kern_ms * 1e3, 2),
+         "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops,
+         "hbm_gbps": round(hbm_gbps, 1), "tflops": round(tflops, 2),
+         "call_us": round(call_ms * 1e3, 2),
+         "call_frac": round((hbm_gbps if bound == "hbm" else tflops) * kern_ms / call_ms / peak, 4)}
+    t = stored_traffic(cfg.name)
+    if t is not None:
+        r["traffic"] = t
+        r["traffic_over_alg_bytes"] = round(t / alg_bytes, 4)
+    return r
+
+
+def kernel_sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(CSRC)):
+        if fn.endswith((".hip", ".hpp")):
+            h.update(fn.encode())
+            with open(os.path.join(CSRC, fn), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_summary_path(workload):
+    return os.path.join(PROFILES, f"decode_traffic_{workload}.md")
+
+
+def _summary_fields(path):
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip().lstrip("-* ").strip()
+            if ":" in line and line.split(":", 1)[0].replace("_", "").isalnum():
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    return fields
+
+
+def stored_traffic(workload):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    if there is none or the kernel sources changed since it was taken."""
+    path = traffic_summary_path(workload)
+    if not os.path.exists(path):
+        return None
+    f = _summary_fields(path)
+    if f.get("kernel_sources_sha256") != kernel_sources_hash():
+        log("traffic summary predates the current kernel sources: traffic = null")
+        return None
+    try:
+        return int(f["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirname, suffix):
+    for root, _, files in os.walk(dirname):
+        for fn in sorted(files):
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirname}")
+
+
+def _short_kernel(name):
+    name = name.replace("kpa::(anonymous namespace)::", "").replace("(kpa::DecodeParams)", "")
+    name = name.replace("kpa::(anonymous namespace)::", "")
+    return name if len(name) < 110 else name[:107] + "..."
+
+
+def summarize_trace(args):
+    """profiles/decode_kernels_<workload>.md from a rocprofv3 --kernel-trace
+    --stats run of this file and the JSON line that run printed."""
+    with open(args.bench_json) as f:
+        res = json.loads(f.read().strip().splitlines()[-1])
+    wl = res["config"]["workload"]
+    rows = _read_csv(_find(args.summarize_trace, "kernel_stats.csv"))
+    lines = [f"# Kernel trace: {wl} decode step", "",
+             "Command (from the repository root on the MI355X; the output directory is scratch):", ""]
+    lines += [f"    {c}" for c in args.cmd] + [""]
+    lines += ["rocprofv3 kernel statistics (all launches of the run, warm-up included):", "",
+              "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{_short_kernel(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    rf = res["roofline"]
+    dec = [r for r in rows if "decode_" in r["Name"] and "_kernel" in r["Name"]]
+    lines += ["", "Same run, bench.py's own figures (HIP events on the launch stream, timed steps only):", "",
+              f"- decode kernel average: {rf['launch_us']} us",
+              f"- decode call (kernel + merge) average: {rf['call_us']} us",
+              f"- ms per step: {res['ms_per_step']}",
+              f"- roofline: {rf['achieved']} {rf['unit']} of {rf['peak']} ({100 * rf['frac']:.1f}%), bound {rf['bound']}"]
+    if dec:
+        avg = float(dec[0]["AverageNs"]) / 1e3
+        lines.append(f"- rocprofv3 decode kernel average: {avg:.1f} us "
+                     f"({100 * (rf['launch_us'] - avg) / avg:+.1f}% for the events)")
+    out = os.path.join(PROFILES, f"decode_kernels_{wl}.md")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
+
+
+def summarize_pmc(args):
+    """profiles/decode_traffic_<workload>.md from two rocprofv3 --pmc runs of
+    this file with --copy-calibration (FETCH_SIZE, then WRITE_SIZE).  The
+    counters of the calibration copies (the last three dispatches of each run,
+    MIB MiB read and written each) give the scale from counter KiB to bytes."""
+    out = {}
+    for counter, d in zip(("FETCH_SIZE", "WRITE_SIZE"), args.summarize_pmc):
+        rows = [r for r in _read_csv(_find(d, "counter_collection.csv")) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = rows[-3:]
+        if len({r["Kernel_Name"] for r in copies}) != 1:
+            raise SystemExit(f"{counter}: the last three dispatches are not one copy kernel")
+        copy_kib = sum(float(r["Counter_Value"]) for r in copies) / 3
+        dec = [r for r in rows if "decode_" in r["Kernel_Name"] and "_kernel" in r["Kernel_Name"]]
+        if not dec:
+            raise SystemExit(f"{counter}: no decode kernel dispatches")
+        names = {r["Kernel_Name"] for r in dec}
+        dec_kib = sum(float(r["Counter_Value"]) for r in dec) / len(dec)
+        scale = args.copy_mib * 1024 / copy_kib
+        out[counter] = dict(copy_kernel=copies[0]["Kernel_Name"], copy_kib=copy_kib, scale=scale,
+                            dec_kib=dec_kib, n=len(dec), kernel=sorted(names))
+    fetch = out["FETCH_SIZE"]["dec_kib"] * 1024 * out["FETCH_SIZE"]["scale"]
+    write = out["WRITE_SIZE"]["dec_kib"] * 1024 * out["WRITE_SIZE"]["scale"]
+    wl = None
+    for c in args.cmd:
+        if "--workload" in c:
+            wl = c.split("--workload", 1)[1].split()[0]
+    wl = wl or "kpa_32k"
+    from workloads import CONFIGS
+    cfg = CONFIGS[wl]
+    n_q = cfg.n_q
+    alg = cfg.batch * cfg.ctx * cfg.bytes_per_token + cfg.batch * n_q * cfg.h * (2 * cfg.d_h + 1) * 4
+    lines = [f"# HBM traffic of the split-KV decode kernel: {wl}", "",
+             "Two counter passes of the same bench command (one counter each), from the repository root:", ""]
+    lines += [f"    {c}" for c in args.cmd] + [""]
+    lines += [f"Decode kernel: `{_short_kernel(k)}`" for k in out["FETCH_SIZE"]["kernel"]] + [""]
+    lines += ["| counter | copy kernel KiB/dispatch | copy bytes | scale | decode KiB/dispatch (raw) | dispatches | decode bytes (scaled) |",
+              "|---|---|---|---|---|---|---|"]
+    for counter, v in out.items():
+        lines.append(f"| {counter} | {v['copy_kib']:.1f} | {args.copy_mib} MiB | {v['scale']:.4f} | "
+                     f"{v['dec_kib']:.1f} | {v['n']} | {v['dec_kib'] * 1024 * v['scale']:.0f} |")
+    lines += ["", f"Calibration kernel: `{_short_kernel(out['FETCH_SIZE']['copy_kernel'])}`, "
+                  f"{args.copy_mib} MiB read and {args.copy_mib} MiB written per dispatch.", "",
+              f"- fetch_bytes_per_launch: {fetch:.0f}",
+              f"- write_bytes_per_launch: {write:.0f}",
+              f"- traffic_bytes_per_launch: {fetch + write:.0f}",
+              f"- alg_bytes_per_launch: {alg}",
+              f"- traffic_over_alg: {(fetch + write) / alg:.4f}",
+              f"- kernel_sources_sha256: {kernel_sources_hash()}", ""]
+    path = traffic_summary_path(wl)
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
 
 
 def cpu_baseline(inp, cfg, target_s, tokens_total):

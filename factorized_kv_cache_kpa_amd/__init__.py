@@ -88,6 +88,8 @@ def load():
     lib.kpa_status_string.restype = ctypes.c_char_p
     lib.kpa_decode_path.argtypes = [DP, I32]
     lib.kpa_decode_path.restype = ctypes.c_char_p
+    lib.kpa_time_next_decode_kernel.argtypes = [P, P]
+    lib.kpa_time_next_decode_kernel.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -190,6 +192,20 @@ def kpa_decode_multiq(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causa
 # --------------------------------------------------------------------------
 # Allocation conveniences (torch does the allocating; no computation here)
 # --------------------------------------------------------------------------
+def kpa_time_next_decode_kernel(start_event, stop_event):
+    """Have the next decode call on this thread record the two events (torch
+    timing events, or None to cancel) around its split-KV decode kernel."""
+    def handle(ev):
+        if ev is None:
+            return None
+        if not isinstance(ev, torch.cuda.Event):
+            raise TypeError("events must be torch.cuda.Event")
+        if not ev.cuda_event:  # torch creates the HIP event on its first record
+            ev.record()
+        return ev.cuda_event
+    _check("kpa_time_next_decode_kernel", load().kpa_time_next_decode_kernel(handle(start_event), handle(stop_event)))
+
+
 def alloc_cache(dims, batch, capacity, device="cuda"):
     n = kpa_cache_bytes(dims, batch, capacity)
     if n == 0 and batch > 0:

@@ -120,11 +120,21 @@ size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t m
     return plan.workspace_bytes;
 }
 
+// Events the next decode call on this thread records around its split-KV
+// decode kernel (kpa_time_next_decode_kernel).
+struct KernelEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+static thread_local KernelEvents t_kernel_events;
+
 static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch, int32_t capacity,
                          const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
                          const float* q, const int32_t* q_pos, float* out, float* lse,
                          void* workspace, size_t workspace_bytes, int32_t num_splits,
                          uint32_t* dev_status, void* stream) {
+    // a pending measurement request applies to this call only
+    const KernelEvents ev = t_kernel_events;
+    t_kernel_events = KernelEvents{};
     int st = check_decode_args(dims, batch, capacity, max_ctx, n_q);
     if (st != KPA_OK) return st;
     if (batch == 0) return KPA_OK;
@@ -168,9 +178,17 @@ static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch,
     P.q_scale = (float)(1.4426950408889634 / (dims->r_k * sqrt((double)dh)));
     P.v_scale = (float)(1.0 / dims->r_v);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (ev.start && hipEventRecord(ev.start, s) != hipSuccess) return KPA_ERR_HIP;
     hipError_t e = launch_plan(plan, P, s);
     if (e != hipSuccess) return KPA_ERR_HIP;
+    if (ev.stop && hipEventRecord(ev.stop, s) != hipSuccess) return KPA_ERR_HIP;
     if (plan.n_split > 1 && launch_merge(P, s) != hipSuccess) return KPA_ERR_HIP;
+    return KPA_OK;
+}
+
+int kpa_time_next_decode_kernel(void* start_event, void* stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr)) return KPA_ERR_NULL_PTR;
+    t_kernel_events = KernelEvents{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
     return KPA_OK;
 }
 

@@ -205,6 +205,20 @@ int kpa_decode_multiq(const kpa_dims* dims, const void* cache, int32_t batch, in
                       void* workspace, size_t workspace_bytes, int32_t num_splits,
                       uint32_t* dev_status, void* stream);
 
+/*
+ * kpa_time_next_decode_kernel -- measurement hook.  start_event and
+ * stop_event are hipEvent_t handles created by the caller with timing
+ * enabled (both non-NULL), or both NULL to cancel a pending request.  The
+ * next kpa_decode / kpa_decode_multiq call made on the same host thread
+ * records start_event on its stream right before its split-KV decode kernel
+ * and stop_event right after it, before the log-sum-exp merge; the request
+ * is then dropped, also when that call fails its checks.  Lets a caller time
+ * the decode kernel alone on the stream it runs on.  The events stay owned
+ * by the caller and must outlive that call.
+ * Returns KPA_OK, or KPA_ERR_NULL_PTR if exactly one handle is NULL.
+ */
+int kpa_time_next_decode_kernel(void* start_event, void* stop_event);
+
 /* Static description of a kpa_status code. */
 const char* kpa_status_string(int status);
 

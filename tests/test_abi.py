@@ -130,3 +130,17 @@ def test_status_strings():
     for code in range(-7, 1):
         assert kpa.kpa_status_string(code)
     assert kpa.kpa_status_string(-99) == "unknown status"
+
+
+def test_kernel_timing_hook_needs_both_events_or_none():
+    lib = kpa.load()
+    assert lib.kpa_time_next_decode_kernel(FAKE, None) == -2  # KPA_ERR_NULL_PTR
+    assert lib.kpa_time_next_decode_kernel(None, FAKE) == -2
+    # both NULL cancels; a pending pair is dropped by the next decode call even
+    # when that call fails its checks, so no later call touches FAKE handles
+    assert lib.kpa_time_next_decode_kernel(None, None) == 0
+    assert lib.kpa_time_next_decode_kernel(FAKE, FAKE) == 0
+    dims = kpa.make_dims(4, 4, 8, 16, 2, 2)
+    st = lib.kpa_decode(ctypes.byref(dims), FAKE, 1, 64, FAKE, 128, FAKE, FAKE, FAKE, None, None, 0, 0, None, None)
+    assert st != 0
+    assert lib.kpa_time_next_decode_kernel(None, None) == 0

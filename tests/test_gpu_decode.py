@@ -171,3 +171,24 @@ def test_decode_full_size_sampled(gpu_lib, name, k):
     got_o = np.stack([go[b, n, hd] for b, n, hd in items])
     got_l = np.array([gl[b, n, hd] for b, n, hd in items])
     assert_close(got_o, got_l, ro, rl, cfg.dtype, f"{name} full size")
+
+
+def test_kernel_timing_hook_brackets_the_decode_kernel(gpu_lib):
+    """The measurement hook records its events around the split-KV kernel
+    only: that interval is positive and no longer than the whole call's, and
+    the results do not change."""
+    cfg = CONFIGS["kpa_32k"]
+    inp = make_inputs(cfg, seed=11, batch=2, ctx=4096)
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    ref_o, ref_l = run_decode(inp, dims, cache, cap, num_splits=8)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    kpa.kpa_time_next_decode_kernel(ev[1], ev[2])
+    go, gl = run_decode(inp, dims, cache, cap, num_splits=8)
+    ev[3].record()
+    torch.cuda.synchronize()
+    t_kernel = ev[1].elapsed_time(ev[2])
+    t_call = ev[0].elapsed_time(ev[3])
+    assert 0.0 < t_kernel <= t_call
+    assert np.array_equal(go, ref_o) and np.array_equal(gl, ref_l)
