@@ -17,8 +17,21 @@ struct Plan {
     size_t workspace_bytes;
 };
 
-// Splits merged by one merge block; more splits go through a second level.
+// Split-KV merge levels.  Up to kMergeGroup chunks per (row, head) are merged
+// by a 256-thread block; up to kMaxSingleLevel by one 1024-thread block when
+// a single pass of loads covers them (at most 16 vectors per thread);
+// otherwise blocks merge kMergeGroup chunks each and a second level merges
+// their results.
 constexpr int kMergeGroup = 64;
+constexpr int kMaxSingleLevel = 1024;
+
+inline bool merge_single_level(int64_t s, int64_t dh) {
+    if (s <= kMergeGroup) return true;
+    if (s > kMaxSingleLevel) return false;
+    const int64_t vec = dh % 4 == 0 ? 4 : 2;
+    const int64_t per_pass = 1024 / (dh / vec);  // chunks one pass of 1024 threads covers
+    return (s + per_pass - 1) / per_pass <= 16;
+}
 
 inline const char* path_name(Path p) {
     switch (p) {
@@ -70,9 +83,11 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
     p.n_split = (int32_t)s;
     p.chunk_tiles = (int32_t)chunk;
     const int64_t h = (int64_t)d.p1 * d.p2, dh = (int64_t)d.q1 * d.q2;
-    p.n_group = s > 1 ? (int32_t)((s + kMergeGroup - 1) / kMergeGroup) : 1;
-    p.part_floats = s > 1 ? (size_t)(rows * s * h * (dh + 2)) : 0;
-    p.part2_floats = p.n_group > 1 ? (size_t)(rows * p.n_group * h * (dh + 2)) : 0;
+    p.n_group = merge_single_level(s, dh) ? 1 : (int32_t)((s + kMergeGroup - 1) / kMergeGroup);
+    // each region starts 16-byte aligned (the merge reads partials as float4)
+    auto round4 = [](size_t x) { return (x + 3) / 4 * 4; };
+    p.part_floats = s > 1 ? round4((size_t)(rows * s * h * (dh + 2))) : 0;
+    p.part2_floats = p.n_group > 1 ? round4((size_t)(rows * p.n_group * h * (dh + 2))) : 0;
     const size_t counters = p.n_group > 1 ? (size_t)(rows * h) : 0;
     p.workspace_bytes = (p.part_floats + p.part2_floats + counters) * sizeof(float);
     return p;

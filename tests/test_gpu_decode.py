@@ -192,3 +192,20 @@ def test_kernel_timing_hook_brackets_the_decode_kernel(gpu_lib):
     t_call = ev[0].elapsed_time(ev[3])
     assert 0.0 < t_kernel <= t_call
     assert np.array_equal(go, ref_o) and np.array_equal(gl, ref_l)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_odd_shape_and_two_level_merge(gpu_lib, dtype):
+    """A shape no matrix-core kernel covers (d_h = 18, not a multiple of 4;
+    ranks 3 and 1) on the general kernel, with chunk counts that take the
+    single-level merge and the two-level merge (more than 64 chunks)."""
+    cfg = CONFIGS["tiny_f32"].scaled(name="odd", p1=3, p2=5, q1=3, q2=6, r_k=3, r_v=1, dtype=dtype,
+                                     sigma_a=0.3, sigma_b=0.3)
+    inp = make_inputs(cfg, seed=12, batch=2, ctx=2400, ragged=True)
+    inp.ctx_len[0] = 2400  # at least 75 tiles in one sequence
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    ro, rl = _oracle(inp)
+    for s in (1, 9, 75):
+        go, gl = run_decode(inp, dims, cache, cap, num_splits=s)
+        assert_close(go, gl, ro, rl, dtype, f"odd shape, splits={s}")
