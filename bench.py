@@ -54,10 +54,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--call-events", action="store_true",
+                    help="also bracket each whole decode call (kernel + merge) with events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device-to-device 3 times (HBM counter calibration)")
     ap.add_argument("--summarize-trace", default=None, metavar="STATS_DIR")
-    ap.add_argument("--bench-json", default=None)
+    ap.add_argument("--bench-json", default=None, help="JSON line of the profiled run")
+    ap.add_argument("--plain-json", default=None, help="JSON line of the same command run without the profiler")
     ap.add_argument("--summarize-pmc", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--copy-mib", type=int, default=256)
     ap.add_argument("--cmd", action="append", default=[], help="command recorded in a summary")
@@ -162,20 +165,24 @@ def main():
             e1.record()
         return ev
 
-    call_ev = timing_events(args.steps)   # the whole decode call (decode kernel + merge)
+    # Timed region: the steps, with the decode kernel of each bracketed by a
+    # pair of HIP events on its stream (every event marker costs the stream a
+    # few microseconds, so the whole-call pair is recorded only on request).
     kern_ev = timing_events(args.steps)   # the split-KV decode kernel alone
+    call_ev = timing_events(args.steps) if args.call_events else None
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
         kpa.kpa_time_next_decode_kernel(*kern_ev[k])
-        step(call_ev[k])
+        step(call_ev[k] if call_ev else None)
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
-    call_ms = np.array([a.elapsed_time(b) for a, b in call_ev])
     kern_ms = np.array([a.elapsed_time(b) for a, b in kern_ev])
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode call {call_ms.mean() * 1e3:.1f} us, "
-        f"decode kernel {kern_ms.mean() * 1e3:.1f} us (median {np.median(kern_ms) * 1e3:.1f})")
+    call_ms = np.array([a.elapsed_time(b) for a, b in call_ev]) if call_ev else None
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode kernel {kern_ms.mean() * 1e3:.1f} us "
+        f"(median {np.median(kern_ms) * 1e3:.1f})"
+        + (f", decode call {call_ms.mean() * 1e3:.1f} us" if call_ev else ""))
 
     if args.copy_calibration > 0:
         # a plain device-to-device copy of known size, after the timed region,
@@ -193,7 +200,8 @@ def main():
     tokens = int(inp.ctx_len.sum().item())  # cached tokens attended per step (per query)
     value = tokens / (ms_per_step / 1e3)
     roofline = decode_roofline(cfg, tokens, q.numel() * 4 + out.numel() * 4 + lse.numel() * 4,
-                               float(kern_ms.mean()), float(call_ms.mean()), kpa.kpa_decode_path(dims, n_q))
+                               float(kern_ms.mean()), float(call_ms.mean()) if call_ev else None,
+                               kpa.kpa_decode_path(dims, n_q))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -244,9 +252,10 @@ def decode_roofline(cfg, tokens, io_bytes, kern_ms, call_ms, path):
          "frac": round(achieved / peak, 4), "traffic": None,
          "kernel": f"split-KV decode kernel ({path})", "launch_us": round(kern_ms * 1e3, 2),
          "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops,
-         "hbm_gbps": round(hbm_gbps, 1), "tflops": round(tflops, 2),
-         "call_us": round(call_ms * 1e3, 2),
-         "call_frac": round((hbm_gbps if bound == "hbm" else tflops) * kern_ms / call_ms / peak, 4)}
+         "hbm_gbps": round(hbm_gbps, 1), "tflops": round(tflops, 2)}
+    if call_ms:
+        r["call_us"] = round(call_ms * 1e3, 2)
+        r["call_frac"] = round(achieved * kern_ms / call_ms / peak, 4)
     t = stored_traffic(cfg.name)
     if t is not None:
         r["traffic"] = t
@@ -334,14 +343,25 @@ def summarize_trace(args):
     rf = res["roofline"]
     dec = [r for r in rows if "decode_" in r["Name"] and "_kernel" in r["Name"]]
     lines += ["", "Same run, bench.py's own figures (HIP events on the launch stream, timed steps only):", "",
-              f"- decode kernel average: {rf['launch_us']} us",
-              f"- decode call (kernel + merge) average: {rf['call_us']} us",
-              f"- ms per step: {res['ms_per_step']}",
+              f"- decode kernel average: {rf['launch_us']} us"]
+    if "call_us" in rf:
+        lines.append(f"- decode call (kernel + merge) average: {rf['call_us']} us")
+    lines += [f"- ms per step: {res['ms_per_step']}",
               f"- roofline: {rf['achieved']} {rf['unit']} of {rf['peak']} ({100 * rf['frac']:.1f}%), bound {rf['bound']}"]
-    if dec:
-        avg = float(dec[0]["AverageNs"]) / 1e3
+    avg = float(dec[0]["AverageNs"]) / 1e3 if dec else None
+    if avg:
         lines.append(f"- rocprofv3 decode kernel average: {avg:.1f} us "
-                     f"({100 * (rf['launch_us'] - avg) / avg:+.1f}% for the events)")
+                     f"({100 * (rf['launch_us'] - avg) / avg:+.1f}% for the events under the profiler)")
+    if args.plain_json:
+        with open(args.plain_json) as f:
+            plain = json.loads(f.read().strip().splitlines()[-1])
+        pr = plain["roofline"]
+        lines += ["", "The same bench.py command without the profiler (same box, right before; the profiler "
+                      "lengthens each dispatch as the events see it):", "",
+                  f"- decode kernel average: {pr['launch_us']} us"
+                  + (f" ({100 * (pr['launch_us'] - avg) / avg:+.1f}% against rocprofv3's average)" if avg else ""),
+                  f"- ms per step: {plain['ms_per_step']}",
+                  f"- roofline: {pr['achieved']} {pr['unit']} of {pr['peak']} ({100 * pr['frac']:.1f}%), bound {pr['bound']}"]
     out = os.path.join(PROFILES, f"decode_kernels_{wl}.md")
     os.makedirs(PROFILES, exist_ok=True)
     with open(out, "w") as f:

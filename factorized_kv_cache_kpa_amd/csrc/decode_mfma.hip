@@ -520,11 +520,11 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 
 template <class C>
 struct Entry {
-    static hipError_t launch(const DecodeParams& P, hipStream_t s) {
+    static hipError_t launch(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
         const int qwg = (P.n_q + C::QPW - 1) / C::QPW;
         const int split_pad = (P.n_split + kXcds - 1) / kXcds * kXcds;
         dim3 grid(split_pad * qwg, P.batch);
-        hipLaunchKernelGGL(decode_mfma_kernel<C>, grid, dim3(C::WAVES * 64), 0, s, P);
+        hipExtLaunchKernelGGL(decode_mfma_kernel<C>, grid, dim3(C::WAVES * 64), 0, s, ev.start, ev.stop, 0, P);
         return hipGetLastError();
     }
     // Workgroups of this kernel one CU holds at once (registers and LDS).
@@ -545,7 +545,7 @@ struct Entry {
 struct MfmaKernel {
     int p1, p2, q1, q2, r_k, r_v;
     bool multi;  // kernel for n_q > 1
-    hipError_t (*launch)(const DecodeParams&, hipStream_t);
+    hipError_t (*launch)(const DecodeParams&, hipStream_t, const KernelEvents&);
     int (*blocks_per_cu)();
     int queries_per_group;
 };
@@ -594,9 +594,9 @@ int decode_mfma_query_groups(const kpa_dims& d, int n_q) {
     return k ? (n_q + k->queries_per_group - 1) / k->queries_per_group : 1;
 }
 
-hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s) {
+hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
     const MfmaKernel* k = find_kernel(P.d, P.n_q);
-    return k ? k->launch(P, s) : hipErrorInvalidValue;
+    return k ? k->launch(P, s, ev) : hipErrorInvalidValue;
 }
 
 }  // namespace kpa

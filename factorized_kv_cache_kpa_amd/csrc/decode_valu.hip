@@ -191,13 +191,13 @@ size_t decode_valu_smem(const kpa_dims& d) {
     return sizeof(float) * ((size_t)h * dh + (size_t)h * kTileSlots + 3 * (size_t)h + d.q2);
 }
 
-hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s) {
+hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
     dim3 grid(P.n_split, P.n_q, P.batch);
     const size_t smem = decode_valu_smem(P.d);
     if (P.d.dtype == KPA_F32)
-        hipLaunchKernelGGL(decode_valu_kernel<true>, grid, dim3(kThreads), smem, s, P);
+        hipExtLaunchKernelGGL(decode_valu_kernel<true>, grid, dim3(kThreads), smem, s, ev.start, ev.stop, 0, P);
     else
-        hipLaunchKernelGGL(decode_valu_kernel<false>, grid, dim3(kThreads), smem, s, P);
+        hipExtLaunchKernelGGL(decode_valu_kernel<false>, grid, dim3(kThreads), smem, s, ev.start, ev.stop, 0, P);
     return hipGetLastError();
 }
 

@@ -120,11 +120,8 @@ size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t m
     return plan.workspace_bytes;
 }
 
-// Events the next decode call on this thread records around its split-KV
-// decode kernel (kpa_time_next_decode_kernel).
-struct KernelEvents {
-    hipEvent_t start = nullptr, stop = nullptr;
-};
+// Events the next decode call on this thread has stamped with its split-KV
+// decode kernel's start and end (kpa_time_next_decode_kernel).
 static thread_local KernelEvents t_kernel_events;
 
 static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch, int32_t capacity,
@@ -178,10 +175,8 @@ static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch,
     P.q_scale = (float)(1.4426950408889634 / (dims->r_k * sqrt((double)dh)));
     P.v_scale = (float)(1.0 / dims->r_v);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (ev.start && hipEventRecord(ev.start, s) != hipSuccess) return KPA_ERR_HIP;
-    hipError_t e = launch_plan(plan, P, s);
+    hipError_t e = launch_plan(plan, P, s, ev);
     if (e != hipSuccess) return KPA_ERR_HIP;
-    if (ev.stop && hipEventRecord(ev.stop, s) != hipSuccess) return KPA_ERR_HIP;
     if (plan.n_split > 1 && launch_merge(P, s) != hipSuccess) return KPA_ERR_HIP;
     return KPA_OK;
 }

@@ -5,6 +5,7 @@
 //       Structured Factorization" (arXiv 2610.12657).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -144,11 +145,17 @@ __device__ __forceinline__ void clear_merge_counters(const DecodeParams& P, int6
     }
 }
 
+// Events a decode launcher has the runtime stamp with its kernel's own start
+// and end (hipExtLaunchKernel), for measurement; both null = plain launch.
+struct KernelEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+
 // Launchers (one per translation unit).
 hipError_t launch_append(const AppendParams& P, hipStream_t s);
-hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s);
+hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_merge(const DecodeParams& P, hipStream_t s);
-hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);
 bool decode_mfma_supported(const kpa_dims& d, int n_q);
 int decode_mfma_blocks_per_cu(const kpa_dims& d, int n_q);
 int decode_mfma_query_groups(const kpa_dims& d, int n_q);

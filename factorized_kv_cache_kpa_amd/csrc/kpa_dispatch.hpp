@@ -93,10 +93,10 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
     return p;
 }
 
-inline hipError_t launch_plan(const Plan& plan, const DecodeParams& P, hipStream_t s) {
+inline hipError_t launch_plan(const Plan& plan, const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
     switch (plan.path) {
-        case Path::kValu: return launch_decode_valu(P, s);
-        case Path::kMfmaSq: return launch_decode_mfma(P, s);
+        case Path::kValu: return launch_decode_valu(P, s, ev);
+        case Path::kMfmaSq: return launch_decode_mfma(P, s, ev);
         default: return hipErrorInvalidValue;
     }
 }

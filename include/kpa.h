@@ -210,11 +210,12 @@ int kpa_decode_multiq(const kpa_dims* dims, const void* cache, int32_t batch, in
  * stop_event are hipEvent_t handles created by the caller with timing
  * enabled (both non-NULL), or both NULL to cancel a pending request.  The
  * next kpa_decode / kpa_decode_multiq call made on the same host thread
- * records start_event on its stream right before its split-KV decode kernel
- * and stop_event right after it, before the log-sum-exp merge; the request
- * is then dropped, also when that call fails its checks.  Lets a caller time
- * the decode kernel alone on the stream it runs on.  The events stay owned
- * by the caller and must outlive that call.
+ * launches its split-KV decode kernel with hipExtLaunchKernel so that the
+ * runtime stamps start_event and stop_event with that kernel's own start and
+ * end on its stream (the log-sum-exp merge is not included, and no extra
+ * marker enters the stream); the request is then dropped, also when that
+ * call fails its checks.  Lets a caller time the decode kernel alone.  The
+ * events stay owned by the caller and must outlive that call.
  * Returns KPA_OK, or KPA_ERR_NULL_PTR if exactly one handle is NULL.
  */
 int kpa_time_next_decode_kernel(void* start_event, void* stop_event);
