@@ -79,6 +79,10 @@ struct Cfg {
     static constexpr int ROWS_P = pow2_at_least(ROWS);
     static constexpr int GROUPS = 64 / ROWS_P;       // lanes per row
     static constexpr int TPG = 32 / GROUPS;          // slots per lane
+    // row stride of the per-wave score scratch, padded so that the softmax's
+    // reads (TPG consecutive floats per lane, rows = lane % ROWS_P) fall in
+    // distinct LDS banks
+    static constexpr int ZS = 32 + (ROWS_P >= 8 ? 4 : ROWS_P == 4 ? 8 : 16);
     static constexpr int QROT = F_IS_B ? QF : QG;    // rotary pairs live in B's feature dim
     // cache sets
     static constexpr int SET_GK = F_IS_B ? 0 : 1;
@@ -99,7 +103,7 @@ struct Cfg {
 // Per-wave LDS scratch: scores, overwritten in place by the softmax weights.
 template <class S>
 struct alignas(16) WaveScratch {
-    float zp[S::ROWS_P][32];
+    float zp[S::ROWS_P][S::ZS];
     float alpha[S::ROWS_P];
     float m_fin[S::ROWS_P];
     float l_fin[S::ROWS_P];
@@ -240,9 +244,15 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
             const bool key = k < KB;
             const int kb = key ? k : k - KB;
             const int left = (key ? S::GK_BYTES : S::GV_BYTES) - kb * 1024;
-            const uint8_t* src = (key ? tile + offGK : tile + offGV) + kb * 1024;
+            // value set: 16-byte chunk q of element row e lands at chunk
+            // q ^ ((e >> 1) & 3) of its 64-byte row (gv_chunk), so the value
+            // phase's reads of 16 rows x 4 chunks hit distinct LDS banks; a
+            // DMA lane writes a fixed LDS position, so it fetches the chunk
+            // that belongs there
+            const int vchunk = (lane & ~3) | ((lane & 3) ^ ((lane >> 3) & 3));
+            const uint8_t* src = (key ? tile + offGK : tile + offGV) + kb * 1024 + (key ? lane : vchunk) * 16;
             constexpr bool kWholeBlocks = S::GK_BYTES % 1024 == 0 && S::GV_BYTES % 1024 == 0;
-            if (kWholeBlocks || lane * 16 < left) dma_to_lds16(src + lane * 16, lds_addr(gdst + k * 1024));
+            if (kWholeBlocks || lane * 16 < left) dma_to_lds16(src, lds_addr(gdst + k * 1024));
         }
 #pragma unroll
         for (int r = 0; r < RK; ++r)
@@ -318,7 +328,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 #pragma unroll
                         for (int bb = 0; bb < ZB; ++bb) {
                             const int R = mb * 32 + 8 * a + 4 * half + bb;
-                            if (kFull32 || R < M) zrow[R * 32 + s] = ok ? zp[u][a][bb] : -INFINITY;
+                            if (kFull32 || R < M) zrow[R * S::ZS + s] = ok ? zp[u][a][bb] : -INFINITY;
                         }
                 } else {
                     float z4[4];
@@ -328,7 +338,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                         // rows 8a + 4half + b: iG = mb*8 + 2a + half, jG = b -- complete in lane
 #pragma unroll
                         for (int a = 0; a < 4; ++a)
-                            if (kFull32 || mb * 32 + 8 * a + 4 * half < M) zrow[(mb * 8 + 2 * a + half) * 32 + s] = ok ? z4[a] : -INFINITY;
+                            if (kFull32 || mb * 32 + 8 * a + 4 * half < M) zrow[(mb * 8 + 2 * a + half) * S::ZS + s] = ok ? z4[a] : -INFINITY;
                     } else if constexpr (QG == 8) {
                         // iG = mb*4 + a, jG = 4half + b: add the other half
 #pragma unroll
@@ -336,14 +346,14 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                         // selects, not a lane-dependent array index (which would go to scratch)
                         const float za = half ? z4[2] : z4[0];
                         const float zb = half ? z4[3] : z4[1];
-                        if (kFull32 || mb * 32 + 16 * half < M) zrow[(mb * 4 + 2 * half + 0) * 32 + s] = ok ? za : -INFINITY;
-                        if (kFull32 || mb * 32 + 16 * half + 8 < M) zrow[(mb * 4 + 2 * half + 1) * 32 + s] = ok ? zb : -INFINITY;
+                        if (kFull32 || mb * 32 + 16 * half < M) zrow[(mb * 4 + 2 * half + 0) * S::ZS + s] = ok ? za : -INFINITY;
+                        if (kFull32 || mb * 32 + 16 * half + 8 < M) zrow[(mb * 4 + 2 * half + 1) * S::ZS + s] = ok ? zb : -INFINITY;
                     } else {
                         // QG == 16: iG = mb*2 + a/2, jG = 8(a%2) + 4half + b
                         float z0 = z4[0] + z4[1], z1 = z4[2] + z4[3];
                         z0 = sum_halves(z0);
                         z1 = sum_halves(z1);
-                        if (kFull32 || mb * 32 + 16 * half < M) zrow[(mb * 2 + half) * 32 + s] = ok ? (half ? z1 : z0) : -INFINITY;
+                        if (kFull32 || mb * 32 + 16 * half < M) zrow[(mb * 2 + half) * S::ZS + s] = ok ? (half ? z1 : z0) : -INFINITY;
                     }
                 }
             }
@@ -426,7 +436,8 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                 for (int r = 0; r < RV; ++r) {
                     float gvf[8];
                     if (row_ok) {
-                        unpack_bf16x8(*reinterpret_cast<const bf16x8*>(gvbase + ((r * M + R_row) * 32 + 8 * g16) * 2), gvf);
+                        const int e = r * M + R_row;  // element row of the value set
+                        unpack_bf16x8(*reinterpret_cast<const bf16x8*>(gvbase + e * 64 + ((g16 ^ ((e >> 1) & 3)) * 16)), gvf);
                     } else {
 #pragma unroll
                         for (int k = 0; k < 8; ++k) gvf[k] = 0.f;
