@@ -209,3 +209,34 @@ def test_odd_shape_and_two_level_merge(gpu_lib, dtype):
     for s in (1, 9, 75):
         go, gl = run_decode(inp, dims, cache, cap, num_splits=s)
         assert_close(go, gl, ro, rl, dtype, f"odd shape, splits={s}")
+
+
+@pytest.mark.parametrize("name,batch,ctx", [("kpa_32k", 32, 8192), ("long_512k", 1, 40000)])
+def test_garbage_workspace_and_repeated_calls(gpu_lib, name, batch, ctx):
+    """The workspace is caller scratch: fill it with random bytes, use it for
+    several calls in a row with the automatic chunk count, and check every
+    call against the oracle (ragged contexts, one of them empty)."""
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, seed=13, batch=batch, ctx=ctx, ragged=True)
+    inp.ctx_len[0] = ctx
+    if batch > 2:
+        inp.ctx_len[1] = 0
+        inp.ctx_len[2] = 33
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    ro, rl = _oracle(inp)
+    h, dh = dims.h, dims.d_h
+    ws = kpa.alloc_workspace(dims, batch, ctx)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda", generator=g))
+    q = inp.q.cuda().view(batch, h, dh)
+    qp = inp.q_pos.cuda().view(batch)
+    cl = inp.ctx_len.cuda()
+    for call in range(3):
+        out = torch.full((batch, h, dh), float("nan"), device="cuda")
+        lse = torch.full((batch, h), float("nan"), device="cuda")
+        kpa.kpa_decode(dims, cache, batch, cap, cl, ctx, q, qp, out, lse, ws)
+        torch.cuda.synchronize()
+        go = out.cpu().numpy().astype(np.float64)[:, None]
+        gl = lse.cpu().numpy().astype(np.float64)[:, None]
+        assert_close(go, gl, ro, rl, cfg.dtype, f"{name} call {call}")
