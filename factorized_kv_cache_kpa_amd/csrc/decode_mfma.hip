@@ -109,6 +109,28 @@ struct alignas(16) WaveScratch {
     float l_fin[S::ROWS_P];
 };
 
+// The G blocks of one tile, HBM -> LDS by DMA: 1 KB blocks of the key set,
+// then of the value set, dealt to the waves round-robin.  A set's last block
+// may be partial: only lanes inside the set copy.  Value set: 16-byte chunk q
+// of element row e lands at chunk q ^ ((e >> 1) & 3) of its 64-byte row, so
+// the value phase's reads of 16 rows x 4 chunks hit distinct LDS banks; a
+// DMA lane writes a fixed LDS position, so it fetches the chunk that belongs
+// there.
+template <class S>
+__device__ __forceinline__ void dma_g_blocks(const uint8_t* gk, const uint8_t* gv, uint8_t* gdst, int wave, int lane) {
+    constexpr int KB = S::GK_BLOCKS, NBLK = S::G_BLOCKS;
+#pragma unroll
+    for (int k = wave; k < NBLK; k += S::WAVES) {
+        const bool key = k < KB;
+        const int kb = key ? k : k - KB;
+        const int left = (key ? S::GK_BYTES : S::GV_BYTES) - kb * 1024;
+        const int vchunk = (lane & ~3) | ((lane & 3) ^ ((lane >> 3) & 3));
+        const uint8_t* src = (key ? gk : gv) + kb * 1024 + (key ? lane : vchunk) * 16;
+        constexpr bool kWholeBlocks = S::GK_BYTES % 1024 == 0 && S::GV_BYTES % 1024 == 0;
+        if (kWholeBlocks || lane * 16 < left) dma_to_lds16(src, lds_addr(gdst + k * 1024));
+    }
+}
+
 template <class S>
 __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kernel(DecodeParams P) {
     constexpr int PG = S::PG_, QG = S::QG_, PF = S::PF_, QF = S::QF_, RK = S::RK_, RV = S::RV_;
@@ -140,6 +162,24 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     WaveScratch<S>& ws = scratch[wave];
     const Layout& L = P.L;
     const int n0 = qwg * S::QPW + qsub * NQW;  // first query of this wave
+
+    // One query per wave: the first tile goes in flight before the query is
+    // prepared (its latency hides the rotation's float64 arithmetic).  Its
+    // G blocks land in gbuf_a by DMA; its F slice is loaded into fa below,
+    // where the registers are declared.
+    constexpr bool kEarly = NQW == 1;
+    int early_first = 0, early_last = 0;
+    if constexpr (kEarly) {
+        int vis_e = 0;
+        for (int n = qwg * S::QPW; n < min(P.n_q, (qwg + 1) * S::QPW); ++n) vis_e = max(vis_e, visible_slots(P, b, n));
+        early_first = split * P.chunk_tiles * kTileSlots;
+        early_last = min(early_first + P.chunk_tiles * kTileSlots, vis_e);
+        if (early_first < early_last) {
+            const uint8_t* tile = P.cache + (int64_t)b * L.n_tiles * L.tile_bytes +
+                                  (int64_t)(early_first / kTileSlots) * L.tile_bytes;
+            dma_g_blocks<S>(tile + L.off[S::SET_GK], tile + L.off[S::SET_GV], gbuf_a, wave, lane);
+        }
+    }
 
     // ---- rotated, scaled queries as MFMA A operands (hi + lo bf16) ----------
     for (int e = threadIdx.x; e < S::QPW * (S::QROT / 2); e += S::WAVES * 64) {
@@ -231,29 +271,12 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     //  * the wave's own F slice: HBM -> registers, double-buffered.
     // At the top of each tile one wait for everything issued a tile earlier
     // and one barrier (all G blocks landed; the other buffer is free).
-    constexpr int KB = S::GK_BLOCKS, NBLK = S::G_BLOCKS;
+    constexpr int KB = S::GK_BLOCKS;
     struct FRegs {
         bf16x8 fk[RK][KC];
         bf16x8 fv[RV][KC];
     };
-    auto issue = [&](const uint8_t* tile, uint8_t* gdst, FRegs& f) {
-#pragma unroll
-        for (int k = wave; k < NBLK; k += S::WAVES) {
-            // 1 KB blocks of the key set, then of the value set; a set's last
-            // block may be partial: only lanes inside the set copy
-            const bool key = k < KB;
-            const int kb = key ? k : k - KB;
-            const int left = (key ? S::GK_BYTES : S::GV_BYTES) - kb * 1024;
-            // value set: 16-byte chunk q of element row e lands at chunk
-            // q ^ ((e >> 1) & 3) of its 64-byte row (gv_chunk), so the value
-            // phase's reads of 16 rows x 4 chunks hit distinct LDS banks; a
-            // DMA lane writes a fixed LDS position, so it fetches the chunk
-            // that belongs there
-            const int vchunk = (lane & ~3) | ((lane & 3) ^ ((lane >> 3) & 3));
-            const uint8_t* src = (key ? tile + offGK : tile + offGV) + kb * 1024 + (key ? lane : vchunk) * 16;
-            constexpr bool kWholeBlocks = S::GK_BYTES % 1024 == 0 && S::GV_BYTES % 1024 == 0;
-            if (kWholeBlocks || lane * 16 < left) dma_to_lds16(src, lds_addr(gdst + k * 1024));
-        }
+    auto load_f = [&](const uint8_t* tile, FRegs& f) {
 #pragma unroll
         for (int r = 0; r < RK; ++r)
 #pragma unroll
@@ -264,6 +287,10 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 #pragma unroll
             for (int nb = 0; nb < KC; ++nb)
                 f.fv[r][nb] = ld16<bf16x8>(tile + offFV + ((int64_t)((r * PF + iF) * QF + 16 * nb + l16) * 32 + 8 * g16) * 2);
+    };
+    auto issue = [&](const uint8_t* tile, uint8_t* gdst, FRegs& f) {
+        dma_g_blocks<S>(tile + offGK, tile + offGV, gdst, wave, lane);
+        load_f(tile, f);
     };
 
     auto process = [&](int s0, const uint8_t* gcur, FRegs& f) {
@@ -464,7 +491,11 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 
     FRegs fa, fb;
     const uint8_t* t0 = seq + (int64_t)(first / kTileSlots) * L.tile_bytes;
-    if (first < last) issue(t0, gbuf_a, fa);
+    if constexpr (kEarly) {
+        if (first < last) load_f(t0, fa);  // the G blocks are on their way already
+    } else {
+        if (first < last) issue(t0, gbuf_a, fa);
+    }
     for (int s0 = first; s0 < last; s0 += 2 * kTileSlots) {
         // tile s0: data in gbuf_a and fa
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the DMA and loads issued one tile ago
