@@ -338,8 +338,9 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 #pragma unroll
                             for (int bb = 0; bb < 4; ++bb) zp[u][a][bb] += w[a * 4 + bb] * g[a][bb];
                         } else {
-                            zp[u][a][0] += w[a * 4 + 0] * g[a][0] + w[a * 4 + 1] * g[a][1] + w[a * 4 + 2] * g[a][2] +
-                                           w[a * 4 + 3] * g[a][3];
+                            // a chain of fused multiply-adds into the running sum
+#pragma unroll
+                            for (int bb = 0; bb < 4; ++bb) zp[u][a][0] = fmaf(w[a * 4 + bb], g[a][bb], zp[u][a][0]);
                         }
                     }
                 }
