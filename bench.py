@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--plain-json", default=None, help="JSON line of the same command run without the profiler")
     ap.add_argument("--summarize-pmc", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--summarize-util", default=None, metavar="PMC_DIR",
+                    help="write profiles/decode_util_<workload>.md from one --pmc run of the activity counters")
     ap.add_argument("--cmd", action="append", default=[], help="command recorded in a summary")
     return ap.parse_args()
 
@@ -73,6 +75,8 @@ def main():
         return summarize_trace(args)
     if args.summarize_pmc:
         return summarize_pmc(args)
+    if args.summarize_util:
+        return summarize_util(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the decode shards by sequence with no communication; see DESIGN.md)", file=sys.stderr)
@@ -420,6 +424,52 @@ def summarize_pmc(args):
               f"- kernel_sources_sha256: {kernel_sources_hash()}", ""]
     path = traffic_summary_path(wl)
     os.makedirs(PROFILES, exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
+def summarize_util(args):
+    """profiles/decode_util_<workload>.md: matrix-core and vector-ALU activity
+    of the decode kernel from one rocprofv3 --pmc run.  GRBM_GUI_ACTIVE sums
+    the busy cycles of the 8 XCDs; SQ_VALU_MFMA_BUSY_CYCLES sums the matrix
+    pipe's busy cycles over all 1024 SIMDs (it equals the kernel's MFMA count
+    times their issue cycles, 32 per 32x32x16 and 16 per 16x16x32 bf16);
+    SQ_ACTIVE_INST_VALU counts vector instructions issued, each holding its
+    SIMD for 4 cycles (64 lanes on 16)."""
+    rows = _read_csv(_find(args.summarize_util, "counter_collection.csv"))
+    dec = [r for r in rows if "decode_" in r["Kernel_Name"] and "_kernel" in r["Kernel_Name"]]
+    if not dec:
+        raise SystemExit("no decode kernel dispatches")
+    vals = {}
+    for r in dec:
+        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    wl = None
+    for c in args.cmd:
+        if "--workload" in c:
+            wl = c.split("--workload", 1)[1].split()[0]
+    wl = wl or "kpa_32k"
+    simds, xcds = 1024, 8
+    cycles = avg["GRBM_GUI_ACTIVE"] / xcds
+    mfma = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simds / cycles
+    valu = (avg["SQ_ACTIVE_INST_VALU"] * 4) / simds / cycles
+    lines = [f"# Matrix-core and vector-ALU activity of the split-KV decode kernel: {wl}", "",
+             "One counter pass of the bench command, from the repository root:", ""]
+    lines += [f"    {c}" for c in args.cmd] + [""]
+    lines += [f"Decode kernel: `{_short_kernel(dec[0]['Kernel_Name'])}`, {len(dec)} dispatches (averages below)", "",
+              "| counter | per dispatch |", "|---|---|"]
+    for k in sorted(avg):
+        lines.append(f"| {k} | {avg[k]:.0f} |")
+    lines += ["", "Derived (GRBM_GUI_ACTIVE sums 8 XCDs; the SQ busy/issue counters sum 1024 SIMDs;"
+                  " a vector instruction holds its SIMD 4 cycles):", "",
+              f"- kernel cycles per XCD: {cycles:.0f}",
+              f"- matrix-core pipe busy: {100 * mfma:.1f}% of SIMD cycles",
+              f"- vector ALU issue busy: {100 * valu:.1f}% of SIMD cycles",
+              f"- vector instructions per matrix instruction: "
+              f"{(avg['SQ_INSTS_VALU'] - avg['SQ_INSTS_MFMA']) / max(avg['SQ_INSTS_MFMA'], 1):.1f}",
+              f"- kernel_sources_sha256: {kernel_sources_hash()}", ""]
+    path = os.path.join(PROFILES, f"decode_util_{wl}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
