@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle sample time")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--factored-query", type=int, default=0, metavar="R_Q",
+                    help="decode with a factored query of rank R_Q (kpa_decode_factored) instead of a dense one")
     ap.add_argument("--call-events", action="store_true",
                     help="also bracket each whole decode call (kernel + merge) with events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -137,8 +139,15 @@ def main():
     lse = torch.empty((nb, n_q, h), device=dev)
     ws = kpa.alloc_workspace(dims, nb, ctx, n_q, args.num_splits, device=dev)
 
+    if args.factored_query > 0:
+        from workloads import make_query_factors
+        a_q, b_q = (t.to(dev).contiguous() for t in make_query_factors(cfg, args.factored_query, seed=0))
+
     def decode():
-        if n_q == 1:
+        if args.factored_query > 0:
+            kpa.kpa_decode_factored(dims, args.factored_query, cache, nb, ctx, ctx_len, ctx, n_q, 1, a_q, b_q,
+                                    q_pos, out, lse, ws, args.num_splits)
+        elif n_q == 1:
             kpa.kpa_decode(dims, cache, nb, ctx, ctx_len, ctx, q.view(nb, h, dh), q_pos.view(nb),
                            out.view(nb, h, dh), lse.view(nb, h), ws, args.num_splits)
         else:
@@ -219,6 +228,7 @@ def main():
         "config": {"workload": cfg.name, "batch": nb, "ctx": ctx, "n_q": n_q,
                    "split": [cfg.p1, cfg.p2, cfg.q1, cfg.q2], "ranks": [cfg.r_k, cfg.r_v],
                    "path": kpa.kpa_decode_path(dims, n_q), "step": "append new token(s) + decode",
+                   "query": f"factored, R_Q = {args.factored_query}" if args.factored_query > 0 else "dense",
                    "parallelism": "single GPU"},
         "achieved_hbm_gbps": roofline["hbm_gbps"], "hbm_pct_of_peak": round(100 * roofline["hbm_gbps"] / HBM_PEAK_GBPS, 2),
         "roofline": roofline, "cpu_baseline": cpu,

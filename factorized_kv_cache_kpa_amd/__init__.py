@@ -84,6 +84,9 @@ def load():
     lib.kpa_decode_multiq.argtypes = [DP, P, I32, I32, P, I32, I32, I32, P, P, P, P, P,
                                       ctypes.c_size_t, I32, P, P]
     lib.kpa_decode_multiq.restype = ctypes.c_int
+    lib.kpa_decode_factored.argtypes = [DP, I32, P, I32, I32, P, I32, I32, I32, P, P, P, P, P, P,
+                                        ctypes.c_size_t, I32, P, P]
+    lib.kpa_decode_factored.restype = ctypes.c_int
     lib.kpa_status_string.argtypes = [ctypes.c_int]
     lib.kpa_status_string.restype = ctypes.c_char_p
     lib.kpa_decode_path.argtypes = [DP, I32]
@@ -187,6 +190,20 @@ def kpa_decode_multiq(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causa
         _ptr(workspace, None, "workspace"), ws_bytes, num_splits,
         _ptr(dev_status, torch.int32, "dev_status"), _stream(stream))
     _check("kpa_decode_multiq", st)
+
+
+def kpa_decode_factored(dims, r_q, cache, batch, capacity, ctx_len, max_ctx, n_q, causal, a_q, b_q, q_pos,
+                        out, lse=None, workspace=None, num_splits=0, dev_status=None, stream=None):
+    """a_q [batch][n_q][r_q][p1][q1], b_q [batch][n_q][r_q][p2][q2] float32 (unrotated)."""
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().kpa_decode_factored(
+        ctypes.byref(dims), r_q, _ptr(cache, torch.uint8, "cache"), batch, capacity,
+        _ptr(ctx_len, torch.int32, "ctx_len"), max_ctx, n_q, int(bool(causal)),
+        _ptr(a_q, torch.float32, "a_q"), _ptr(b_q, torch.float32, "b_q"), _ptr(q_pos, torch.int32, "q_pos"),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(workspace, None, "workspace"), ws_bytes, num_splits,
+        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream))
+    _check("kpa_decode_factored", st)
 
 
 # --------------------------------------------------------------------------

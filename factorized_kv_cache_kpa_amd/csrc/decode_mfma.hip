@@ -198,14 +198,14 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 #pragma unroll
     for (int u = 0; u < NQW; ++u) {
         const int n = min(n0 + u, P.n_q - 1);  // queries past n_q compute and are discarded
-        const float* qg = P.q + ((int64_t)b * P.n_q + n) * S::H * S::DH;
+        const int64_t qrow = (int64_t)b * P.n_q + n;
         const int nq = qsub * NQW + u;
 #pragma unroll
         for (int mb = 0; mb < MB32; ++mb) {
             const int R = mb * 32 + s;
             const bool row_ok = kFull32 || R < M;  // padding rows of the last block are zero
             const int iG = row_ok ? R / QG : 0, jG = row_ok ? R % QG : 0;
-            const float* qi = qg + (int64_t)S::head(iG, iF) * S::DH;
+            const int qh = S::head(iG, iF);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 float v[8];
@@ -215,13 +215,13 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                     float x, y;  // this element and its rotary partner
                     int m, first;
                     if constexpr (S::F_IS_B_) {
-                        x = qi[S::feat(jG, jF)];
-                        y = qi[S::feat(jG, jF ^ 1)];
+                        x = query_elem(P, qrow, qh, S::feat(jG, jF));
+                        y = query_elem(P, qrow, qh, S::feat(jG, jF ^ 1));
                         m = jF >> 1;
                         first = !(jF & 1);
                     } else {
-                        x = qi[S::feat(jG, jF)];
-                        y = qi[S::feat(jG ^ 1, jF)];
+                        x = query_elem(P, qrow, qh, S::feat(jG, jF));
+                        y = query_elem(P, qrow, qh, S::feat(jG ^ 1, jF));
                         m = jG >> 1;
                         first = !(jG & 1);
                     }

@@ -4,7 +4,8 @@
 // kernels do not cover.
 //
 // Per (chunk of the cache, query, sequence) one workgroup:
-//   1. rotates the query with R_KPA(q_pos) and folds in log2(e)/(R_K sqrt(d_h))
+//   1. rotates the query (dense, or expanded from its Kronecker factors) with
+//      R_KPA(q_pos) and folds in log2(e)/(R_K sqrt(d_h))
 //      ([KPA] Def. 2.3, §2.3);
 //   2. per 32-slot tile, scores every (head, slot) in factor space: the query
 //      is contracted with B~^K over j2, then with A^K over j1 and summed over
@@ -69,11 +70,11 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P) {
         l_run[i] = 0.f;
     }
     __syncthreads();
-    const float* qg = P.q + ((int64_t)b * P.n_q + n) * h * dh;
+    const int64_t qrow = (int64_t)b * P.n_q + n;
     for (int pr = tid; pr < h * dh / 2; pr += kThreads) {
         const int e = 2 * pr;
         const int m = (e % d.q2) / 2;
-        const float x0 = qg[e], x1 = qg[e + 1];
+        const float x0 = query_elem(P, qrow, e / dh, e % dh), x1 = query_elem(P, qrow, e / dh, e % dh + 1);
         const float c = cs[2 * m], sn = cs[2 * m + 1];
         qr[e] = (x0 * c - x1 * sn) * P.q_scale;
         qr[e + 1] = (x0 * sn + x1 * c) * P.q_scale;

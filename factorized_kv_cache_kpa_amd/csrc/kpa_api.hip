@@ -124,9 +124,11 @@ size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t m
 // decode kernel's start and end (kpa_time_next_decode_kernel).
 static thread_local KernelEvents t_kernel_events;
 
+// factored: the query is (a_q, b_q, r_q); otherwise the dense q.
 static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch, int32_t capacity,
-                         const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
-                         const float* q, const int32_t* q_pos, float* out, float* lse,
+                         const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal, bool factored,
+                         const float* q, const float* a_q, const float* b_q, int32_t r_q,
+                         const int32_t* q_pos, float* out, float* lse,
                          void* workspace, size_t workspace_bytes, int32_t num_splits,
                          uint32_t* dev_status, void* stream) {
     // a pending measurement request applies to this call only
@@ -134,9 +136,12 @@ static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch,
     t_kernel_events = KernelEvents{};
     int st = check_decode_args(dims, batch, capacity, max_ctx, n_q);
     if (st != KPA_OK) return st;
+    if (factored && (r_q < 1 || r_q > KPA_MAX_RANK)) return KPA_ERR_INVALID_DIMS;
     if (batch == 0) return KPA_OK;
-    if (!cache || !ctx_len || !q || !q_pos || !out) return KPA_ERR_NULL_PTR;
-    if (!aligned(cache, 16) || !aligned(q, 16) || !aligned(out, 16)) return KPA_ERR_INVALID_ARG;
+    if (!cache || !ctx_len || !q_pos || !out || (factored ? (!a_q || !b_q) : !q)) return KPA_ERR_NULL_PTR;
+    if (!aligned(cache, 16) || !aligned(out, 16) || (!factored && !aligned(q, 16)) ||
+        (factored && (!aligned(a_q, 4) || !aligned(b_q, 4))))
+        return KPA_ERR_INVALID_ARG;
     Plan plan = plan_decode(*dims, batch, max_ctx, n_q, num_splits, num_cus());
     if (plan.path == Path::kUnsupported) return KPA_ERR_UNSUPPORTED;
     if (plan.workspace_bytes > 0) {
@@ -154,6 +159,9 @@ static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch,
     P.causal = causal ? 1 : 0;
     P.ctx_len = ctx_len;
     P.q = q;
+    P.a_q = a_q;
+    P.b_q = b_q;
+    P.r_q = factored ? r_q : 0;
     P.q_pos = q_pos;
     P.out = out;
     P.lse = lse;
@@ -191,8 +199,8 @@ int kpa_decode(const kpa_dims* dims, const void* cache, int32_t batch, int32_t c
                const int32_t* ctx_len, int32_t max_ctx, const float* q, const int32_t* q_pos,
                float* out, float* lse, void* workspace, size_t workspace_bytes,
                int32_t num_splits, uint32_t* dev_status, void* stream) {
-    return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, 1, 0, q, q_pos, out, lse,
-                         workspace, workspace_bytes, num_splits, dev_status, stream);
+    return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, 1, 0, false, q, nullptr, nullptr, 0, q_pos,
+                         out, lse, workspace, workspace_bytes, num_splits, dev_status, stream);
 }
 
 int kpa_decode_multiq(const kpa_dims* dims, const void* cache, int32_t batch, int32_t capacity,
@@ -200,8 +208,17 @@ int kpa_decode_multiq(const kpa_dims* dims, const void* cache, int32_t batch, in
                       const float* q, const int32_t* q_pos, float* out, float* lse,
                       void* workspace, size_t workspace_bytes, int32_t num_splits,
                       uint32_t* dev_status, void* stream) {
-    return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causal, q, q_pos, out,
-                         lse, workspace, workspace_bytes, num_splits, dev_status, stream);
+    return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causal, false, q, nullptr, nullptr, 0,
+                         q_pos, out, lse, workspace, workspace_bytes, num_splits, dev_status, stream);
+}
+
+int kpa_decode_factored(const kpa_dims* dims, int32_t r_q, const void* cache, int32_t batch, int32_t capacity,
+                        const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
+                        const float* a_q, const float* b_q, const int32_t* q_pos, float* out, float* lse,
+                        void* workspace, size_t workspace_bytes, int32_t num_splits,
+                        uint32_t* dev_status, void* stream) {
+    return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causal, true, nullptr, a_q, b_q, r_q,
+                         q_pos, out, lse, workspace, workspace_bytes, num_splits, dev_status, stream);
 }
 
 const char* kpa_status_string(int status) {

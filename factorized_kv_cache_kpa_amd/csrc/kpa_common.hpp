@@ -104,7 +104,10 @@ struct DecodeParams {
     int32_t batch, capacity, max_ctx;
     int32_t n_q, causal;
     const int32_t* ctx_len;
-    const float* q;
+    const float* q;       // dense query [batch][n_q][h][d_h], or null with a_q/b_q
+    const float* a_q;     // factored query: [batch][n_q][r_q][p1][q1]
+    const float* b_q;     //                 [batch][n_q][r_q][p2][q2]
+    int32_t r_q;
     const int32_t* q_pos;
     float* out;
     float* lse;
@@ -121,6 +124,21 @@ struct DecodeParams {
     float q_scale;        // log2(e) / (R_K sqrt(d_h))
     float v_scale;        // 1 / R_V
 };
+
+// Element (i, j) of the unrotated query of row (b, n): the dense query's, or,
+// for a factored query, (1/R_Q) sum_r A^Q_r[i1, j1] B^Q_r[i2, j2] with
+// i = i1 p2 + i2, j = j1 q2 + j2 ([KPA] Def. 2.1, Eq. (5): the query has the
+// keys' Kronecker form).
+__device__ __forceinline__ float query_elem(const DecodeParams& P, int64_t row, int i, int j) {
+    const kpa_dims& d = P.d;
+    if (P.a_q == nullptr) return P.q[(row * (d.p1 * d.p2) + i) * (d.q1 * d.q2) + j];
+    const int i1 = i / d.p2, i2 = i % d.p2, j1 = j / d.q2, j2 = j % d.q2;
+    const float* a = P.a_q + ((row * P.r_q) * d.p1 + i1) * d.q1 + j1;
+    const float* bb = P.b_q + ((row * P.r_q) * d.p2 + i2) * d.q2 + j2;
+    float acc = 0.f;
+    for (int r = 0; r < P.r_q; ++r) acc = fmaf(a[(int64_t)r * d.p1 * d.q1], bb[(int64_t)r * d.p2 * d.q2], acc);
+    return acc / (float)P.r_q;
+}
 
 // Visible slots of query n of sequence b (causal: the n_q newest slots hold
 // the queries' own tokens).  Out-of-range ctx_len is clamped and flagged.

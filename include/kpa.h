@@ -206,6 +206,29 @@ int kpa_decode_multiq(const kpa_dims* dims, const void* cache, int32_t batch, in
                       uint32_t* dev_status, void* stream);
 
 /*
+ * kpa_decode_factored -- decode with a factored query: the query of each
+ * (sequence, query) row has the keys' Kronecker form,
+ *   Q = (1/R_Q) sum_r A^Q_r (x) B^Q_r,  A^Q_r: p1 x q1,  B^Q_r: p2 x q2
+ * ([KPA] Eq. (5)-(6), Prop. 2.2: scores then follow from head-level
+ * A^Q . A^K and feature-level B^Q . B~^K products; [TPA] summary page,
+ * factored queries).  Arguments as kpa_decode_multiq, with
+ *   r_q: 1 <= R_Q <= KPA_MAX_RANK;
+ *   a_q [batch][n_q][r_q][p1][q1], b_q [batch][n_q][r_q][p2][q2]: float32,
+ *       device, unrotated (RoPE at q_pos is applied to B^Q, as to B^K);
+ *   n_q >= 1 queries per sequence, causal as for kpa_decode_multiq (ignored
+ *       for n_q = 1).
+ * The same kernels as the dense decode run; each workgroup expands the
+ * query elements it needs from the factors in its prologue.  The workspace
+ * is sized by kpa_decode_workspace_bytes(dims, batch, max_ctx, n_q, num_splits).
+ * Returns as kpa_decode; KPA_ERR_INVALID_DIMS for r_q out of range.
+ */
+int kpa_decode_factored(const kpa_dims* dims, int32_t r_q, const void* cache, int32_t batch, int32_t capacity,
+                        const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
+                        const float* a_q, const float* b_q, const int32_t* q_pos, float* out, float* lse,
+                        void* workspace, size_t workspace_bytes, int32_t num_splits,
+                        uint32_t* dev_status, void* stream);
+
+/*
  * kpa_time_next_decode_kernel -- measurement hook.  start_event and
  * stop_event are hipEvent_t handles created by the caller with timing
  * enabled (both non-NULL), or both NULL to cancel a pending request.  The

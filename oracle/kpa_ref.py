@@ -210,6 +210,22 @@ def decode(a_k, b_k, a_v, b_v, positions, ctx_len, q, q_pos, *, causal=True,
     return out, lse
 
 
+def query_from_factors(a_q, b_q) -> np.ndarray:
+    """Dense queries of factored ones: for every (sequence, query) row,
+    (1/R_Q) sum_r A^Q_r (x) B^Q_r ([KPA] Eq. (5) with Def. 2.1, the keys' form).
+
+    a_q: [B][n_q][R_Q][p1][q1], b_q: [B][n_q][R_Q][p2][q2] -> [B][n_q][h][d_h].
+    """
+    a_q = np.asarray(a_q, np.float64)
+    b_q = np.asarray(b_q, np.float64)
+    nb, nq = a_q.shape[0], a_q.shape[1]
+    out = np.zeros((nb, nq, a_q.shape[3] * b_q.shape[3], a_q.shape[4] * b_q.shape[4]))
+    for b in range(nb):
+        for n in range(nq):
+            out[b, n] = kron_reconstruct(a_q[b, n], b_q[b, n])
+    return out
+
+
 def factored_score(a_q, b_q, a_k, b_k, i1: int, i2: int) -> float:
     """Prop. 2.2 / Eq. (6): the score of head (i1, i2) from the factors alone.
 

@@ -115,6 +115,13 @@ def test_null_and_range_errors_return_before_launch():
     assert lib.kpa_decode(d, FAKE, 4, 4096, FAKE, 4096, FAKE, FAKE, FAKE, None, None, need, 8,
                           None, None) == -4
     assert lib.kpa_decode(d, None, 0, 4096, None, 4096, None, None, None, None, None, 0, 0, None, None) == 0
+    # factored query: rank out of range, missing factor, nothing to do
+    fq = lib.kpa_decode_factored
+    assert fq(d, 0, FAKE, 1, 64, FAKE, 64, 1, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -1
+    assert fq(d, 17, FAKE, 1, 64, FAKE, 64, 1, 0, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -1
+    assert fq(d, 2, FAKE, 1, 64, FAKE, 64, 1, 0, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -2
+    assert fq(d, 2, FAKE, 1, 64, FAKE, 64, 1, 0, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -2
+    assert fq(d, 2, None, 0, 64, None, 64, 1, 0, None, None, None, None, None, None, 0, 0, None, None) == 0
 
 
 def test_workspace_sizes_follow_the_split_count():

@@ -3,7 +3,8 @@
 Each case swaps one oracle function for a plausible wrong variant -- a
 transposed Kronecker order, a dropped 1/R, a flipped rotation sign, the
 other Kronecker order of the rotary operator, the wrong softmax scale, a
-causal off-by-one -- and checks that at least one pin fails.
+causal off-by-one, a factored query expanded with its factors' roles
+transposed -- and checks that at least one pin fails.
 """
 import numpy as np
 import pytest
@@ -60,6 +61,20 @@ def _decode_causal_off_by_one(a_k, b_k, a_v, b_v, positions, ctx_len, q, q_pos, 
     return np.stack(outs, 1), np.stack(lses, 1)
 
 
+_orig_query_from_factors = ref.query_from_factors
+
+
+def _query_factors_swapped(a_q, b_q):
+    # the roles of the head and feature factors exchanged in the expansion
+    a_q, b_q = np.asarray(a_q, np.float64), np.asarray(b_q, np.float64)
+    nb, nq, r = a_q.shape[:3]
+    out = np.zeros((nb, nq, a_q.shape[3] * b_q.shape[3], a_q.shape[4] * b_q.shape[4]))
+    for b in range(nb):
+        for n in range(nq):
+            out[b, n] = sum(np.kron(b_q[b, n, k], a_q[b, n, k]) for k in range(r)) / r
+    return out
+
+
 MUTATIONS = [
     ("kron_reconstruct", _kron_swapped, [pins.test_kron_entry_index_convention]),
     ("kron_reconstruct", _kron_no_norm, [pins.test_kron_sum_is_normalised_by_rank,
@@ -70,6 +85,8 @@ MUTATIONS = [
     ("attention_one_query", _attention_wrong_scale,
      [lambda: pins.test_non_contextual_tpa_reduces_to_textbook_attention("gqa")]),
     ("decode", _decode_causal_off_by_one, [pins.test_causal_first_query_sees_only_its_own_token]),
+    ("query_from_factors", _query_factors_swapped, [pins.test_query_from_factors_matches_element_formula,
+                                                    pins.test_factored_query_decode_equals_attention_from_factored_scores]),
 ]
 
 

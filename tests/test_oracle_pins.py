@@ -314,3 +314,55 @@ def test_causal_first_query_sees_only_its_own_token():
     for b in range(out.shape[0]):
         v0 = sum(ref.kron_block(av[b, 0, r], bv[b, 0, r]) for r in range(av.shape[2])) / av.shape[2]
         np.testing.assert_allclose(out[b, 0], v0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Factored query ([KPA] Eqs. (5)-(6), Prop. 2.2)
+# ---------------------------------------------------------------------------
+def test_query_from_factors_matches_element_formula():
+    rng = np.random.default_rng(21)
+    r_q, p1, q1, p2, q2 = 3, 2, 3, 4, 2
+    a_q = rng.normal(size=(2, 2, r_q, p1, q1))
+    b_q = rng.normal(size=(2, 2, r_q, p2, q2))
+    q = ref.query_from_factors(a_q, b_q)
+    for b in range(2):
+        for n in range(2):
+            for i1 in range(p1):
+                for i2 in range(p2):
+                    for j1 in range(q1):
+                        for j2 in range(q2):
+                            want = sum(a_q[b, n, r, i1, j1] * b_q[b, n, r, i2, j2] for r in range(r_q)) / r_q
+                            assert abs(q[b, n, i1 * p2 + i2, j1 * q2 + j2] - want) < 1e-14
+
+
+def test_factored_query_decode_equals_attention_from_factored_scores():
+    """Decode with the expanded query equals attention built from Eq. (6)
+    scores of the factors alone, with RoPE applied to B^Q and B^K rows
+    (Thm. 2.4) and V rebuilt from its factors (Eq. (4))."""
+    rng = np.random.default_rng(22)
+    r_q, r_k, r_v, p1, q1, p2, q2 = 2, 2, 3, 2, 2, 2, 4
+    ctx, nq, base = 7, 2, 10000.0
+    a_k = rng.normal(size=(1, ctx, r_k, p1, q1))
+    b_k = rng.normal(size=(1, ctx, r_k, p2, q2))
+    a_v = rng.normal(size=(1, ctx, r_v, p1, q1))
+    b_v = rng.normal(size=(1, ctx, r_v, p2, q2))
+    a_q = rng.normal(size=(1, nq, r_q, p1, q1))
+    b_q = rng.normal(size=(1, nq, r_q, p2, q2))
+    positions = np.arange(ctx)[None] * 3 + 5
+    q_pos = np.array([[positions[0, ctx - 2], positions[0, ctx - 1]]])
+    got, got_lse = ref.decode(a_k, b_k, a_v, b_v, positions, np.array([ctx]), ref.query_from_factors(a_q, b_q),
+                              q_pos, causal=True, base=base)
+    h, d_h = p1 * p2, q1 * q2
+    for n in range(nq):
+        vis = ctx - nq + n + 1
+        bq_rot = ref.append_rotate(b_q[0, n], q_pos[0, n], base)
+        for i1 in range(p1):
+            for i2 in range(p2):
+                z = np.array([ref.factored_score(a_q[0, n], bq_rot, a_k[0, s],
+                                                 ref.append_rotate(b_k[0, s], positions[0, s], base), i1, i2)
+                              for s in range(vis)]) / math.sqrt(d_h)
+                w = np.exp(z - z.max())
+                v = np.stack([ref.kron_reconstruct(a_v[0, s], b_v[0, s])[i1 * p2 + i2] for s in range(vis)])
+                want = (w[:, None] * v).sum(0) / w.sum()
+                assert np.allclose(got[0, n, i1 * p2 + i2], want, atol=1e-12, rtol=1e-12)
+                assert abs(got_lse[0, n, i1 * p2 + i2] - (z.max() + math.log(w.sum()))) < 1e-12

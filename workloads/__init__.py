@@ -5,6 +5,6 @@ problem shapes and draws random inputs.  Both the HIP path and the CPU oracle
 consume what it returns.
 """
 from .configs import CONFIGS, Config, SWEEP_SHAPES
-from .gen import Inputs, make_inputs
+from .gen import Inputs, make_inputs, make_query_factors
 
-__all__ = ["CONFIGS", "Config", "SWEEP_SHAPES", "Inputs", "make_inputs"]
+__all__ = ["CONFIGS", "Config", "SWEEP_SHAPES", "Inputs", "make_inputs", "make_query_factors"]

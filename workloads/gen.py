@@ -11,6 +11,11 @@ Recipe (the same for every consumer):
   * ``ragged``: per-sequence context lengths drawn uniformly in [n_q, ctx] with a
     second generator seeded ``seed + 1``.
 The factors are the unrotated ones the caller hands to the cache append.
+
+Factored queries (``make_query_factors``): their own generator seeded
+``seed + 2``; A^Q [batch][n_q][R_Q][p1][q1] with the config's A deviation,
+then B^Q [batch][n_q][R_Q][p2][q2] with its B deviation, both scaled so that
+the expanded query has unit-variance elements like the dense one, float32.
 """
 from __future__ import annotations
 
@@ -72,3 +77,16 @@ def make_inputs(cfg: Config, seed: int = 0, *, batch: int | None = None, ctx: in
     q_pos = (ctx_len.view(-1, 1) - nq + torch.arange(nq, dtype=torch.int32).view(1, -1)
              + pos_offset).to(torch.int32).contiguous()
     return Inputs(cfg, a_k, b_k, a_v, b_v, positions, ctx_len, q, q_pos)
+
+
+def make_query_factors(cfg: Config, r_q: int, seed: int = 0, *, batch: int | None = None,
+                       n_q: int | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Random factors of a factored query (see the module docstring)."""
+    nb = cfg.batch if batch is None else batch
+    nq = cfg.n_q if n_q is None else n_q
+    g = torch.Generator().manual_seed(seed + 2)
+    # an element of (1/R) sum_r a_r b_r has variance sa^2 sb^2 / R: scale it to 1
+    s = (r_q ** 0.5) ** 0.5
+    a_q = torch.randn((nb, nq, r_q, cfg.p1, cfg.q1), generator=g, dtype=torch.float32).mul_(s)
+    b_q = torch.randn((nb, nq, r_q, cfg.p2, cfg.q2), generator=g, dtype=torch.float32).mul_(s)
+    return a_q, b_q
