@@ -131,6 +131,53 @@ __device__ __forceinline__ void dma_g_blocks(const uint8_t* gk, const uint8_t* g
     }
 }
 
+// Query elements (iG, iF, jG, jF0 .. jF0 + 7) of row `row`, unrotated.  Dense:
+// two 16-byte loads.  Factored ((1/R_Q) sum_r A^Q_r (x) B^Q_r): per rank one
+// element of the G-side factor times 8 consecutive elements of the F-side
+// factor -- its feature dimension is the 16-wide one, so the 8 are contiguous.
+template <class S>
+__device__ __forceinline__ void query_group8(const DecodeParams& P, int64_t row, int iG, int iF, int jG, int jF0,
+                                             float* out) {
+    if (P.a_q == nullptr) {
+        const float* src = P.q + (row * S::H + S::head(iG, iF)) * S::DH;
+        if constexpr (S::F_IS_B_) {  // feat(jG, jF) = jG * QF + jF: contiguous in jF
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(src + S::feat(jG, jF0));
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + S::feat(jG, jF0) + 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                out[k] = lo[k];
+                out[4 + k] = hi[k];
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) out[k] = src[S::feat(jG, jF0 + k)];
+        }
+        return;
+    }
+    // F = B: A^Q_r[iG][jG] * B^Q_r[iF][jF];  F = A: A^Q_r[iF][jF] * B^Q_r[iG][jG]
+    constexpr int PA = S::F_IS_B_ ? S::PG_ : S::PF_, QA = S::F_IS_B_ ? S::QG_ : S::QF_;
+    constexpr int PB = S::F_IS_B_ ? S::PF_ : S::PG_, QB = S::F_IS_B_ ? S::QF_ : S::QG_;
+    const float* fs = S::F_IS_B_ ? P.b_q : P.a_q;  // the F side's factor (8 contiguous)
+    const float* gs = S::F_IS_B_ ? P.a_q : P.b_q;  // the G side's factor (one element)
+    constexpr int F_SET = S::F_IS_B_ ? PB * QB : PA * QA, G_SET = S::F_IS_B_ ? PA * QA : PB * QB;
+    const float* f = fs + row * P.r_q * F_SET + iF * S::QF_ + jF0;
+    const float* g = gs + row * P.r_q * G_SET + iG * S::QG_ + jG;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < P.r_q; ++r) {
+        const float gv = g[(int64_t)r * G_SET];
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(f + (int64_t)r * F_SET);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(f + (int64_t)r * F_SET + 4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            acc[k] = fmaf(gv, lo[k], acc[k]);
+            acc[4 + k] = fmaf(gv, hi[k], acc[4 + k]);
+        }
+    }
+    const float inv = 1.f / (float)P.r_q;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) out[k] = acc[k] * inv;
+}
+
 template <class S>
 __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kernel(DecodeParams P) {
     constexpr int PG = S::PG_, QG = S::QG_, PF = S::PF_, QF = S::QF_, RK = S::RK_, RV = S::RV_;
@@ -205,23 +252,29 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
             const int R = mb * 32 + s;
             const bool row_ok = kFull32 || R < M;  // padding rows of the last block are zero
             const int iG = row_ok ? R / QG : 0, jG = row_ok ? R % QG : 0;
-            const int qh = S::head(iG, iF);
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
+                // the 8 query elements (jG, jF0 .. jF0 + 7) of this lane and
+                // their rotary partners: (jG, jF ^ 1) when F = B (inside the
+                // same 8), (jG ^ 1, jF) when F = A
+                const int jF0 = 16 * kc + 8 * half;
+                float xs[8], ys[8];
+                query_group8<S>(P, qrow, iG, iF, jG, jF0, xs);
+                if constexpr (!S::F_IS_B_) query_group8<S>(P, qrow, iG, iF, jG ^ 1, jF0, ys);
                 float v[8];
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                    const int jF = 16 * kc + 8 * half + k;
+                    const int jF = jF0 + k;
                     float x, y;  // this element and its rotary partner
                     int m, first;
                     if constexpr (S::F_IS_B_) {
-                        x = query_elem(P, qrow, qh, S::feat(jG, jF));
-                        y = query_elem(P, qrow, qh, S::feat(jG, jF ^ 1));
+                        x = xs[k];
+                        y = xs[k ^ 1];
                         m = jF >> 1;
                         first = !(jF & 1);
                     } else {
-                        x = query_elem(P, qrow, qh, S::feat(jG, jF));
-                        y = query_elem(P, qrow, qh, S::feat(jG ^ 1, jF));
+                        x = xs[k];
+                        y = ys[k];
                         m = jG >> 1;
                         first = !(jG & 1);
                     }

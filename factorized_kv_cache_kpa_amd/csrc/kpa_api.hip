@@ -140,7 +140,7 @@ static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch,
     if (batch == 0) return KPA_OK;
     if (!cache || !ctx_len || !q_pos || !out || (factored ? (!a_q || !b_q) : !q)) return KPA_ERR_NULL_PTR;
     if (!aligned(cache, 16) || !aligned(out, 16) || (!factored && !aligned(q, 16)) ||
-        (factored && (!aligned(a_q, 4) || !aligned(b_q, 4))))
+        (factored && (!aligned(a_q, 16) || !aligned(b_q, 16))))
         return KPA_ERR_INVALID_ARG;
     Plan plan = plan_decode(*dims, batch, max_ctx, n_q, num_splits, num_cus());
     if (plan.path == Path::kUnsupported) return KPA_ERR_UNSUPPORTED;

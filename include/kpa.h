@@ -214,7 +214,8 @@ int kpa_decode_multiq(const kpa_dims* dims, const void* cache, int32_t batch, in
  * factored queries).  Arguments as kpa_decode_multiq, with
  *   r_q: 1 <= R_Q <= KPA_MAX_RANK;
  *   a_q [batch][n_q][r_q][p1][q1], b_q [batch][n_q][r_q][p2][q2]: float32,
- *       device, unrotated (RoPE at q_pos is applied to B^Q, as to B^K);
+ *       device, 16-byte aligned, unrotated (RoPE at q_pos is applied to B^Q,
+ *       as to B^K);
  *   n_q >= 1 queries per sequence, causal as for kpa_decode_multiq (ignored
  *       for n_q = 1).
  * The same kernels as the dense decode run; each workgroup expands the
