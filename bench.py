@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--plain-json", default=None, help="JSON line of the same command run without the profiler")
     ap.add_argument("--summarize-pmc", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--sweep", choices=["flashtpa"], default=None,
+                    help="time the decode over FlashTPA's benchmark shapes instead of one workload")
+    ap.add_argument("--sweep-out", default=None, help="write the sweep table (markdown) here")
     ap.add_argument("--summarize-util", default=None, metavar="PMC_DIR",
                     help="write profiles/decode_util_<workload>.md from one --pmc run of the activity counters")
     ap.add_argument("--cmd", action="append", default=[], help="command recorded in a summary")
@@ -79,6 +82,8 @@ def main():
         return summarize_pmc(args)
     if args.summarize_util:
         return summarize_util(args)
+    if args.sweep:
+        return sweep_flashtpa(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the decode shards by sequence with no communication; see DESIGN.md)", file=sys.stderr)
@@ -437,6 +442,84 @@ def summarize_pmc(args):
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
+
+
+def sweep_flashtpa(args):
+    """Decode kernel time over FlashTPA's benchmark grid (TPA split, d_h = 64,
+    R_K = R_V = 1; heads x batch x sequence length).  Factors and queries are
+    drawn on the GPU from a seeded generator (no oracle here: the same shapes
+    are parity-tested at small sizes); the cache is filled by kpa_cache_append
+    before timing.  One line per shape: kernel and whole-call time (decode +
+    merge), cached tokens/s and the kernel's HBM roofline fraction."""
+    import numpy as np
+    import torch
+
+    import factorized_kv_cache_kpa_amd as kpa
+    from workloads import FLASHTPA_BATCHES, FLASHTPA_HEADS, FLASHTPA_SEQS, flashtpa_config
+
+    kpa.load()
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(0)
+    rows = []
+    for h in FLASHTPA_HEADS:
+        for nb in FLASHTPA_BATCHES:
+            for ctx in FLASHTPA_SEQS:
+                cfg = flashtpa_config(h, nb, ctx)
+                dims = kpa.make_dims(cfg.p1, cfg.p2, cfg.q1, cfg.q2, cfg.r_k, cfg.r_v, dtype=cfg.dtype)
+                cache = kpa.alloc_cache(dims, nb, ctx, device=dev)
+                chunk = 8192
+                for s0 in range(0, ctx, chunk):
+                    n = min(chunk, ctx - s0)
+
+                    def draw(p, q):
+                        return (torch.randn((nb, n, 1, p, q), generator=g, device=dev) * 0.125).to(torch.bfloat16)
+
+                    pos = torch.arange(s0, s0 + n, dtype=torch.int32, device=dev).repeat(nb, 1).contiguous()
+                    kpa.kpa_cache_append(dims, cache, nb, ctx, draw(h, 1), draw(1, 64), draw(h, 1), draw(1, 64), pos,
+                                         torch.full((nb,), s0, dtype=torch.int32, device=dev), n_new=n)
+                q = torch.randn((nb, h, 64), generator=g, device=dev)
+                q_pos = torch.full((nb,), ctx - 1, dtype=torch.int32, device=dev)
+                ctx_len = torch.full((nb,), ctx, dtype=torch.int32, device=dev)
+                out = torch.empty((nb, h, 64), device=dev)
+                lse = torch.empty((nb, h), device=dev)
+                ws = kpa.alloc_workspace(dims, nb, ctx, device=dev)
+
+                def decode():
+                    kpa.kpa_decode(dims, cache, nb, ctx, ctx_len, ctx, q, q_pos, out, lse, ws)
+
+                for _ in range(3):
+                    decode()
+                reps = 10
+                kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+                cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+                for a, b in kev + cev:
+                    a.record()
+                    b.record()
+                torch.cuda.synchronize()
+                for k in range(reps):
+                    kpa.kpa_time_next_decode_kernel(*kev[k])
+                    cev[k][0].record()
+                    decode()
+                    cev[k][1].record()
+                torch.cuda.synchronize()
+                kern = float(np.median([a.elapsed_time(b) for a, b in kev])) * 1e3
+                call = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
+                tokens = nb * ctx
+                gbs = (tokens * cfg.bytes_per_token) / (kern * 1e-6) / 1e9
+                rows.append((h, nb, ctx, kern, call, tokens / (call * 1e-6), gbs))
+                log(f"h={h} batch={nb} seq={ctx}: kernel {kern:.1f} us, call {call:.1f} us, {gbs:.0f} GB/s")
+                del cache, ws
+                torch.cuda.empty_cache()
+    lines = ["| h | batch | seq | decode kernel us | call (kernel + merge) us | cached tokens/s | kernel GB/s | of 8 TB/s |",
+             "|---|---|---|---|---|---|---|---|"]
+    for h, nb, ctx, kern, call, tps, gbs in rows:
+        lines.append(f"| {h} | {nb} | {ctx} | {kern:.1f} | {call:.1f} | {tps:.3e} | {gbs:.0f} | "
+                     f"{100 * gbs / HBM_PEAK_GBPS:.1f}% |")
+    table = "\n".join(lines)
+    print(table)
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write(table + "\n")
 
 
 def summarize_util(args):

@@ -662,6 +662,10 @@ const MfmaKernel kKernels[] = {
     KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, true, 8, 8, 4, 16, 4, 4, false, 2, 2, 2),
     // TPA split (A: h x 1, B: 1 x d_h): G = A with feature dimension 1, F = B
     KPA_MFMA_ENTRY(12, 1, 1, 64, 2, 2, false, 12, 1, 1, 64, 2, 2, true, 1, 1, 1),
+    // FlashTPA's benchmark shapes: d_h = 64, R_K = R_V = 1, h = 16 / 32 / 48
+    KPA_MFMA_ENTRY(16, 1, 1, 64, 1, 1, false, 16, 1, 1, 64, 1, 1, true, 1, 1, 2),
+    KPA_MFMA_ENTRY(32, 1, 1, 64, 1, 1, false, 32, 1, 1, 64, 1, 1, true, 1, 1, 2),
+    KPA_MFMA_ENTRY(48, 1, 1, 64, 1, 1, false, 48, 1, 1, 64, 1, 1, true, 1, 1, 1),
 };
 #undef KPA_MFMA_ENTRY
 

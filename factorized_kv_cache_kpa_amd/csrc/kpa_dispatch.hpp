@@ -1,6 +1,8 @@
 // Kernel-path selection and split-KV planning (host only).
 #pragma once
 
+#include <algorithm>
+
 #include "kpa_common.hpp"
 
 namespace kpa {
@@ -70,6 +72,13 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
         const int64_t min_tiles_per_chunk = 2;
         const int64_t cap = (tiles + min_tiles_per_chunk - 1) / min_tiles_per_chunk;
         if (s > cap) s = cap;
+        // a second merge level costs a same-address atomic per block (slow
+        // on this part): stay within one level; fewer, longer chunks still
+        // fill the chip
+        const int64_t dh = (int64_t)d.q1 * d.q2;
+        const int64_t vec = dh % 4 == 0 ? 4 : 2;
+        const int64_t one_level = std::min<int64_t>(kMaxSingleLevel, 16 * (1024 / (dh / vec)));
+        if (s > one_level) s = std::max<int64_t>(one_level, kMergeGroup);
     }
     if (s > tiles) s = tiles;
     if (s < 1) s = 1;

@@ -240,3 +240,19 @@ def test_garbage_workspace_and_repeated_calls(gpu_lib, name, batch, ctx):
         go = out.cpu().numpy().astype(np.float64)[:, None]
         gl = lse.cpu().numpy().astype(np.float64)[:, None]
         assert_close(go, gl, ro, rl, cfg.dtype, f"{name} call {call}")
+
+
+@pytest.mark.parametrize("h", [16, 32, 48])
+def test_flashtpa_shapes_match_oracle(gpu_lib, h):
+    """FlashTPA's benchmark shapes (TPA split, d_h = 64, R_K = R_V = 1) on their
+    matrix-core instantiations: ragged contexts over several chunks."""
+    from workloads import flashtpa_config
+    cfg = flashtpa_config(h, 3, 2100)
+    inp = make_inputs(cfg, seed=14, ragged=True)
+    dims = dims_of(cfg)
+    assert kpa.kpa_decode_path(dims, 1) == "mfma_bf16"
+    cache, cap = fill_cache(inp, dims)
+    ro, rl = _oracle(inp)
+    for s in (0, 5):
+        go, gl = run_decode(inp, dims, cache, cap, num_splits=s)
+        assert_close(go, gl, ro, rl, cfg.dtype, f"flashtpa h={h} splits={s}")

@@ -4,7 +4,9 @@ This package holds no step of the attention method: it only names the
 problem shapes and draws random inputs.  Both the HIP path and the CPU oracle
 consume what it returns.
 """
-from .configs import CONFIGS, Config, SWEEP_SHAPES
+from .configs import (CONFIGS, FLASHTPA_BATCHES, FLASHTPA_HEADS, FLASHTPA_SEQS, SWEEP_SHAPES, Config,
+                      flashtpa_config)
 from .gen import Inputs, make_inputs, make_query_factors
 
-__all__ = ["CONFIGS", "Config", "SWEEP_SHAPES", "Inputs", "make_inputs", "make_query_factors"]
+__all__ = ["CONFIGS", "Config", "SWEEP_SHAPES", "FLASHTPA_HEADS", "FLASHTPA_SEQS", "FLASHTPA_BATCHES",
+           "flashtpa_config", "Inputs", "make_inputs", "make_query_factors"]

@@ -89,3 +89,19 @@ SWEEP_SHAPES = [
     (5, 5),                            # 1.5B, h = 25
     (6, 2), (4, 3), (3, 4), (2, 6),    # 125M, h = 12
 ]
+
+
+# FlashTPA decoding benchmark shapes ("Tensor Product Attention Is All You
+# Need", summary page: d_model 1024 / 2048 / 3072, d_h = 64, R_K = R_V = 1,
+# sequence lengths 2^12 .. 2^19, batch 1 .. 16), as TPA's degenerate split of
+# KPA: A_r is h x 1, B_r is 1 x 64.  The pages give no factor distribution;
+# the TPA config's sd 1/8 is used.
+FLASHTPA_HEADS = (16, 32, 48)
+FLASHTPA_SEQS = (1 << 12, 1 << 14, 1 << 16, 1 << 19)
+FLASHTPA_BATCHES = (1, 4, 16)
+
+
+def flashtpa_config(h: int, batch: int, ctx: int) -> Config:
+    return Config(f"flashtpa_h{h}_b{batch}_s{ctx}", h, 1, 1, 64, 1, 1, "bf16", batch=batch, ctx=ctx,
+                  sigma_a=0.125, sigma_b=0.125)
+
