@@ -116,9 +116,14 @@ def _ptr(t, dtype=None, name="tensor"):
     return t.data_ptr()
 
 
-def _stream(stream):
+def _stream(stream, on):
+    """HIP stream handle: the given stream, else the current stream of the
+    device that tensor `on` lives on (read without building a Stream object,
+    which costs microseconds per call)."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        if on is None:
+            return torch.cuda.current_stream().cuda_stream
+        return torch._C._cuda_getCurrentRawStream(on.device.index)
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
@@ -159,7 +164,7 @@ def kpa_cache_append(dims, cache, batch, capacity, a_k, b_k, a_v, b_v, positions
         ctypes.byref(dims), _ptr(cache, torch.uint8, "cache"), batch, capacity,
         _ptr(a_k, dt, "a_k"), _ptr(b_k, dt, "b_k"), _ptr(a_v, dt, "a_v"), _ptr(b_v, dt, "b_v"),
         _ptr(positions, torch.int32, "positions"), _ptr(slot0, torch.int32, "slot0"), int(n_new),
-        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream))
+        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream, cache))
     _check("kpa_cache_append", st)
 
 
@@ -175,7 +180,7 @@ def kpa_decode(dims, cache, batch, capacity, ctx_len, max_ctx, q, q_pos, out, ls
         _ptr(ctx_len, torch.int32, "ctx_len"), max_ctx, _ptr(q, torch.float32, "q"),
         _ptr(q_pos, torch.int32, "q_pos"), _ptr(out, torch.float32, "out"),
         _ptr(lse, torch.float32, "lse"), _ptr(workspace, None, "workspace"), ws_bytes, num_splits,
-        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream))
+        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream, cache))
     _check("kpa_decode", st)
 
 
@@ -188,7 +193,7 @@ def kpa_decode_multiq(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causa
         _ptr(q, torch.float32, "q"), _ptr(q_pos, torch.int32, "q_pos"),
         _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
         _ptr(workspace, None, "workspace"), ws_bytes, num_splits,
-        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream))
+        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream, cache))
     _check("kpa_decode_multiq", st)
 
 
@@ -202,7 +207,7 @@ def kpa_decode_factored(dims, r_q, cache, batch, capacity, ctx_len, max_ctx, n_q
         _ptr(a_q, torch.float32, "a_q"), _ptr(b_q, torch.float32, "b_q"), _ptr(q_pos, torch.int32, "q_pos"),
         _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
         _ptr(workspace, None, "workspace"), ws_bytes, num_splits,
-        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream))
+        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream, cache))
     _check("kpa_decode_factored", st)
 
 
