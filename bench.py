@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--factored-query", type=int, default=0, metavar="R_Q",
                     help="decode with a factored query of rank R_Q (kpa_decode_factored) instead of a dense one")
+    ap.add_argument("--unfused", action="store_true",
+                    help="step as two calls (kpa_cache_append, then the decode) instead of kpa_append_decode")
     ap.add_argument("--call-events", action="store_true",
                     help="also bracket each whole decode call (kernel + merge) with events")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -159,7 +161,18 @@ def main():
             kpa.kpa_decode_multiq(dims, cache, nb, ctx, ctx_len, ctx, n_q, 1, q, q_pos, out, lse, ws,
                                   args.num_splits)
 
+    fused = not args.unfused and args.factored_query == 0
+
     def step(ev=None):
+        if fused:
+            # one call: the matrix-core decode kernel writes the new tokens itself
+            if ev is not None:
+                ev[0].record()
+            kpa.kpa_append_decode(dims, cache, nb, ctx, new_ak, new_bk, new_av, new_bv, new_pos, slot0, ctx_len,
+                                  ctx, n_q, 1, q, q_pos, out, lse, ws, args.num_splits, n_new=n_new)
+            if ev is not None:
+                ev[1].record()
+            return
         kpa.kpa_cache_append(dims, cache, nb, ctx, new_ak, new_bk, new_av, new_bv, new_pos, slot0,
                              n_new=n_new)
         if ev is not None:
@@ -183,19 +196,27 @@ def main():
             e1.record()
         return ev
 
-    # Timed region: the steps, with the decode kernel of each bracketed by a
-    # pair of HIP events on its stream (every event marker costs the stream a
-    # few microseconds, so the whole-call pair is recorded only on request).
-    kern_ev = timing_events(args.steps)   # the split-KV decode kernel alone
-    call_ev = timing_events(args.steps) if args.call_events else None
+    # Timed region: the steps alone.  Nothing else enters the stream: even
+    # the events that a launch stamps with its kernel's start and end cost the
+    # stream time between dispatches.
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    for k in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+
+    # Then the same number of steps again, each with its split-KV decode kernel
+    # bracketed by a pair of HIP events on its stream, for the kernel's own
+    # duration (the whole-call pair only on request).
+    kern_ev = timing_events(args.steps)
+    call_ev = timing_events(args.steps) if args.call_events else None
+    torch.cuda.synchronize()
     for k in range(args.steps):
         kpa.kpa_time_next_decode_kernel(*kern_ev[k])
         step(call_ev[k] if call_ev else None)
     torch.cuda.synchronize()
-    t_end = time.perf_counter()
-    ms_per_step = (t_end - t_start) * 1e3 / args.steps
     kern_ms = np.array([a.elapsed_time(b) for a, b in kern_ev])
     call_ms = np.array([a.elapsed_time(b) for a, b in call_ev]) if call_ev else None
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode kernel {kern_ms.mean() * 1e3:.1f} us "
@@ -217,7 +238,10 @@ def main():
 
     tokens = int(inp.ctx_len.sum().item())  # cached tokens attended per step (per query)
     value = tokens / (ms_per_step / 1e3)
-    roofline = decode_roofline(cfg, tokens, q.numel() * 4 + out.numel() * 4 + lse.numel() * 4,
+    # the fused kernel also reads the step's new factors and writes them (and
+    # their positions) into the cache
+    app_bytes = nb * n_new * (2 * cfg.bytes_per_token + 2 * 4) if fused else 0
+    roofline = decode_roofline(cfg, tokens, q.numel() * 4 + out.numel() * 4 + lse.numel() * 4 + app_bytes,
                                float(kern_ms.mean()), float(call_ms.mean()) if call_ev else None,
                                kpa.kpa_decode_path(dims, n_q))
 
@@ -232,7 +256,8 @@ def main():
         "data": "synthetic (seeded normal factors; no dataset)",
         "config": {"workload": cfg.name, "batch": nb, "ctx": ctx, "n_q": n_q,
                    "split": [cfg.p1, cfg.p2, cfg.q1, cfg.q2], "ranks": [cfg.r_k, cfg.r_v],
-                   "path": kpa.kpa_decode_path(dims, n_q), "step": "append new token(s) + decode",
+                   "path": kpa.kpa_decode_path(dims, n_q), "step": ("append new token(s) + decode, one call (kpa_append_decode)" if fused
+                            else "append new token(s) + decode, two calls"),
                    "query": f"factored, R_Q = {args.factored_query}" if args.factored_query > 0 else "dense",
                    "parallelism": "single GPU"},
         "achieved_hbm_gbps": roofline["hbm_gbps"], "hbm_pct_of_peak": round(100 * roofline["hbm_gbps"] / HBM_PEAK_GBPS, 2),

@@ -87,6 +87,9 @@ def load():
     lib.kpa_decode_factored.argtypes = [DP, I32, P, I32, I32, P, I32, I32, I32, P, P, P, P, P, P,
                                         ctypes.c_size_t, I32, P, P]
     lib.kpa_decode_factored.restype = ctypes.c_int
+    lib.kpa_append_decode.argtypes = [DP, P, I32, I32, P, P, P, P, P, P, I32, P, I32, I32, I32, P, P, P, P, P,
+                                      ctypes.c_size_t, I32, P, P]
+    lib.kpa_append_decode.restype = ctypes.c_int
     lib.kpa_status_string.argtypes = [ctypes.c_int]
     lib.kpa_status_string.restype = ctypes.c_char_p
     lib.kpa_decode_path.argtypes = [DP, I32]
@@ -209,6 +212,27 @@ def kpa_decode_factored(dims, r_q, cache, batch, capacity, ctx_len, max_ctx, n_q
         _ptr(workspace, None, "workspace"), ws_bytes, num_splits,
         _ptr(dev_status, torch.int32, "dev_status"), _stream(stream, cache))
     _check("kpa_decode_factored", st)
+
+
+def kpa_append_decode(dims, cache, batch, capacity, a_k, b_k, a_v, b_v, positions, slot0, ctx_len, max_ctx,
+                      n_q, causal, q, q_pos, out, lse=None, workspace=None, num_splits=0, n_new=None,
+                      dev_status=None, stream=None):
+    """kpa_cache_append of the new tokens, then kpa_decode_multiq, as one call
+    (fused into the decode kernel where the matrix-core path runs)."""
+    dt = dims.torch_dtype
+    if n_new is None:
+        n_new = a_k.shape[1] if a_k is not None and a_k.dim() > 1 else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().kpa_append_decode(
+        ctypes.byref(dims), _ptr(cache, torch.uint8, "cache"), batch, capacity,
+        _ptr(a_k, dt, "a_k"), _ptr(b_k, dt, "b_k"), _ptr(a_v, dt, "a_v"), _ptr(b_v, dt, "b_v"),
+        _ptr(positions, torch.int32, "positions"), _ptr(slot0, torch.int32, "slot0"), int(n_new),
+        _ptr(ctx_len, torch.int32, "ctx_len"), max_ctx, n_q, int(bool(causal)),
+        _ptr(q, torch.float32, "q"), _ptr(q_pos, torch.int32, "q_pos"),
+        _ptr(out, torch.float32, "out"), _ptr(lse, torch.float32, "lse"),
+        _ptr(workspace, None, "workspace"), ws_bytes, num_splits,
+        _ptr(dev_status, torch.int32, "dev_status"), _stream(stream, cache))
+    _check("kpa_append_decode", st)
 
 
 # --------------------------------------------------------------------------

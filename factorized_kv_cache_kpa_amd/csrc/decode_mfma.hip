@@ -40,6 +40,7 @@
 #include <atomic>
 #include <type_traits>
 
+#include "kpa_append.hpp"
 #include "kpa_common.hpp"
 #include "kpa_mfma.hpp"
 
@@ -259,6 +260,17 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     WaveScratch<S>& ws = scratch[wave];
     const Layout& L = P.L;
     const int n0 = qwg * S::QPW + qsub * NQW;  // first query of this wave
+
+    // slot of the first new token of a fused append (single-query kernels),
+    // read now so that its latency overlaps the prologue.  A vector load:
+    // scalar loads complete out of order, so waiting on this one would also
+    // hold up every kernel-argument load issued after it.
+    int app_slot0_v = 0;
+    if (NQW == 1 && P.app.n_new > 0) {
+        int lane_zero = 0;
+        asm volatile("" : "+v"(lane_zero));
+        app_slot0_v = P.app.slot0[b + lane_zero];
+    }
 
     // One query per wave: the first tile goes in flight before the query is
     // prepared (its latency hides the rotation's float64 arithmetic).  Its
@@ -616,6 +628,40 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
         if (first < last) load_f(t0, fa);  // the G blocks are on their way already
     } else {
         if (first < last) issue(t0, gbuf_a, fa);
+    }
+    // Fused append (kpa_append_decode, single-query kernels; the host runs
+    // the append kernel first for the others): each new token is written by
+    // the workgroup of the chunk whose slots hold it (past every chunk: the
+    // last) before it reads it.  The slot0 value arrives behind the first
+    // tile's G blocks (loads complete in order), so workgroups owning no token
+    // wait here for what the tile loop's first wait would wait for anyway.
+    // The owner writes its tokens and waits for the stores, all before the
+    // next tile's loads are issued; for a token in the first tile it fetches
+    // that tile again (the loop's first wait covers it).
+    if (kEarly && P.app.n_new > 0) {
+        // keeps the wait for slot0 (and the loads ahead of it) after the
+        // first tile's loads have been issued
+        asm volatile("" : "+v"(app_slot0_v)::"memory");
+        const int app_slot0 = __builtin_amdgcn_readfirstlane(app_slot0_v);
+        const int span = P.chunk_tiles * kTileSlots;
+        bool owned = false, in_first = false;
+        for (int n = 0; n < P.app.n_new; ++n) {
+            const int j = app_slot0 + n;
+            const int owner = j < 0 ? 0 : min(j / span, P.n_split - 1);
+            if (owner != split) continue;
+            append_token<false>(P.d, L, P.cache_w, P.capacity, P.app, P.dev_status, b, n, threadIdx.x,
+                                S::WAVES * 64);
+            owned = true;
+            if (j >= first && j < first + kTileSlots) in_first = true;
+        }
+        if (owned) {
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's stores are done
+            __syncthreads();                     // ... and every other wave's
+            if (in_first && first < last) {
+                dma_g_blocks<S>(t0 + offGK, t0 + offGV, gbuf_a, wave, lane);
+                load_f(t0, fa);
+            }
+        }
     }
     if constexpr (S::G32_) {
         // One bf16 stage (gbuf_a) and one float32 copy (gbuf_b).  Per tile:

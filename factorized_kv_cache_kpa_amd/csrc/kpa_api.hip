@@ -102,13 +102,7 @@ int kpa_cache_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t c
     P.cache = static_cast<uint8_t*>(cache);
     P.batch = batch;
     P.capacity = capacity;
-    P.n_new = n_new;
-    P.a_k = a_k;
-    P.b_k = b_k;
-    P.a_v = a_v;
-    P.b_v = b_v;
-    P.positions = positions;
-    P.slot0 = slot0;
+    P.in = AppendInputs{a_k, b_k, a_v, b_v, positions, slot0, n_new};
     P.dev_status = dev_status;
     return launch_append(P, static_cast<hipStream_t>(stream)) == hipSuccess ? KPA_OK : KPA_ERR_HIP;
 }
@@ -124,20 +118,25 @@ size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t m
 // decode kernel's start and end (kpa_time_next_decode_kernel).
 static thread_local KernelEvents t_kernel_events;
 
-// factored: the query is (a_q, b_q, r_q); otherwise the dense q.
+// factored: the query is (a_q, b_q, r_q); otherwise the dense q.  app: new
+// tokens to append to the (writable) cache first, or NULL.
 static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch, int32_t capacity,
                          const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal, bool factored,
                          const float* q, const float* a_q, const float* b_q, int32_t r_q,
                          const int32_t* q_pos, float* out, float* lse,
                          void* workspace, size_t workspace_bytes, int32_t num_splits,
-                         uint32_t* dev_status, void* stream) {
+                         uint32_t* dev_status, void* stream, const AppendInputs* app = nullptr) {
     // a pending measurement request applies to this call only
     const KernelEvents ev = t_kernel_events;
     t_kernel_events = KernelEvents{};
     int st = check_decode_args(dims, batch, capacity, max_ctx, n_q);
     if (st != KPA_OK) return st;
     if (factored && (r_q < 1 || r_q > KPA_MAX_RANK)) return KPA_ERR_INVALID_DIMS;
+    if (app && app->n_new < 0) return KPA_ERR_INVALID_ARG;
     if (batch == 0) return KPA_OK;
+    if (app && app->n_new > 0 &&
+        (!app->a_k || !app->b_k || !app->a_v || !app->b_v || !app->positions || !app->slot0))
+        return KPA_ERR_NULL_PTR;
     if (!cache || !ctx_len || !q_pos || !out || (factored ? (!a_q || !b_q) : !q)) return KPA_ERR_NULL_PTR;
     if (!aligned(cache, 16) || !aligned(out, 16) || (!factored && !aligned(q, 16)) ||
         (factored && (!aligned(a_q, 16) || !aligned(b_q, 16))))
@@ -183,6 +182,23 @@ static int decode_common(const kpa_dims* dims, const void* cache, int32_t batch,
     P.q_scale = (float)(1.4426950408889634 / (dims->r_k * sqrt((double)dh)));
     P.v_scale = (float)(1.0 / dims->r_v);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (app && app->n_new > 0) {
+        if (plan.path == Path::kMfmaSq && n_q == 1) {
+            // the single-query matrix-core kernels write the new tokens themselves
+            P.app = *app;
+            P.cache_w = const_cast<uint8_t*>(P.cache);
+        } else {
+            AppendParams A{};
+            A.d = *dims;
+            A.L = P.L;
+            A.cache = const_cast<uint8_t*>(P.cache);
+            A.batch = batch;
+            A.capacity = capacity;
+            A.in = *app;
+            A.dev_status = dev_status;
+            if (launch_append(A, s) != hipSuccess) return KPA_ERR_HIP;
+        }
+    }
     hipError_t e = launch_plan(plan, P, s, ev);
     if (e != hipSuccess) return KPA_ERR_HIP;
     if (plan.n_split > 1 && launch_merge(P, s) != hipSuccess) return KPA_ERR_HIP;
@@ -219,6 +235,18 @@ int kpa_decode_factored(const kpa_dims* dims, int32_t r_q, const void* cache, in
                         uint32_t* dev_status, void* stream) {
     return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causal, true, nullptr, a_q, b_q, r_q,
                          q_pos, out, lse, workspace, workspace_bytes, num_splits, dev_status, stream);
+}
+
+int kpa_append_decode(const kpa_dims* dims, void* cache, int32_t batch, int32_t capacity,
+                      const void* a_k, const void* b_k, const void* a_v, const void* b_v,
+                      const int32_t* positions, const int32_t* slot0, int32_t n_new,
+                      const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
+                      const float* q, const int32_t* q_pos, float* out, float* lse,
+                      void* workspace, size_t workspace_bytes, int32_t num_splits,
+                      uint32_t* dev_status, void* stream) {
+    const AppendInputs app{a_k, b_k, a_v, b_v, positions, slot0, n_new};
+    return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causal, false, q, nullptr, nullptr, 0,
+                         q_pos, out, lse, workspace, workspace_bytes, num_splits, dev_status, stream, &app);
 }
 
 const char* kpa_status_string(int status) {

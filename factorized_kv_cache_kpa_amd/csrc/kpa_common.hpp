@@ -86,14 +86,21 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
 // ---------------------------------------------------------------------------
 // Launch parameters
 // ---------------------------------------------------------------------------
+// New tokens for the cache: token n of sequence b goes to slot slot0[b] + n
+// at position positions[b * n_new + n]; factor tensors [batch][n_new][...].
+struct AppendInputs {
+    const void *a_k, *b_k, *a_v, *b_v;
+    const int32_t* positions;
+    const int32_t* slot0;
+    int32_t n_new;
+};
+
 struct AppendParams {
     kpa_dims d;
     Layout L;
     uint8_t* cache;
-    int32_t batch, capacity, n_new;
-    const void *a_k, *b_k, *a_v, *b_v;
-    const int32_t* positions;
-    const int32_t* slot0;
+    int32_t batch, capacity;
+    AppendInputs in;
     uint32_t* dev_status;
 };
 
@@ -123,6 +130,10 @@ struct DecodeParams {
     uint32_t* merge_count; // [batch][n_q][h] arrival counters of the second level
     float q_scale;        // log2(e) / (R_K sqrt(d_h))
     float v_scale;        // 1 / R_V
+    // fused append (kpa_append_decode): app.n_new > 0 has the workgroups write
+    // the new tokens of their own chunk into cache_w before reading them
+    AppendInputs app;
+    uint8_t* cache_w;
 };
 
 // Element (i, j) of the unrotated query of row (b, n): the dense query's, or,

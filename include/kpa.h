@@ -230,10 +230,34 @@ int kpa_decode_factored(const kpa_dims* dims, int32_t r_q, const void* cache, in
                         uint32_t* dev_status, void* stream);
 
 /*
+ * kpa_append_decode -- one decode step: kpa_cache_append of n_new tokens per
+ * sequence, then kpa_decode_multiq over the updated cache (the pages' decode
+ * step writes the new token's factors to the cache and attends over it:
+ * [KPA] §2.5; [TPA] summary page, "RoPE Compatibility and Acceleration").
+ * Arguments: those of kpa_cache_append (cache writable, a_k .. slot0, n_new
+ * >= 0; n_new = 0 needs none of a_k .. slot0) and of kpa_decode_multiq
+ * (n_q = 1 is the single-query decode).  Results, cache bytes and dev_status
+ * bits equal those of the two calls made in that order on the same stream.
+ * With one query per sequence on the matrix-core kernels the append is fused
+ * into the decode kernel (one launch fewer): each new token is written by
+ * the workgroup whose KV chunk holds its slot, before it reads it; other
+ * paths launch the append kernel first.  Returns as kpa_decode_multiq; KPA_ERR_INVALID_ARG for n_new < 0,
+ * KPA_ERR_NULL_PTR for a missing append input when n_new > 0 and batch > 0.
+ */
+int kpa_append_decode(const kpa_dims* dims, void* cache, int32_t batch, int32_t capacity,
+                      const void* a_k, const void* b_k, const void* a_v, const void* b_v,
+                      const int32_t* positions, const int32_t* slot0, int32_t n_new,
+                      const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
+                      const float* q, const int32_t* q_pos, float* out, float* lse,
+                      void* workspace, size_t workspace_bytes, int32_t num_splits,
+                      uint32_t* dev_status, void* stream);
+
+/*
  * kpa_time_next_decode_kernel -- measurement hook.  start_event and
  * stop_event are hipEvent_t handles created by the caller with timing
  * enabled (both non-NULL), or both NULL to cancel a pending request.  The
- * next kpa_decode / kpa_decode_multiq call made on the same host thread
+ * next decode call (kpa_decode, kpa_decode_multiq, kpa_decode_factored,
+ * kpa_append_decode) made on the same host thread
  * launches its split-KV decode kernel with hipExtLaunchKernel so that the
  * runtime stamps start_event and stop_event with that kernel's own start and
  * end on its stream (the log-sum-exp merge is not included, and no extra

@@ -122,6 +122,22 @@ def test_null_and_range_errors_return_before_launch():
     assert fq(d, 2, FAKE, 1, 64, FAKE, 64, 1, 0, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -2
     assert fq(d, 2, FAKE, 1, 64, FAKE, 64, 1, 0, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -2
     assert fq(d, 2, None, 0, 64, None, 64, 1, 0, None, None, None, None, None, None, 0, 0, None, None) == 0
+    # append + decode: the append arguments are checked first, then the decode's
+    ad = lib.kpa_append_decode
+    big = 1 << 30
+    assert ad(d, FAKE, 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 64, 1, 0, FAKE, FAKE, FAKE, None,
+              FAKE, big, 0, None, None) == -7
+    assert ad(d, FAKE, 1, 64, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, 64, 1, 0, FAKE, FAKE, FAKE, None,
+              FAKE, big, 0, None, None) == -2
+    assert ad(d, FAKE, 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, FAKE, 64, 1, 0, FAKE, FAKE, FAKE, None,
+              FAKE, big, 0, None, None) == -2
+    # n_new = 0 needs no append input; the decode's own checks still apply
+    assert ad(d, None, 1, 64, None, None, None, None, None, None, 0, FAKE, 64, 1, 0, FAKE, FAKE, FAKE, None,
+              FAKE, big, 0, None, None) == -2
+    assert ad(d, FAKE, 1, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, 65, 1, 0, FAKE, FAKE, FAKE, None,
+              FAKE, big, 0, None, None) == -7
+    assert ad(d, None, 0, 64, None, None, None, None, None, None, 1, None, 64, 1, 0, None, None, None, None,
+              None, 0, 0, None, None) == 0
 
 
 def test_workspace_sizes_follow_the_split_count():
