@@ -56,6 +56,11 @@ def parse():
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--factored-query", type=int, default=0, metavar="R_Q",
                     help="decode with a factored query of rank R_Q (kpa_decode_factored) instead of a dense one")
+    ap.add_argument("--prewarm-s", type=float, default=0.3,
+                    help="seconds of untimed steps before the warm-up steps, so that the clocks reach their "
+                         "steady state (a compute-bound step runs ~15%% slower in the first ~50 ms)")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="time the decode kernel of every N-th timed step with HIP events")
     ap.add_argument("--unfused", action="store_true",
                     help="step as two calls (kpa_cache_append, then the decode) instead of kpa_append_decode")
     ap.add_argument("--call-events", action="store_true",
@@ -181,6 +186,16 @@ def main():
         if ev is not None:
             ev[1].record()
 
+    # untimed steps until the clocks settle, then the warm-up steps proper
+    t_pre = time.perf_counter()
+    n_pre = 0
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        for _ in range(10):
+            step()
+        n_pre += 10
+        torch.cuda.synchronize()
+    if n_pre:
+        log(f"pre-warm: {n_pre} steps in {time.perf_counter() - t_pre:.2f} s")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -196,30 +211,32 @@ def main():
             e1.record()
         return ev
 
-    # Timed region: the steps alone.  Nothing else enters the stream: even
-    # the events that a launch stamps with its kernel's start and end cost the
-    # stream time between dispatches.
+    # Timed region: K steps.  Every event_every-th step's split-KV decode
+    # kernel is bracketed by a pair of HIP events on its stream, stamped by
+    # the launch itself with the kernel's own start and end (the whole-call
+    # pair only on request).  Not every step: even these events cost the
+    # stream time between dispatches (~10 us a step on kpa_32k, measured).
+    every = max(1, args.event_every)
+    sampled = list(range(every - 1, args.steps, every)) or [args.steps - 1]
+    kern_ev = dict(zip(sampled, timing_events(len(sampled))))
+    call_ev = dict(zip(sampled, timing_events(len(sampled)))) if args.call_events else None
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for k in range(args.steps):
-        step()
+        if k in kern_ev:
+            kpa.kpa_time_next_decode_kernel(*kern_ev[k])
+            step(call_ev[k] if call_ev else None)
+        else:
+            step()
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
-
-    # Then the same number of steps again, each with its split-KV decode kernel
-    # bracketed by a pair of HIP events on its stream, for the kernel's own
-    # duration (the whole-call pair only on request).
-    kern_ev = timing_events(args.steps)
-    call_ev = timing_events(args.steps) if args.call_events else None
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        kpa.kpa_time_next_decode_kernel(*kern_ev[k])
-        step(call_ev[k] if call_ev else None)
-    torch.cuda.synchronize()
+    kern_ev = list(kern_ev.values())
+    call_ev = list(call_ev.values()) if call_ev else None
     kern_ms = np.array([a.elapsed_time(b) for a, b in kern_ev])
     call_ms = np.array([a.elapsed_time(b) for a, b in call_ev]) if call_ev else None
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, decode kernel {kern_ms.mean() * 1e3:.1f} us "
+        f"over {len(kern_ms)} sampled steps "
         f"(median {np.median(kern_ms) * 1e3:.1f})"
         + (f", decode call {call_ms.mean() * 1e3:.1f} us" if call_ev else ""))
 
@@ -262,6 +279,7 @@ def main():
                    "parallelism": "single GPU"},
         "achieved_hbm_gbps": roofline["hbm_gbps"], "hbm_pct_of_peak": round(100 * roofline["hbm_gbps"] / HBM_PEAK_GBPS, 2),
         "roofline": roofline, "cpu_baseline": cpu,
+        "event_every": max(1, args.event_every), "prewarm_s": args.prewarm_s,
     }
     line = json.dumps(res)
     print(line, flush=True)
@@ -386,16 +404,30 @@ def summarize_trace(args):
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
     rf = res["roofline"]
     dec = [r for r in rows if "decode_" in r["Name"] and "_kernel" in r["Name"]]
-    lines += ["", "Same run, bench.py's own figures (HIP events on the launch stream, timed steps only):", "",
+    lines += ["", "Same run, bench.py's own figures (HIP events on the launch stream, every "
+                  f"{res.get('event_every', 1)}-th timed step):", "",
               f"- decode kernel average: {rf['launch_us']} us"]
     if "call_us" in rf:
         lines.append(f"- decode call (kernel + merge) average: {rf['call_us']} us")
     lines += [f"- ms per step: {res['ms_per_step']}",
               f"- roofline: {rf['achieved']} {rf['unit']} of {rf['peak']} ({100 * rf['frac']:.1f}%), bound {rf['bound']}"]
     avg = float(dec[0]["AverageNs"]) / 1e3 if dec else None
+    # the last K decode dispatches are the timed steps; every event_every-th carried events
+    k = int(res["steps"])
+    every = int(res.get("event_every", 1))
+    trace = [r for r in _read_csv(_find(args.summarize_trace, "kernel_trace.csv"))
+             if "decode_" in r["Kernel_Name"] and "_kernel" in r["Kernel_Name"]]
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in trace]
+    if len(durs) >= k:
+        timed = durs[-k:]
+        sampled = [timed[i] for i in range(every - 1, k, every)] or [timed[-1]]
+        s_avg = sum(sampled) / len(sampled)
+        lines.append(f"- rocprofv3, the {len(sampled)} dispatches the events timed: average {s_avg:.1f} us "
+                     f"({100 * (rf['launch_us'] - s_avg) / s_avg:+.1f}% for the events)")
+        lines.append(f"- rocprofv3, all {k} timed steps: decode kernel average {sum(timed) / k:.1f} us")
     if avg:
-        lines.append(f"- rocprofv3 decode kernel average: {avg:.1f} us "
-                     f"({100 * (rf['launch_us'] - avg) / avg:+.1f}% for the events under the profiler)")
+        lines.append(f"- rocprofv3 decode kernel average over every dispatch of the run: {avg:.1f} us")
     if args.plain_json:
         with open(args.plain_json) as f:
             plain = json.loads(f.read().strip().splitlines()[-1])
