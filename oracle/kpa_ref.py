@@ -19,7 +19,11 @@ Readings of points the pages leave open (each is listed in the design doc):
     (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos);
   * the score is scaled by 1/sqrt(d_h), d_h = d1*d2 ([KPA] §2.3);
   * V is never rotated ([KPA] Fig. 1 caption);
-  * an empty context gives output 0 and log-sum-exp -inf.
+  * an empty context gives output 0 and log-sum-exp -inf;
+  * the factor projection ([KPA] Eq. (5)) takes one stacked weight matrix,
+    rows W^{B^K}, W^{A^K}, W^{A^V}, W^{B^V} (the pages merge the ranks of each
+    factor type; stacking the four types is this build's choice), and each
+    product block is reshaped row-major to [R][p][q].
 """
 from __future__ import annotations
 
@@ -38,6 +42,9 @@ __all__ = [
     "attention_one_query",
     "decode",
     "factored_score",
+    "project_factors",
+    "round_bf16",
+    "projected_cache_values",
 ]
 
 
@@ -244,3 +251,60 @@ def factored_score(a_q, b_q, a_k, b_k, i1: int, i2: int) -> float:
             feature_level = float(np.dot(b_q[r, i2], b_k[rp, i2]))
             total += head_level * feature_level
     return total / (a_q.shape[0] * a_k.shape[0])
+
+
+# ---------------------------------------------------------------------------
+# Factor projection from hidden states ([KPA] Eq. (5) and the merged form
+# after it)
+# ---------------------------------------------------------------------------
+def project_factors(x, w, r_k: int, r_v: int, p1: int, q1: int, p2: int, q2: int):
+    """The four factor sets of tokens x from one merged weight matrix.
+
+    [KPA] Eq. (5): A^K_r(x) = W^{A^K}_r x, B^K_r(x) = W^{B^K}_r x, W^{A^K}_r of
+    shape (h1 d1) x d_model; the ranks are merged into one matrix per factor
+    type, (R_K h1 d1) x d_model, whose product is reshaped to R_K x h1 x d1
+    (read: row-major, row r h1 d1 + i1 d1 + j1 -> [r][i1][j1]).  Here the four
+    merged matrices are stacked into one w of F rows in the order
+    W^{B^K}, W^{A^K}, W^{A^V}, W^{B^V}.
+
+    x: [..., d_model]; w: [F][d_model].  Returns (a_k, b_k, a_v, b_v), float64,
+    shapes [..., R][p][q], unrotated.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    sizes = [r_k * p2 * q2, r_k * p1 * q1, r_v * p1 * q1, r_v * p2 * q2]
+    if w.shape[0] != sum(sizes) or w.shape[1] != x.shape[-1]:
+        raise ValueError("w must be F x d_model with F = (R_K + R_V)(p1 q1 + p2 q2)")
+    y = x @ w.T  # [..., F]
+    lead = x.shape[:-1]
+    parts = []
+    o = 0
+    for n in sizes:
+        parts.append(y[..., o:o + n])
+        o += n
+    b_k = parts[0].reshape(*lead, r_k, p2, q2)
+    a_k = parts[1].reshape(*lead, r_k, p1, q1)
+    a_v = parts[2].reshape(*lead, r_v, p1, q1)
+    b_v = parts[3].reshape(*lead, r_v, p2, q2)
+    return a_k, b_k, a_v, b_v
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 (8 significant bits, ties
+    to even), returned as float64.  Finite normal range only."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)  # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+
+
+def projected_cache_values(x, w, positions, r_k: int, r_v: int, p1: int, q1: int, p2: int, q2: int,
+                           base: float = 10000.0):
+    """What the cache holds for tokens x after projection and append, before
+    the final rounding to the cache type: A^K, A^V, B^V as projected, and
+    B~^K = R^(2)(pos) B^K ([KPA] Thm. 2.4, Eq. (8)), all float64.
+
+    x: [T][d_model], positions: [T].  Returns (a_k, b_k_rotated, a_v, b_v).
+    """
+    a_k, b_k, a_v, b_v = project_factors(x, w, r_k, r_v, p1, q1, p2, q2)
+    b_rot = np.stack([append_rotate(b_k[t], float(positions[t]), base) for t in range(b_k.shape[0])])
+    return a_k, b_rot, a_v, b_v

@@ -75,6 +75,17 @@ def _query_factors_swapped(a_q, b_q):
     return out
 
 
+_orig_project_factors = ref.project_factors
+
+
+def _project_sets_swapped(x, w, r_k, r_v, p1, q1, p2, q2):
+    # the W^{A^K} and W^{B^K} blocks read in the other order
+    n_b, n_a = r_k * p2 * q2, r_k * p1 * q1
+    w = np.asarray(w, np.float64)
+    w2 = np.concatenate([w[n_b:n_b + n_a], w[:n_b], w[n_b + n_a:]]) if n_a == n_b else w[::-1]
+    return _orig_project_factors(x, w2, r_k, r_v, p1, q1, p2, q2)
+
+
 MUTATIONS = [
     ("kron_reconstruct", _kron_swapped, [pins.test_kron_entry_index_convention]),
     ("kron_reconstruct", _kron_no_norm, [pins.test_kron_sum_is_normalised_by_rank,
@@ -87,6 +98,8 @@ MUTATIONS = [
     ("decode", _decode_causal_off_by_one, [pins.test_causal_first_query_sees_only_its_own_token]),
     ("query_from_factors", _query_factors_swapped, [pins.test_query_from_factors_matches_element_formula,
                                                     pins.test_factored_query_decode_equals_attention_from_factored_scores]),
+    ("project_factors", _project_sets_swapped,
+     [pins.test_projection_of_unit_vectors_reads_weight_columns_in_the_stated_order]),
 ]
 
 

@@ -366,3 +366,80 @@ def test_factored_query_decode_equals_attention_from_factored_scores():
                 want = (w[:, None] * v).sum(0) / w.sum()
                 assert np.allclose(got[0, n, i1 * p2 + i2], want, atol=1e-12, rtol=1e-12)
                 assert abs(got_lse[0, n, i1 * p2 + i2] - (z.max() + math.log(w.sum()))) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Factor projection from hidden states ([KPA] Eq. (5), the merged form after it)
+# ---------------------------------------------------------------------------
+PROJ = dict(r_k=2, r_v=3, p1=2, q1=3, p2=4, q2=2)
+
+
+def _proj_sizes(r_k, r_v, p1, q1, p2, q2):
+    return [("b_k", r_k, p2, q2), ("a_k", r_k, p1, q1), ("a_v", r_v, p1, q1), ("b_v", r_v, p2, q2)]
+
+
+def test_projection_of_unit_vectors_reads_weight_columns_in_the_stated_order():
+    """x = e_c returns column c of w: rows in the order W^{B^K}, W^{A^K},
+    W^{A^V}, W^{B^V}, each block read row-major as [R][p][q]."""
+    rng = np.random.default_rng(31)
+    sizes = _proj_sizes(**PROJ)
+    n_rows = sum(r * p * q for _, r, p, q in sizes)
+    d_model = 5
+    w = rng.normal(size=(n_rows, d_model))
+    for c in range(d_model):
+        x = np.zeros(d_model)
+        x[c] = 1.0
+        got = dict(zip(("a_k", "b_k", "a_v", "b_v"), ref.project_factors(x, w, **PROJ)))
+        row = 0
+        for name, r_n, p, q in sizes:
+            for r in range(r_n):
+                for i in range(p):
+                    for j in range(q):
+                        assert got[name][r, i, j] == w[row, c], (name, r, i, j)
+                        row += 1
+
+
+def test_projection_is_linear_and_keys_are_quadratic_in_the_hidden_state():
+    """Each factor is a linear map of x (Eq. (5)), so K_t = (1/R) sum A_r(x) (x) B_r(x)
+    scales with the square of x and the factors add."""
+    rng = np.random.default_rng(32)
+    sizes = _proj_sizes(**PROJ)
+    n_rows = sum(r * p * q for _, r, p, q in sizes)
+    w = rng.normal(size=(n_rows, 7))
+    x1, x2 = rng.normal(size=7), rng.normal(size=7)
+    f1, f2 = ref.project_factors(x1, w, **PROJ), ref.project_factors(x2, w, **PROJ)
+    f12 = ref.project_factors(x1 + 2.5 * x2, w, **PROJ)
+    for a, b, c in zip(f1, f2, f12):
+        assert np.allclose(c, a + 2.5 * b, atol=1e-12)
+    a_k, b_k, _, _ = f1
+    a_k3, b_k3, _, _ = ref.project_factors(3.0 * x1, w, **PROJ)
+    assert np.allclose(ref.kron_reconstruct(a_k3, b_k3), 9.0 * ref.kron_reconstruct(a_k, b_k), atol=1e-10)
+
+
+def test_round_bf16_matches_torch_and_ties_to_even():
+    rng = np.random.default_rng(33)
+    v = rng.normal(size=4000).astype(np.float32) * np.float32(3.0)  # float32-exact inputs
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ref.round_bf16(v.astype(np.float64)), want)
+    # halfway cases: 1 + 2^-8 -> 1 (even), 1 + 3 * 2^-8 -> 1 + 2^-6 (even)
+    assert ref.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert ref.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    assert ref.round_bf16(np.array([-(1.0 + 3 * 2.0 ** -8)]))[0] == -(1.0 + 2.0 ** -6)
+
+
+def test_projected_cache_values_rotate_only_the_key_b_factor():
+    rng = np.random.default_rng(34)
+    sizes = _proj_sizes(**PROJ)
+    n_rows = sum(r * p * q for _, r, p, q in sizes)
+    w = rng.normal(size=(n_rows, 6))
+    x = rng.normal(size=(3, 6))
+    pos = np.array([0, 5, 1000])
+    a_k, b_k, a_v, b_v = ref.project_factors(x, w, **PROJ)
+    ca_k, cb_k, ca_v, cb_v = ref.projected_cache_values(x, w, pos, **PROJ)
+    assert np.array_equal(ca_k, a_k) and np.array_equal(ca_v, a_v) and np.array_equal(cb_v, b_v)
+    assert np.allclose(cb_k[0], b_k[0], atol=1e-15)  # position 0: no rotation
+    for t in range(3):
+        # each rotated row keeps its norm per rotation pair
+        n0 = (b_k[t].reshape(-1, 2) ** 2).sum(-1)
+        n1 = (cb_k[t].reshape(-1, 2) ** 2).sum(-1)
+        assert np.allclose(n0, n1, atol=1e-12)
