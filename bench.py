@@ -72,7 +72,7 @@ def parse():
     ap.add_argument("--plain-json", default=None, help="JSON line of the same command run without the profiler")
     ap.add_argument("--summarize-pmc", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--copy-mib", type=int, default=256)
-    ap.add_argument("--sweep", choices=["flashtpa"], default=None,
+    ap.add_argument("--sweep", choices=["flashtpa", "project"], default=None,
                     help="time the decode over FlashTPA's benchmark shapes instead of one workload")
     ap.add_argument("--sweep-out", default=None, help="write the sweep table (markdown) here")
     ap.add_argument("--summarize-util", default=None, metavar="PMC_DIR",
@@ -89,11 +89,13 @@ def main():
         return summarize_pmc(args)
     if args.summarize_util:
         return summarize_util(args)
+    if args.sweep == "project":
+        return sweep_project(args)
     if args.sweep:
         return sweep_flashtpa(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the decode shards by sequence with no communication; see DESIGN.md)", file=sys.stderr)
+              "(the decode would shard by sequence, with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -499,6 +501,96 @@ def summarize_pmc(args):
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
+
+
+def sweep_project(args):
+    """kpa_project_append (factor projection of hidden states into the cache,
+    one GEMM on the matrix cores) for every bf16 configuration, d_model =
+    h * d_h, at the decode step's token count and at 4096 and 32768 tokens.
+    Weights and hidden states are seeded bf16 normals drawn on the GPU (parity
+    is tested at these shapes in tests/test_gpu_project.py).  Kernel time from
+    HIP events stamped by the launch (median of 10); the HBM roofline counts
+    x, W, the factors written and the positions once; the matrix-core
+    roofline counts 2 * tokens * d_model * F flop.  The CPU column is the
+    float64 oracle projection (NumPy, x @ W^T plus the B^K rotation) timed on
+    a sample of at most 256 tokens."""
+    import numpy as np
+    import torch
+
+    import factorized_kv_cache_kpa_amd as kpa
+    from workloads import CONFIGS
+
+    kpa.load()
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(0)
+    rows = []
+    for name in ("tpa_degenerate", "kpa_32k", "long_512k", "multiq_16"):
+        cfg = CONFIGS[name]
+        dims = kpa.make_dims(cfg.p1, cfg.p2, cfg.q1, cfg.q2, cfg.r_k, cfg.r_v, dtype=cfg.dtype,
+                             rope_base=cfg.rope_base)
+        d_model = cfg.h * cfg.d_h
+        n_feat = (cfg.r_k + cfg.r_v) * (cfg.p1 * cfg.q1 + cfg.p2 * cfg.q2)
+        w = (torch.randn((n_feat, d_model), generator=g, device=dev) / d_model ** 0.5).to(torch.bfloat16)
+        for nb, n_new in ((cfg.batch, cfg.n_q), (1, 4096), (1, 32768)):
+            m = nb * n_new
+            cap = n_new
+            x = torch.randn((nb, n_new, d_model), generator=g, device=dev).to(torch.bfloat16)
+            pos = torch.arange(n_new, dtype=torch.int32, device=dev).repeat(nb, 1).contiguous()
+            slot0 = torch.zeros(nb, dtype=torch.int32, device=dev)
+            cache = kpa.alloc_cache(dims, nb, cap, device=dev)
+
+            def call():
+                kpa.kpa_project_append(dims, cache, nb, cap, x, w, pos, slot0, n_new=n_new)
+
+            for _ in range(3):
+                call()
+            reps = 10
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in ev:
+                a.record()
+                b.record()
+            torch.cuda.synchronize()
+            for a, b in ev:
+                kpa.kpa_time_next_decode_kernel(a, b)
+                call()
+            torch.cuda.synchronize()
+            kern = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+            nbytes = m * d_model * 2 + n_feat * d_model * 2 + m * n_feat * 2 + m * 4
+            gbs = nbytes / (kern * 1e-6) / 1e9
+            tfl = 2.0 * m * d_model * n_feat / (kern * 1e-6) / 1e12
+            cpu_tps = cpu_baseline_project(cfg, x.reshape(m, d_model), w, pos.reshape(-1))
+            rows.append((name, d_model, n_feat, m, kern, gbs, tfl, m / (kern * 1e-6), cpu_tps))
+            log(f"{name} d_model={d_model} F={n_feat} tokens={m}: {kern:.1f} us, {gbs:.0f} GB/s, {tfl:.1f} TFLOP/s")
+            del cache, x
+            torch.cuda.empty_cache()
+    lines = ["| config | d_model | F | tokens | kernel us | GB/s | of 8 TB/s | TFLOP/s | of 2.5 PFLOP/s | "
+             "tokens/s | CPU oracle tokens/s |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name, d_model, n_feat, m, kern, gbs, tfl, tps, cpu in rows:
+        lines.append(f"| {name} | {d_model} | {n_feat} | {m} | {kern:.1f} | {gbs:.0f} | {100 * gbs / HBM_PEAK_GBPS:.1f}% "
+                     f"| {tfl:.1f} | {100 * tfl / 2500.0:.2f}% | {tps:.3e} | {cpu:.3e} |")
+    table = "\n".join(lines)
+    print(table)
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write(table + "\n")
+
+
+def cpu_baseline_project(cfg, x, w, positions, max_tokens=256):
+    """CPU baseline of the projection: the float64 oracle (NumPy x @ W^T, then
+    the B^K rotation) on the first max_tokens tokens; tokens per second."""
+    import numpy as np
+    import torch
+
+    from oracle import kpa_ref
+
+    ms = min(x.shape[0], max_tokens)
+    xs = x[:ms].to(torch.float64).cpu().numpy()
+    wsd = w.to(torch.float64).cpu().numpy()
+    ps = positions[:ms].cpu().numpy()
+    t0 = time.perf_counter()
+    kpa_ref.projected_cache_values(xs, wsd, ps, cfg.r_k, cfg.r_v, cfg.p1, cfg.q1, cfg.p2, cfg.q2, cfg.rope_base)
+    return ms / (time.perf_counter() - t0)
 
 
 def sweep_flashtpa(args):

@@ -87,6 +87,8 @@ def load():
     lib.kpa_decode_factored.argtypes = [DP, I32, P, I32, I32, P, I32, I32, I32, P, P, P, P, P, P,
                                         ctypes.c_size_t, I32, P, P]
     lib.kpa_decode_factored.restype = ctypes.c_int
+    lib.kpa_project_append.argtypes = [DP, P, I32, I32, P, I32, P, P, P, I32, P, P]
+    lib.kpa_project_append.restype = ctypes.c_int
     lib.kpa_append_decode.argtypes = [DP, P, I32, I32, P, P, P, P, P, P, I32, P, I32, I32, I32, P, P, P, P, P,
                                       ctypes.c_size_t, I32, P, P]
     lib.kpa_append_decode.restype = ctypes.c_int
@@ -169,6 +171,19 @@ def kpa_cache_append(dims, cache, batch, capacity, a_k, b_k, a_v, b_v, positions
         _ptr(positions, torch.int32, "positions"), _ptr(slot0, torch.int32, "slot0"), int(n_new),
         _ptr(dev_status, torch.int32, "dev_status"), _stream(stream, cache))
     _check("kpa_cache_append", st)
+
+
+def kpa_project_append(dims, cache, batch, capacity, x, w, positions, slot0, n_new=None, dev_status=None,
+                       stream=None):
+    """x [batch][n_new][d_model] bf16, w [F][d_model] bf16 (rows B^K, A^K, A^V, B^V)."""
+    if n_new is None:
+        n_new = x.shape[1] if x.dim() > 2 else 0
+    st = load().kpa_project_append(
+        ctypes.byref(dims), _ptr(cache, torch.uint8, "cache"), batch, capacity, _ptr(x, torch.bfloat16, "x"),
+        int(x.shape[-1]), _ptr(w, torch.bfloat16, "w"), _ptr(positions, torch.int32, "positions"),
+        _ptr(slot0, torch.int32, "slot0"), int(n_new), _ptr(dev_status, torch.int32, "dev_status"),
+        _stream(stream, cache))
+    _check("kpa_project_append", st)
 
 
 def kpa_decode_workspace_bytes(dims, batch, max_ctx, n_q=1, num_splits=0) -> int:

@@ -107,6 +107,42 @@ int kpa_cache_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t c
     return launch_append(P, static_cast<hipStream_t>(stream)) == hipSuccess ? KPA_OK : KPA_ERR_HIP;
 }
 
+// Events the next decode or projection call on this thread has stamped with
+// its main kernel's start and end (kpa_time_next_decode_kernel).
+static thread_local KernelEvents t_kernel_events;
+
+int kpa_project_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t capacity, const void* x,
+                       int32_t d_model, const void* w, const int32_t* positions, const int32_t* slot0,
+                       int32_t n_new, uint32_t* dev_status, void* stream) {
+    // a pending measurement request applies to this call only
+    const KernelEvents ev = t_kernel_events;
+    t_kernel_events = KernelEvents{};
+    int st = check_dims(dims);
+    if (st != KPA_OK) return st;
+    if (batch < 0 || capacity < 0 || n_new < 0 || batch > 65535) return KPA_ERR_INVALID_ARG;
+    if (d_model <= 0 || d_model % 64 != 0 || d_model > (1 << 20)) return KPA_ERR_INVALID_ARG;
+    if (batch == 0 || n_new == 0) return KPA_OK;
+    const int64_t n_tok = (int64_t)batch * n_new;
+    if (n_tok > 65535LL * 32) return KPA_ERR_INVALID_ARG;
+    if (!cache || !x || !w || !positions || !slot0) return KPA_ERR_NULL_PTR;
+    if (!aligned(cache, 16) || !aligned(x, 16) || !aligned(w, 16)) return KPA_ERR_INVALID_ARG;
+    ProjectParams P{};
+    P.d = *dims;
+    P.L = make_layout(*dims, batch, capacity);
+    P.cache = static_cast<uint8_t*>(cache);
+    P.capacity = capacity;
+    P.n_new = n_new;
+    P.n_tok = (int32_t)n_tok;
+    P.n_feat = P.L.elems[0] + P.L.elems[1] + P.L.elems[2] + P.L.elems[3];
+    P.d_model = d_model;
+    P.x = static_cast<const uint16_t*>(x);
+    P.w = static_cast<const uint16_t*>(w);
+    P.positions = positions;
+    P.slot0 = slot0;
+    P.dev_status = dev_status;
+    return launch_project_append(P, static_cast<hipStream_t>(stream), ev) == hipSuccess ? KPA_OK : KPA_ERR_HIP;
+}
+
 size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t max_ctx, int32_t n_q,
                                   int32_t num_splits) {
     if (check_decode_args(dims, batch, max_ctx, max_ctx, n_q) != KPA_OK) return 0;
@@ -114,9 +150,6 @@ size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t m
     return plan.workspace_bytes;
 }
 
-// Events the next decode call on this thread has stamped with its split-KV
-// decode kernel's start and end (kpa_time_next_decode_kernel).
-static thread_local KernelEvents t_kernel_events;
 
 // factored: the query is (a_q, b_q, r_q); otherwise the dense q.  app: new
 // tokens to append to the (writable) cache first, or NULL.

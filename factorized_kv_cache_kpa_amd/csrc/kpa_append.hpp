@@ -20,6 +20,17 @@ namespace kpa {
 template <typename T>
 __device__ __forceinline__ void store_elem(uint8_t* p, T v) { *reinterpret_cast<T*>(p) = v; }
 
+// One RoPE pair of a B^K row, in float64: (x0, x1) at features (2m, 2m+1)
+// turned by pos * theta_m, theta_m = base^(-2m/q2).
+__device__ __forceinline__ void rope_pair(double x0, double x1, int pos, int m, int q2, double log2_base,
+                                          double& y0, double& y1) {
+    const double theta = exp2(-(2.0 * m / q2) * log2_base);
+    double sn, cs;
+    sincos((double)pos * theta, &sn, &cs);
+    y0 = x0 * cs - x1 * sn;
+    y1 = x0 * sn + x1 * cs;
+}
+
 // Slot of token n of sequence b (may be out of range; the writer checks).
 __device__ __forceinline__ int append_slot(const AppendInputs& in, int b, int n) { return in.slot0[b] + n; }
 
@@ -74,11 +85,8 @@ __device__ void append_token(const kpa_dims& d, const Layout& L, uint8_t* cache,
             x0 = bf16_to_f32(bk[e0]);
             x1 = bf16_to_f32(bk[e0 + 1]);
         }
-        const double theta = exp2(-(2.0 * m / q2) * log2_base);
-        double sn, cs;
-        sincos((double)pos * theta, &sn, &cs);
-        const double y0 = x0 * cs - x1 * sn;
-        const double y1 = x0 * sn + x1 * cs;
+        double y0, y1;
+        rope_pair(x0, x1, pos, m, q2, log2_base, y0, y1);
         if constexpr (kF32) {
             store_elem<float>(tile_base + elem_offset(L, 1, e0, t), (float)y0);
             store_elem<float>(tile_base + elem_offset(L, 1, e0 + 1, t), (float)y1);

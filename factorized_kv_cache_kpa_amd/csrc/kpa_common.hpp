@@ -104,6 +104,20 @@ struct AppendParams {
     uint32_t* dev_status;
 };
 
+// kpa_project_append: hidden states x [n_tok][d_model] and the stacked
+// weight w [n_feat][d_model] (rows B^K, A^K, A^V, B^V), bf16.
+struct ProjectParams {
+    kpa_dims d;
+    Layout L;
+    uint8_t* cache;
+    int32_t capacity, n_new, n_tok, n_feat, d_model;
+    const uint16_t* x;
+    const uint16_t* w;
+    const int32_t* positions;
+    const int32_t* slot0;
+    uint32_t* dev_status;
+};
+
 struct DecodeParams {
     kpa_dims d;
     Layout L;
@@ -182,6 +196,7 @@ struct KernelEvents {
 
 // Launchers (one per translation unit).
 hipError_t launch_append(const AppendParams& P, hipStream_t s);
+hipError_t launch_project_append(const ProjectParams& P, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_merge(const DecodeParams& P, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);

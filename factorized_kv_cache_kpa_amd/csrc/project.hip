@@ -1,0 +1,178 @@
+// kpa_project_append kernel: the factor projection of new tokens' hidden
+// states as one GEMM on the matrix cores, its epilogue writing the factors
+// straight into the tiled cache.
+//
+// [KPA] "Kronecker Product Attention: Memory-Efficient KV Compression via
+//       Structured Factorization", Eq. (5) and the text after it: every
+//       factor is a linear map of the token's hidden state, the ranks of a
+//       factor type merged into one weight matrix whose product is reshaped to
+//       [R][p][q].  Here the four merged matrices are stacked into one weight
+//       (rows B^K, A^K, A^V, B^V), so one GEMM yields every factor of a token.
+//       The cache then receives what kpa_cache_append would store (Thm. 2.4,
+//       §2.5: only B^K rotated), except that B^K is rotated from the float32
+//       products and every value is rounded once, to the cache type.
+//
+// Out[f][t] = sum_c W[f][c] x[t][c]: M = factor rows (f), N = tokens (t),
+// K = d_model, bf16 operands with float32 accumulation
+// (v_mfma_f32_32x32x16_bf16).  One workgroup per 32 rows x 32 tokens; its NW
+// waves (4, 8 or 16: as many as d_model allows, so that more loads of the
+// weight are in flight) split d_model NW ways and add their partial tiles
+// through LDS.  In
+// the accumulator layout a lane holds one token and, for register r, row
+// 8 (r / 4) + 4 (lane / 32) + r % 4: the two features of a RoPE pair (even,
+// odd) sit in neighbouring registers of one lane.
+#include "kpa_append.hpp"
+#include "kpa_common.hpp"
+#include "kpa_mfma.hpp"
+
+namespace kpa {
+namespace {
+
+template <bool kF32, int NW>
+__global__ void __launch_bounds__(NW * 64) project_append_kernel(ProjectParams P) {
+    __shared__ float part[NW][16][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int F = P.n_feat, M = P.n_tok, K = P.d_model;
+    const int f = blockIdx.x * 32 + l32;  // A-operand row of this lane
+    const int t = blockIdx.y * 32 + l32;  // B-operand column (token) of this lane
+    const bool f_ok = f < F, t_ok = t < M;
+    const uint8_t* wrow = reinterpret_cast<const uint8_t*>(P.w + (int64_t)(f_ok ? f : 0) * K);
+    const uint8_t* xrow = reinterpret_cast<const uint8_t*>(P.x + (int64_t)(t_ok ? t : 0) * K);
+    const int kq = K / NW;  // a multiple of 16 (the launcher picks NW so)
+    // the lane's token for the epilogue (column blockIdx.y * 32 + lane % 32):
+    // its slot and position are read now, their latency hidden by the GEMM
+    const int tok = t;
+    const int tb = t_ok ? tok / P.n_new : 0, tn = t_ok ? tok % P.n_new : 0;
+    const int slot = t_ok ? P.slot0[tb] + tn : -1;
+    const int pos = t_ok ? P.positions[tok] : -1;
+    const int k0 = wave * kq;
+    // The K order inside each block of 64 is permuted (the same for both
+    // operands, so the sums are unchanged): in MFMA step s of a block, lane
+    // (m, hi) supplies elements 32 hi + 8 s .. + 7, so over the block's four
+    // steps each lane reads 64 contiguous bytes and each row is read as whole
+    // 128-byte lines (a tail shorter than 128 keeps the plain order: lane
+    // (m, hi) supplies elements 8 hi .. 8 hi + 7 of the step).  Operands of KU steps are loaded before any of them is
+    // used (every load in flight at once: at decode-sized token counts there
+    // are few workgroups); two accumulators so consecutive products do not
+    // wait for each other.  Rows past F and tokens past the end read row 0 /
+    // token 0: their products land in outputs the epilogue never stores.
+    constexpr int KU = 8;  // two blocks of 64
+    f32x16 acc0 = {}, acc1 = {};
+    int k = k0;
+    for (; k + 16 * KU <= k0 + kq; k += 16 * KU) {
+        bf16x8 a[KU], bm[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const int e = k + 64 * (u / 4) + 32 * hi + 8 * (u % 4);
+            a[u] = ld16<bf16x8>(wrow + (int64_t)e * 2);
+            bm[u] = ld16<bf16x8>(xrow + (int64_t)e * 2);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load issued before the first product
+#pragma unroll
+        for (int u = 0; u < KU; u += 2) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], bm[u], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u + 1], bm[u + 1], acc1, 0, 0, 0);
+        }
+    }
+    for (; k < k0 + kq; k += 16) {  // the rest, one step at a time in the plain K order
+        const int e = k + 8 * hi;
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ld16<bf16x8>(wrow + (int64_t)e * 2),
+                                                     ld16<bf16x8>(xrow + (int64_t)e * 2), acc0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[wave][r][lane] = acc0[r] + acc1[r];
+    __syncthreads();
+
+    // waves 0 .. 3 finish: wave w takes registers 4w .. 4w+3 of every lane,
+    // rows 8w + 4hi + j
+    if (wave >= 4) return;
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s += part[w][4 * wave + j][lane];
+        v[j] = s;
+    }
+    if (!t_ok) return;
+    const int b = tb;
+    // one lane per token reports and records (the workgroup of the first rows)
+    const bool recorder = blockIdx.x == 0 && wave == 0 && hi == 0;
+    if (slot < 0 || slot >= P.capacity || pos < 0) {
+        if (recorder && P.dev_status) {
+            uint32_t bits = 0;
+            if (slot < 0 || slot >= P.capacity) bits |= KPA_DEV_SLOT_OUT_OF_RANGE;
+            if (pos < 0) bits |= KPA_DEV_NEGATIVE_POSITION;
+            atomicOr(P.dev_status, bits);
+        }
+        return;
+    }
+    const Layout& L = P.L;
+    uint8_t* tile_base = P.cache + ((int64_t)b * L.n_tiles + slot / kTileSlots) * L.tile_bytes;
+    const int ts = slot % kTileSlots;
+    // stacked rows: B^K [0, n1), A^K [n1, n10), A^V [n10, n102), B^V [n102, F)
+    const int n1 = L.elems[1], n10 = n1 + L.elems[0], n102 = n10 + L.elems[2];
+    const int q2 = P.d.q2;
+    const double log2_base = log2((double)P.d.rope_base);
+    const int fb = blockIdx.x * 32 + 8 * wave + 4 * hi;  // row of v[0]; a multiple of 4
+    auto put = [&](int c, int e, float val) {
+        if constexpr (kF32)
+            store_elem<float>(tile_base + elem_offset(L, c, e, ts), val);
+        else
+            store_elem<uint16_t>(tile_base + elem_offset(L, c, e, ts), f32_to_bf16_rne(val));
+    };
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int fr = fb + j;
+        if (fr >= F) break;
+        if (fr < n1) {
+            // B^K: rows fr (even) and fr + 1 form one RoPE pair (n1 is even)
+            if (j % 2 == 0) {
+                double y0, y1;
+                rope_pair((double)v[j], (double)v[j + 1], pos, (fr % q2) / 2, q2, log2_base, y0, y1);
+                if constexpr (kF32) {
+                    store_elem<float>(tile_base + elem_offset(L, 1, fr, ts), (float)y0);
+                    store_elem<float>(tile_base + elem_offset(L, 1, fr + 1, ts), (float)y1);
+                } else {
+                    store_elem<uint16_t>(tile_base + elem_offset(L, 1, fr, ts), f64_to_bf16_rne(y0));
+                    store_elem<uint16_t>(tile_base + elem_offset(L, 1, fr + 1, ts), f64_to_bf16_rne(y1));
+                }
+            }
+        } else if (fr < n10) {
+            put(0, fr - n1, v[j]);
+        } else if (fr < n102) {
+            put(2, fr - n10, v[j]);
+        } else {
+            put(3, fr - n102, v[j]);
+        }
+    }
+    if (recorder) {
+        int32_t* positions = reinterpret_cast<int32_t*>(P.cache + L.positions_off);
+        positions[(int64_t)b * L.n_tiles * kTileSlots + slot] = pos;
+    }
+}
+
+template <int NW>
+void launch_nw(const ProjectParams& P, hipStream_t s, const KernelEvents& ev) {
+    dim3 grid((P.n_feat + 31) / 32, (P.n_tok + 31) / 32);
+    if (P.d.dtype == KPA_F32)
+        hipExtLaunchKernelGGL((project_append_kernel<true, NW>), grid, dim3(NW * 64), 0, s, ev.start, ev.stop, 0, P);
+    else
+        hipExtLaunchKernelGGL((project_append_kernel<false, NW>), grid, dim3(NW * 64), 0, s, ev.start, ev.stop, 0, P);
+}
+
+}  // namespace
+
+// d_model is a multiple of 64; each wave's share must be a multiple of 16.
+hipError_t launch_project_append(const ProjectParams& P, hipStream_t s, const KernelEvents& ev) {
+    if (P.d_model % (16 * 16) == 0 && P.d_model >= 1024)
+        launch_nw<16>(P, s, ev);
+    else if (P.d_model % (8 * 16) == 0 && P.d_model >= 512)
+        launch_nw<8>(P, s, ev);
+    else
+        launch_nw<4>(P, s, ev);
+    return hipGetLastError();
+}
+
+}  // namespace kpa

@@ -160,6 +160,33 @@ int kpa_cache_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t c
 /* Workspace bytes kpa_decode / kpa_decode_multiq need for these arguments
  * (partial results of the split-KV decode).  num_splits as in kpa_decode.
  * Uses the current device's CU count. */
+/*
+ * kpa_project_append -- project n_new tokens' hidden states to their factors
+ * and write them into the cache, in one kernel ([KPA] Eq. (5) and the merged
+ * form after it: every factor is a linear map of the hidden state, the ranks
+ * of a factor type merged into one matrix whose product is reshaped to
+ * [R][p][q]; the four merged matrices are stacked here).
+ *   x [batch][n_new][d_model]: bf16, device, 16-byte aligned; the hidden
+ *       states (token n of sequence b at row b * n_new + n).
+ *   d_model: a positive multiple of 64.
+ *   w [F][d_model]: bf16, device, 16-byte aligned, F = (R_K + R_V)(p1 q1 + p2 q2);
+ *       rows W^{B^K} (R_K p2 q2 rows), W^{A^K} (R_K p1 q1), W^{A^V}
+ *       (R_V p1 q1), W^{B^V} (R_V p2 q2), each block's rows in [R][p][q]
+ *       row-major order.
+ *   positions, slot0, dev_status, cache: as kpa_cache_append.
+ * The products are accumulated in float32 on the matrix cores (bf16
+ * operands).  The cache then holds what kpa_cache_append of those products
+ * would store, except that B~^K = R^(2)(pos) B^K is computed in float64 from
+ * the float32 products and every value is rounded once to dims.dtype (no
+ * intermediate bf16 factor tensor).  Returns KPA_OK, KPA_ERR_NULL_PTR,
+ * KPA_ERR_DTYPE, KPA_ERR_INVALID_DIMS, KPA_ERR_INVALID_ARG (d_model not a
+ * positive multiple of 64, batch * n_new above 2^21, misaligned pointers) or
+ * KPA_ERR_HIP; n_new = 0 or batch = 0 is a no-op.
+ */
+int kpa_project_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t capacity, const void* x,
+                       int32_t d_model, const void* w, const int32_t* positions, const int32_t* slot0,
+                       int32_t n_new, uint32_t* dev_status, void* stream);
+
 size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t max_ctx,
                                   int32_t n_q, int32_t num_splits);
 
@@ -257,13 +284,14 @@ int kpa_append_decode(const kpa_dims* dims, void* cache, int32_t batch, int32_t 
  * stop_event are hipEvent_t handles created by the caller with timing
  * enabled (both non-NULL), or both NULL to cancel a pending request.  The
  * next decode call (kpa_decode, kpa_decode_multiq, kpa_decode_factored,
- * kpa_append_decode) made on the same host thread
- * launches its split-KV decode kernel with hipExtLaunchKernel so that the
- * runtime stamps start_event and stop_event with that kernel's own start and
- * end on its stream (the log-sum-exp merge is not included, and no extra
- * marker enters the stream); the request is then dropped, also when that
- * call fails its checks.  Lets a caller time the decode kernel alone.  The
- * events stay owned by the caller and must outlive that call.
+ * kpa_append_decode) or kpa_project_append call made on the same host thread
+ * launches its main kernel (the split-KV decode kernel; the projection
+ * kernel) with hipExtLaunchKernel, so that the runtime stamps start_event
+ * and stop_event with that kernel's own start and end on its stream (the
+ * log-sum-exp merge is not included).  The request is then dropped, also
+ * when that call fails its checks.  The stamped events still cost the stream
+ * a few microseconds between dispatches: time a sample of calls, not every
+ * one.  The events stay owned by the caller and must outlive that call.
  * Returns KPA_OK, or KPA_ERR_NULL_PTR if exactly one handle is NULL.
  */
 int kpa_time_next_decode_kernel(void* start_event, void* stop_event);

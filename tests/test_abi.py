@@ -122,6 +122,15 @@ def test_null_and_range_errors_return_before_launch():
     assert fq(d, 2, FAKE, 1, 64, FAKE, 64, 1, 0, FAKE, None, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -2
     assert fq(d, 2, FAKE, 1, 64, FAKE, 64, 1, 0, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0, None, None) == -2
     assert fq(d, 2, None, 0, 64, None, 64, 1, 0, None, None, None, None, None, None, 0, 0, None, None) == 0
+    # projection + append: d_model a positive multiple of 64, pointers, nothing to do
+    pa = lib.kpa_project_append
+    assert pa(d, FAKE, 1, 64, FAKE, 100, FAKE, FAKE, FAKE, 1, None, None) == -7
+    assert pa(d, FAKE, 1, 64, FAKE, 0, FAKE, FAKE, FAKE, 1, None, None) == -7
+    assert pa(d, FAKE, 1, 64, None, 128, FAKE, FAKE, FAKE, 1, None, None) == -2
+    assert pa(d, FAKE, 1, 64, FAKE, 128, FAKE, FAKE, None, 1, None, None) == -2
+    assert pa(d, FAKE + 2, 1, 64, FAKE, 128, FAKE, FAKE, FAKE, 1, None, None) == -7
+    assert pa(d, None, 0, 64, None, 128, None, None, None, 1, None, None) == 0
+    assert pa(d, None, 1, 64, None, 128, None, None, None, 0, None, None) == 0
     # append + decode: the append arguments are checked first, then the decode's
     ad = lib.kpa_append_decode
     big = 1 << 30
