@@ -119,14 +119,34 @@ __device__ MergeOut merge_group(const float* ml, int64_t ml_stride, const float*
     for (int k = k0 + U * KL; active && k < n; k += KL)
         axpy<VEC>(sh.w[k], *reinterpret_cast<const V*>(o + (int64_t)k * o_stride + c * VEC), acc);
     // add the KL partial sums of each column block
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) part[t * VEC + e] = acc[e];
-    __syncthreads();
     MergeOut r{M, L, {0.f, 0.f, 0.f, 0.f}};
-    if (t < CB) {
-        for (int j = 0; j < KL; ++j)
+    if ((CB & (CB - 1)) == 0 && CB <= 64) {
+        // CB a power of two: the lanes of a column block sit CB apart in every
+        // wave, so the wave adds them with shuffles, then the NW wave sums
+        // meet in LDS
+        if (!active)
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) r.acc[e] += part[(j * CB + t) * VEC + e];
+            for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+        for (int x = CB; x < 64; x <<= 1)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], x);
+        if ((t & 63) < CB)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) part[((t >> 6) * CB + c) * VEC + e] = acc[e];
+        __syncthreads();
+        if (t < CB)
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) r.acc[e] += part[(w * CB + t) * VEC + e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) part[t * VEC + e] = acc[e];
+        __syncthreads();
+        if (t < CB) {
+            for (int j = 0; j < KL; ++j)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) r.acc[e] += part[(j * CB + t) * VEC + e];
+        }
     }
     __syncthreads();  // the LDS is reused by the caller
     return r;
@@ -145,30 +165,36 @@ __device__ __forceinline__ void store_out(float* dst, const MergeOut& r, float s
     *reinterpret_cast<V*>(dst) = x;
 }
 
-// One block per (row, head, group of chunks).  group_size = n_split for a
-// single level, kMergeGroup with a second level (n_group > 1).
+// One block per (row, head, group of chunks) -- or, for a single level, per
+// (row, head, slice of the d_h columns): blockIdx.y is the group with a second
+// level (n_group > 1), else the column slice (col_split slices; every slice's
+// block reads all (m, l) pairs for the weights and merges its own columns, so
+// a long chunk list is spread over more blocks).  group_size = n_split for a
+// single level, kMergeGroup with a second level.
 template <int VEC, int U, int T>
-__global__ void __launch_bounds__(T) merge_kernel(DecodeParams P, int group_size) {
+__global__ void __launch_bounds__(T) merge_kernel(DecodeParams P, int group_size, int col_split) {
     __shared__ MergeLds sh;
     __shared__ float part[T * VEC];
     __shared__ int is_last;
     const int h = P.d.p1 * P.d.p2, dh = P.d.q1 * P.d.q2;
     const int64_t row = blockIdx.x / h;  // (b, n)
     const int i = blockIdx.x % h;
-    const int g = blockIdx.y;
     const int S = P.n_split, G = P.n_group;
+    const int g = G > 1 ? blockIdx.y : 0;
+    const int dh_part = dh / col_split;                   // columns of this block
+    const int col0 = G > 1 ? 0 : blockIdx.y * dh_part;    // first column of this block
     const int k0 = g * group_size;
     const int n = min(S - k0, group_size);
     const int t = threadIdx.x;
-    const bool has_out = t < dh / VEC;
+    const bool has_out = t < dh_part / VEC;
 
     MergeOut r = merge_group<VEC, U, T>(P.part_ml + ((row * S + k0) * h + i) * 2, (int64_t)h * 2,
-                                        P.part_o + ((row * S + k0) * h + i) * (int64_t)dh, (int64_t)h * dh, n, dh,
-                                        sh, part);
+                                        P.part_o + ((row * S + k0) * h + i) * (int64_t)dh + col0, (int64_t)h * dh, n,
+                                        dh_part, sh, part);
     if (T > 256 || G == 1) {  // the 1024-thread blocks are single-level only
         const float inv = r.L > 0.f ? 1.f / r.L : 0.f;
-        if (has_out) store_out<VEC>(P.out + (row * h + i) * dh + t * VEC, r, inv);
-        if (P.lse && t == 0) P.lse[row * h + i] = r.L > 0.f ? (r.M + log2f(r.L)) * kLn2 : -INFINITY;
+        if (has_out) store_out<VEC>(P.out + (row * h + i) * dh + col0 + t * VEC, r, inv);
+        if (P.lse && t == 0 && col0 == 0) P.lse[row * h + i] = r.L > 0.f ? (r.M + log2f(r.L)) * kLn2 : -INFINITY;
         return;
     }
 
@@ -197,36 +223,46 @@ __global__ void __launch_bounds__(T) merge_kernel(DecodeParams P, int group_size
 }
 
 template <int VEC, int U, int T>
-void launch_one(const DecodeParams& P, int group_size, hipStream_t s) {
+void launch_one(const DecodeParams& P, int group_size, int col_split, hipStream_t s) {
     const int h = P.d.p1 * P.d.p2;
-    hipLaunchKernelGGL((merge_kernel<VEC, U, T>), dim3(P.batch * P.n_q * h, P.n_group), dim3(T), 0, s, P, group_size);
+    const int gy = P.n_group > 1 ? P.n_group : col_split;
+    hipLaunchKernelGGL((merge_kernel<VEC, U, T>), dim3(P.batch * P.n_q * h, gy), dim3(T), 0, s, P, group_size,
+                       col_split);
 }
 
 // Loads per thread: the smallest power of two covering the group's chunks.
 template <int VEC, int T>
-void launch_u(const DecodeParams& P, int group_size, hipStream_t s) {
+void launch_u(const DecodeParams& P, int group_size, int col_split, hipStream_t s) {
     const int dh = P.d.q1 * P.d.q2;
-    const int KL = T / (dh / VEC);
+    const int KL = T / (dh / col_split / VEC);
     const int need = (group_size + KL - 1) / KL;
-    if (need <= 1) launch_one<VEC, 1, T>(P, group_size, s);
-    else if (need <= 2) launch_one<VEC, 2, T>(P, group_size, s);
-    else if (need <= 4) launch_one<VEC, 4, T>(P, group_size, s);
-    else if (need <= 8) launch_one<VEC, 8, T>(P, group_size, s);
-    else launch_one<VEC, 16, T>(P, group_size, s);
+    if (need <= 1) launch_one<VEC, 1, T>(P, group_size, col_split, s);
+    else if (need <= 2) launch_one<VEC, 2, T>(P, group_size, col_split, s);
+    else if (need <= 4) launch_one<VEC, 4, T>(P, group_size, col_split, s);
+    else if (need <= 8) launch_one<VEC, 8, T>(P, group_size, col_split, s);
+    else launch_one<VEC, 16, T>(P, group_size, col_split, s);
 }
 
 // Block size: the smallest of 64 / 128 / 256 threads that covers the group
 // with at most 8 loads per thread (fewer threads per output, fewer
-// block-wide barriers); 1024 threads for a wide single level.
+// block-wide barriers); 1024 threads for a wide single level, whose columns
+// are split over blocks until there are ~256 of them (the block count is
+// otherwise rows x heads, 32 for a single long sequence).
 template <int VEC>
 void launch_vec(const DecodeParams& P, hipStream_t s) {
     const int gs = P.n_group > 1 ? kMergeGroup : P.n_split;  // chunks per block
-    if (gs > kMergeGroup) return launch_u<VEC, 1024>(P, gs, s);
+    if (gs > kMergeGroup) {
+        const int64_t blocks = (int64_t)P.batch * P.n_q * P.d.p1 * P.d.p2;
+        const int cb = P.d.q1 * P.d.q2 / VEC;  // column blocks of d_h
+        int cs = 1;
+        while (cb % (2 * cs) == 0 && blocks * cs < 256) cs *= 2;
+        return launch_u<VEC, 1024>(P, gs, cs, s);
+    }
     const int CB = P.d.q1 * P.d.q2 / VEC;
     auto need = [&](int T) { return T / CB > 0 ? (gs + T / CB - 1) / (T / CB) : 1 << 30; };
-    if (need(64) <= 8) return launch_u<VEC, 64>(P, gs, s);
-    if (need(128) <= 8) return launch_u<VEC, 128>(P, gs, s);
-    return launch_u<VEC, 256>(P, gs, s);
+    if (need(64) <= 8) return launch_u<VEC, 64>(P, gs, 1, s);
+    if (need(128) <= 8) return launch_u<VEC, 128>(P, gs, 1, s);
+    return launch_u<VEC, 256>(P, gs, 1, s);
 }
 
 }  // namespace
