@@ -8,8 +8,9 @@ float64 oracle.  Before the step the new tokens' slots hold other tokens'
 factors, so a step that skipped or misplaced its append would read them.
 Cases cover every kernel shape, new tokens in the first tile of a KV chunk
 (one-tile chunks), tokens straddling two chunks, ragged contexts, the
-vector-ALU path (append kernel launched first), an out-of-range slot and
-n_new = 0.
+vector-ALU path (append kernel launched first), an out-of-range slot,
+n_new = 0, more new tokens than queries, and new tokens written past the
+context (stored, but not read by this step's decode).
 """
 import numpy as np
 import pytest
@@ -46,11 +47,14 @@ def _stale_copy(inp, dims, cap, n_new, seed):
     return cache, cache.clone()
 
 
-def _step(inp, dims, cache, cap, n_new, fused, num_splits=0, causal=True, status=None, slot0=None):
+def _step(inp, dims, cache, cap, n_new, fused, num_splits=0, causal=True, status=None, slot0=None, new=None):
+    """One step: append n_new tokens (by default the last n_new of each
+    context, else `new` = (a_k, b_k, a_v, b_v, positions, slot0)), then decode
+    inp's queries over inp.ctx_len; fused or as two calls."""
     nb, nq = inp.batch, inp.q.shape[1]
     h, dh = dims.h, dims.d_h
     mc = int(inp.ctx_len.max().item())
-    ak, bk, av, bv, pos, s0 = _new_tokens(inp, n_new)
+    ak, bk, av, bv, pos, s0 = _new_tokens(inp, n_new) if new is None else new
     if slot0 is not None:
         s0 = slot0
     q = inp.q.cuda().contiguous()
@@ -163,3 +167,70 @@ def test_fused_step_full_size_equals_append_then_decode(gpu_lib, name):
     assert np.all(np.isfinite(fo))
     assert torch.equal(cache_seq, cache_fused), "cache bytes differ"
     assert np.array_equal(so, fo) and np.array_equal(sl, fl), "outputs differ"
+
+
+MORE_CASES = [
+    # name, batch, ctx, n_new, ragged, num_splits  (one query)
+    ("kpa_32k", 2, 770, 3, False, 25),          # slots 767 .. 769: one-tile chunks 23 and 24
+    ("tpa_degenerate", 2, 642, 5, False, 21),   # slots 637 .. 641 straddle chunks 19 and 20
+    ("long_512k", 2, 1000, 40, True, 0),
+    ("multiq_16", 2, 530, 9, True, 0),
+]
+
+
+@pytest.mark.parametrize("name,batch,ctx,n_new,ragged,num_splits", MORE_CASES)
+def test_fused_step_with_more_new_tokens_than_queries(gpu_lib, name, batch, ctx, n_new, ragged, num_splits):
+    cfg = _cfg(name)
+    inp = make_inputs(cfg, seed=25, batch=batch, ctx=ctx, n_q=1, ragged=ragged)
+    if ragged:  # every context holds the step's tokens
+        inp.ctx_len.clamp_(min=n_new)
+        inp.q_pos.copy_(inp.ctx_len.view(-1, 1) - 1)
+    dims = dims_of(cfg)
+    cache_seq, cache_fused = _stale_copy(inp, dims, ctx, n_new, seed=25)
+    so, sl = _step(inp, dims, cache_seq, ctx, n_new, fused=False, num_splits=num_splits)
+    fo, fl = _step(inp, dims, cache_fused, ctx, n_new, fused=True, num_splits=num_splits)
+    assert torch.equal(cache_seq, cache_fused), "cache bytes differ"
+    assert np.array_equal(so, fo) and np.array_equal(sl, fl, equal_nan=True), "outputs differ"
+    ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
+                               inp.q, inp.q_pos, causal=True)
+    assert_close(fo.astype(np.float64), fl.astype(np.float64), ro, rl, cfg.dtype, f"{name} fused step")
+
+
+PAST_CASES = [
+    # name, batch, ctx, n_new, gap past the context, extra capacity, ragged, num_splits
+    ("kpa_32k", 2, 700, 1, 0, 64, True, 0),       # right after the context, same tile or the next
+    ("kpa_32k", 2, 704, 2, 0, 64, False, 22),     # one-tile chunks: slot 704 is past the last chunk
+    ("kpa_32k", 2, 704, 1, 50, 96, False, 0),     # far past the context
+    ("long_512k", 2, 1500, 3, 7, 64, True, 0),
+    ("tpa_degenerate", 3, 400, 2, 31, 80, True, 13),
+]
+
+
+@pytest.mark.parametrize("name,batch,ctx,n_new,gap,extra,ragged,num_splits", PAST_CASES)
+def test_fused_step_writes_tokens_past_the_context(gpu_lib, name, batch, ctx, n_new, gap, extra, ragged, num_splits):
+    """New tokens at slots ctx_len + gap ..: the step stores them like the
+    append does, and its decode, over ctx_len slots, does not read them."""
+    cfg = _cfg(name)
+    inp = make_inputs(cfg, seed=26, batch=batch, ctx=ctx, n_q=1, ragged=ragged)
+    dims = dims_of(cfg)
+    cap = ctx + extra
+    cache_seq, _ = fill_cache(inp, dims, capacity=cap)
+    cache_fused = cache_seq.clone()
+    junk = make_inputs(cfg, seed=126, batch=batch, ctx=n_new)
+    slot0 = (inp.ctx_len + gap).to(torch.int32)
+    assert int(slot0.max()) + n_new <= cap
+    new = tuple(t.contiguous().cuda() for t in (junk.a_k, junk.b_k, junk.a_v, junk.b_v))
+    new += ((slot0.view(-1, 1) + torch.arange(n_new, dtype=torch.int32).view(1, -1)).contiguous().cuda(),
+            slot0.contiguous().cuda())
+    res = []
+    for cache, fused in ((cache_seq, False), (cache_fused, True)):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        res.append(_step(inp, dims, cache, cap, n_new, fused, num_splits=num_splits, status=status, new=new)
+                   + (int(status.item()),))
+    assert res[0][2] == res[1][2] == 0
+    assert torch.equal(cache_seq, cache_fused), "cache bytes differ"
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1]), "outputs differ"
+    ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
+                               inp.q, inp.q_pos, causal=True)
+    assert_close(res[1][0].astype(np.float64), res[1][1].astype(np.float64), ro, rl, cfg.dtype,
+                 f"{name} step with tokens past the context")
