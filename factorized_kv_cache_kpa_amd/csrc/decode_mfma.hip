@@ -55,6 +55,12 @@ template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int NQW, 
 struct Cfg {
     static constexpr int PG_ = PG, QG_ = QG, PF_ = PF, QF_ = QF, RK_ = RK, RV_ = RV;
     static constexpr bool F_IS_B_ = F_IS_B;
+    // Kernels with one query per workgroup serve single-query decode, where a
+    // tile's bytes are read once per step: their cache loads carry the
+    // nontemporal hint (kpa_32k's kernel: 140 -> 126 us).  The multi-query
+    // kernels' query groups share each tile through L2: no hint there (it
+    // cost multiq_16 2%).
+    static constexpr bool NT_ = NQW * NQG == 1;
     static constexpr int NQW_ = NQW;                 // queries per wave
     static constexpr int NQG_ = NQG;                 // query subgroups per workgroup
     static constexpr int QPW = NQW * NQG;            // queries per workgroup
@@ -138,8 +144,15 @@ __device__ __forceinline__ void dma_g_blocks(const uint8_t* gk, const uint8_t* g
         const int vchunk = (lane & ~3) | ((lane & 3) ^ ((lane >> 3) & 3));
         const uint8_t* src = (key ? gk : gv) + kb * 1024 + (key ? lane : vchunk) * 16;
         constexpr bool kWholeBlocks = S::GK_BYTES % 1024 == 0 && S::GV_BYTES % 1024 == 0;
-        if (kWholeBlocks || lane * 16 < left) dma_to_lds16(src, lds_addr(gdst + k * 1024));
+        if (kWholeBlocks || lane * 16 < left) dma_to_lds16<S::NT_>(src, lds_addr(gdst + k * 1024));
     }
+}
+
+// One wave's F factor bytes, HBM -> registers.
+template <class S>
+__device__ __forceinline__ bf16x8 ld_f(const uint8_t* p) {
+    if constexpr (S::NT_) return ld16_nt<bf16x8>(p);
+    else return ld16<bf16x8>(p);
 }
 
 // G32: convert the bf16 G factors of one tile (the DMA stage, layout as
@@ -396,12 +409,12 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
         for (int r = 0; r < RK; ++r)
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc)
-                f.fk[r][kc] = ld16<bf16x8>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + 2 * kc + half) * 512 + s * 16);
+                f.fk[r][kc] = ld_f<S>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + 2 * kc + half) * 512 + s * 16);
 #pragma unroll
         for (int r = 0; r < RV; ++r)
 #pragma unroll
             for (int nb = 0; nb < KC; ++nb)
-                f.fv[r][nb] = ld16<bf16x8>(tile + offFV + ((int64_t)((r * PF + iF) * QF + 16 * nb + l16) * 32 + 8 * g16) * 2);
+                f.fv[r][nb] = ld_f<S>(tile + offFV + ((int64_t)((r * PF + iF) * QF + 16 * nb + l16) * 32 + 8 * g16) * 2);
     };
     auto issue = [&](const uint8_t* tile, uint8_t* gdst, FRegs& f) {
         dma_g_blocks<S>(tile + offGK, tile + offGV, gdst, wave, lane);
