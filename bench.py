@@ -12,6 +12,10 @@ Prints ONE JSON line with the cached-tokens-attended rate, the roofline of
 the split-KV decode kernel (algorithmic bytes or flops / that kernel's
 average duration, bracketed with HIP events on its own stream by the
 library's measurement hook), and the CPU oracle timed on a bounded sample.
+After the timed steps a plain streaming read of the same cache bytes
+(kpa_stream_xor, nontemporal 16-byte loads) is timed the same way; the
+roofline carries its rate and the decode kernel's fraction of it, the
+measured ceiling beside the published 8 TB/s.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -65,6 +69,8 @@ def parse():
                     help="step as two calls (kpa_cache_append, then the decode) instead of kpa_append_decode")
     ap.add_argument("--call-events", action="store_true",
                     help="also bracket each whole decode call (kernel + merge) with events")
+    ap.add_argument("--no-stream-read", action="store_true",
+                    help="skip the streaming-read measurement of the cache bytes after the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy MIB MiB device-to-device 3 times (HBM counter calibration)")
     ap.add_argument("--summarize-trace", default=None, metavar="STATS_DIR")
@@ -255,6 +261,11 @@ def main():
         log(f"calibration: 3 copies of {args.copy_calibration} MiB")
         del src, dst
 
+    # Measured ceiling: a plain streaming read (kpa_stream_xor) of the same
+    # cache bytes, its launches timed like the decode kernel's (each stamps
+    # its own start and end), three workgroups per CU.
+    stream_gbps = None if args.no_stream_read else stream_read_gbps(cache, dev)
+
     tokens = int(inp.ctx_len.sum().item())  # cached tokens attended per step (per query)
     value = tokens / (ms_per_step / 1e3)
     # the fused kernel also reads the step's new factors and writes them (and
@@ -263,6 +274,9 @@ def main():
     roofline = decode_roofline(cfg, tokens, q.numel() * 4 + out.numel() * 4 + lse.numel() * 4 + app_bytes,
                                float(kern_ms.mean()), float(call_ms.mean()) if call_ev else None,
                                kpa.kpa_decode_path(dims, n_q))
+    if stream_gbps:
+        roofline["stream_read_gbps"] = round(stream_gbps, 1)
+        roofline["hbm_frac_of_stream_read"] = round(roofline["hbm_gbps"] / stream_gbps, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -288,6 +302,34 @@ def main():
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(line + "\n")
+
+
+def stream_read_gbps(buf, dev, launches=20):
+    """GB/s of kpa_stream_xor over the bytes of `buf` (mean over `launches`
+    launches, each bracketed by its own start and end events)."""
+    import numpy as np
+    import torch
+
+    import factorized_kv_cache_kpa_amd as kpa
+
+    nbytes = buf.numel() * buf.element_size() // 16 * 16
+    n_blocks = 3 * torch.cuda.get_device_properties(dev).multi_processor_count
+    partial = torch.empty(n_blocks, dtype=torch.int32, device=dev)
+    for _ in range(5):
+        kpa.kpa_stream_xor(buf, partial, nbytes=nbytes)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+    for a, b in ev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for a, b in ev:
+        kpa.kpa_time_next_decode_kernel(a, b)
+        kpa.kpa_stream_xor(buf, partial, nbytes=nbytes)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    log(f"streaming read of the cache ({nbytes / 1e6:.1f} MB, {n_blocks} workgroups): {ms * 1e3:.1f} us, "
+        f"{nbytes / (ms * 1e-3) / 1e9:.1f} GB/s")
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def alg_flops_per_query_token(cfg):

@@ -97,6 +97,8 @@ def load():
     lib.kpa_decode_path.argtypes = [DP, I32]
     lib.kpa_decode_path.restype = ctypes.c_char_p
     lib.kpa_time_next_decode_kernel.argtypes = [P, P]
+    lib.kpa_stream_xor.argtypes = [P, ctypes.c_size_t, P, I32, P]
+    lib.kpa_stream_xor.restype = ctypes.c_int
     lib.kpa_time_next_decode_kernel.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -184,6 +186,21 @@ def kpa_project_append(dims, cache, batch, capacity, x, w, positions, slot0, n_n
         _ptr(slot0, torch.int32, "slot0"), int(n_new), _ptr(dev_status, torch.int32, "dev_status"),
         _stream(stream, cache))
     _check("kpa_project_append", st)
+
+
+def kpa_stream_xor(buf, partial, n_blocks=None, nbytes=None, stream=None):
+    """Streaming read of `buf` (any contiguous device tensor; the first
+    `nbytes` bytes, default all): partial[w] = XOR of the 32-bit words of
+    workgroup w's contiguous share.  partial: int32 [n_blocks]."""
+    if n_blocks is None:
+        n_blocks = partial.numel()
+    if partial.numel() < n_blocks:
+        raise ValueError("partial holds fewer than n_blocks words")
+    if nbytes is None:
+        nbytes = buf.numel() * buf.element_size()
+    st = load().kpa_stream_xor(_ptr(buf, None, "buf"), int(nbytes), _ptr(partial, torch.int32, "partial"),
+                               int(n_blocks), _stream(stream, buf))
+    _check("kpa_stream_xor", st)
 
 
 def kpa_decode_workspace_bytes(dims, batch, max_ctx, n_q=1, num_splits=0) -> int:

@@ -679,26 +679,28 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     if constexpr (S::G32_) {
         // One bf16 stage (gbuf_a) and one float32 copy (gbuf_b).  Per tile:
         // wait for the tile's loads; barrier (stage complete, every wave done
-        // reading the previous copy); convert; barrier (copy complete, stage
-        // free); issue the next tile's loads; compute.
-        auto stage_tile = [&]() {
+        // reading the previous copy); issue the next tile's F loads (their
+        // registers are free), so that bytes stay in flight while the waves
+        // convert; convert; barrier (copy complete, stage free); issue the
+        // next tile's G DMA; compute.
+        auto stage_tile = [&](const uint8_t* next, FRegs& fnext) {
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
+            if (next) load_f(next, fnext);
             convert_g<S>(gbuf_a, gbuf_b);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            if (next) dma_g_blocks<S>(next + offGK, next + offGV, gbuf_a, wave, lane);
         };
         for (int s0 = first; s0 < last; s0 += 2 * kTileSlots) {
-            stage_tile();
             const uint8_t* tile = seq + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
-            if (s0 + kTileSlots < last) issue(tile + L.tile_bytes, gbuf_a, fb);
+            stage_tile(s0 + kTileSlots < last ? tile + L.tile_bytes : nullptr, fb);
             process(s0, gbuf_b, fa);
             if (s0 + kTileSlots >= last) break;
-            stage_tile();
-            if (s0 + 2 * kTileSlots < last) issue(tile + 2 * L.tile_bytes, gbuf_a, fa);
+            stage_tile(s0 + 2 * kTileSlots < last ? tile + 2 * L.tile_bytes : nullptr, fa);
             process(s0 + kTileSlots, gbuf_b, fb);
         }
     } else

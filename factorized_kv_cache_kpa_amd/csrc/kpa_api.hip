@@ -107,8 +107,9 @@ int kpa_cache_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t c
     return launch_append(P, static_cast<hipStream_t>(stream)) == hipSuccess ? KPA_OK : KPA_ERR_HIP;
 }
 
-// Events the next decode or projection call on this thread has stamped with
-// its main kernel's start and end (kpa_time_next_decode_kernel).
+// Events the next decode, projection or streaming-read call on this thread
+// has stamped with its main kernel's start and end
+// (kpa_time_next_decode_kernel).
 static thread_local KernelEvents t_kernel_events;
 
 int kpa_project_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t capacity, const void* x,
@@ -141,6 +142,18 @@ int kpa_project_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t
     P.slot0 = slot0;
     P.dev_status = dev_status;
     return launch_project_append(P, static_cast<hipStream_t>(stream), ev) == hipSuccess ? KPA_OK : KPA_ERR_HIP;
+}
+
+int kpa_stream_xor(const void* buf, size_t bytes, uint32_t* partial, int32_t n_blocks, void* stream) {
+    // a pending measurement request applies to this call only
+    const KernelEvents ev = t_kernel_events;
+    t_kernel_events = KernelEvents{};
+    if (!buf || !partial) return KPA_ERR_NULL_PTR;
+    if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40) || !aligned(buf, 16)) return KPA_ERR_INVALID_ARG;
+    if (n_blocks < 1 || n_blocks > 65535) return KPA_ERR_INVALID_ARG;
+    return launch_stream_xor(buf, (int64_t)bytes, partial, n_blocks, static_cast<hipStream_t>(stream), ev) == hipSuccess
+               ? KPA_OK
+               : KPA_ERR_HIP;
 }
 
 size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t max_ctx, int32_t n_q,

@@ -199,6 +199,8 @@ hipError_t launch_append(const AppendParams& P, hipStream_t s);
 hipError_t launch_project_append(const ProjectParams& P, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);
 hipError_t launch_merge(const DecodeParams& P, hipStream_t s);
+hipError_t launch_stream_xor(const void* buf, int64_t bytes, uint32_t* partial, int n_blocks, hipStream_t s,
+                             const KernelEvents& ev);
 hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);
 bool decode_mfma_supported(const kpa_dims& d, int n_q);
 int decode_mfma_blocks_per_cu(const kpa_dims& d, int n_q);

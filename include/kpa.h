@@ -284,9 +284,9 @@ int kpa_append_decode(const kpa_dims* dims, void* cache, int32_t batch, int32_t 
  * stop_event are hipEvent_t handles created by the caller with timing
  * enabled (both non-NULL), or both NULL to cancel a pending request.  The
  * next decode call (kpa_decode, kpa_decode_multiq, kpa_decode_factored,
- * kpa_append_decode) or kpa_project_append call made on the same host thread
- * launches its main kernel (the split-KV decode kernel; the projection
- * kernel) with hipExtLaunchKernel, so that the runtime stamps start_event
+ * kpa_append_decode), kpa_project_append or kpa_stream_xor call made on the
+ * same host thread launches its main kernel (the split-KV decode kernel; the
+ * projection kernel; the streaming read) with hipExtLaunchKernel, so that the runtime stamps start_event
  * and stop_event with that kernel's own start and end on its stream (the
  * log-sum-exp merge is not included).  The request is then dropped, also
  * when that call fails its checks.  The stamped events still cost the stream
@@ -295,6 +295,26 @@ int kpa_append_decode(const kpa_dims* dims, void* cache, int32_t batch, int32_t 
  * Returns KPA_OK, or KPA_ERR_NULL_PTR if exactly one handle is NULL.
  */
 int kpa_time_next_decode_kernel(void* start_event, void* stop_event);
+
+/*
+ * kpa_stream_xor -- measurement aid, not part of the method: the rate of a
+ * plain streaming read, against which the decode kernels' HBM rate is set
+ * (run it over the same buffer a decode reads, e.g. the cache).  Reads the
+ * `bytes` bytes at `buf` once, with 16-byte nontemporal loads (the decode
+ * kernels' load form).  n_blocks workgroups each take one contiguous share:
+ * with n16 = bytes / 16 and C = ceil(n16 / n_blocks), workgroup w reads the
+ * 16-byte words [w C, min((w + 1) C, n16)) and writes to partial[w] the XOR
+ * of their 32-bit words (0 for an empty share), so the XOR of partial[] is
+ * the XOR of every 32-bit word of the buffer.
+ *   buf      device, 16-byte aligned, `bytes` readable; bytes a positive
+ *            multiple of 16, at most 2^40
+ *   partial  device uint32_t[n_blocks], written
+ *   n_blocks 1 .. 65535 (the chip holds 8 such workgroups per CU at once;
+ *            3 per CU is the decode kernels' usual grid)
+ * Consumes a pending kpa_time_next_decode_kernel request.  Returns KPA_OK,
+ * KPA_ERR_NULL_PTR, KPA_ERR_INVALID_ARG (sizes, alignment), KPA_ERR_HIP.
+ */
+int kpa_stream_xor(const void* buf, size_t bytes, uint32_t* partial, int32_t n_blocks, void* stream);
 
 /* Static description of a kpa_status code. */
 const char* kpa_status_string(int status);

@@ -147,6 +147,15 @@ def test_null_and_range_errors_return_before_launch():
               FAKE, big, 0, None, None) == -7
     assert ad(d, None, 0, 64, None, None, None, None, None, None, 1, None, 64, 1, 0, None, None, None, None,
               None, 0, 0, None, None) == 0
+    # streaming read (measurement aid): pointers, sizes, alignment, block count
+    sx = lib.kpa_stream_xor
+    assert sx(None, 1024, FAKE, 4, None) == -2
+    assert sx(FAKE, 1024, None, 4, None) == -2
+    assert sx(FAKE, 0, FAKE, 4, None) == -7
+    assert sx(FAKE, 1000, FAKE, 4, None) == -7
+    assert sx(FAKE + 8, 1024, FAKE, 4, None) == -7
+    assert sx(FAKE, 1024, FAKE, 0, None) == -7
+    assert sx(FAKE, 1024, FAKE, 65536, None) == -7
 
 
 def test_workspace_sizes_follow_the_split_count():
