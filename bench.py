@@ -194,7 +194,36 @@ def main():
         if ev is not None:
             ev[1].record()
 
-    # untimed steps until the clocks settle, then the warm-up steps proper
+    def timing_events(n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in ev:  # create the HIP events before the timed region
+            e0.record()
+            e1.record()
+        return ev
+
+    # Every event_every-th timed step's split-KV decode kernel is bracketed by
+    # a pair of HIP events on its stream, stamped by the launch itself with
+    # the kernel's own start and end (the whole-call pair only on request).
+    # Not every step: even these events cost the stream time between
+    # dispatches (~10 us a step on kpa_32k, measured).
+    every = max(1, args.event_every)
+    sampled = list(range(every - 1, args.steps, every)) or [args.steps - 1]
+    kern_ev = dict(zip(sampled, timing_events(len(sampled))))
+    call_ev = dict(zip(sampled, timing_events(len(sampled)))) if args.call_events else None
+
+    # One step and its output check first: every host-side first use (torch's
+    # own kernels included) happens here, not between the warm-up and the
+    # timed steps.  An idle gap there (tens of ms) lets the clocks drop, and
+    # the timed steps then ran in the recovery transient (measured: long_512k
+    # 130 -> 160-190 us per dispatch for the next few ms).
+    step()
+    torch.cuda.synchronize()
+    if not torch.isfinite(out).all():
+        log("non-finite decode output")
+        sys.exit(1)
+
+    # untimed steps until the clocks settle, then the warm-up steps proper,
+    # then the timed steps with no host work in between
     t_pre = time.perf_counter()
     n_pre = 0
     while time.perf_counter() - t_pre < args.prewarm_s:
@@ -207,28 +236,8 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    if not torch.isfinite(out).all():
-        log("non-finite decode output")
-        sys.exit(1)
-    log(f"warmup done ({args.warmup} steps)")
 
-    def timing_events(n):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for e0, e1 in ev:  # create the HIP events before the timed region
-            e0.record()
-            e1.record()
-        return ev
-
-    # Timed region: K steps.  Every event_every-th step's split-KV decode
-    # kernel is bracketed by a pair of HIP events on its stream, stamped by
-    # the launch itself with the kernel's own start and end (the whole-call
-    # pair only on request).  Not every step: even these events cost the
-    # stream time between dispatches (~10 us a step on kpa_32k, measured).
-    every = max(1, args.event_every)
-    sampled = list(range(every - 1, args.steps, every)) or [args.steps - 1]
-    kern_ev = dict(zip(sampled, timing_events(len(sampled))))
-    call_ev = dict(zip(sampled, timing_events(len(sampled)))) if args.call_events else None
-    torch.cuda.synchronize()
+    # Timed region: K steps.
     t_start = time.perf_counter()
     for k in range(args.steps):
         if k in kern_ev:
@@ -238,6 +247,10 @@ def main():
             step()
     torch.cuda.synchronize()
     t_end = time.perf_counter()
+    if not torch.isfinite(out).all():
+        log("non-finite decode output")
+        sys.exit(1)
+    log(f"warm-up {args.warmup} steps, then {args.steps} timed")
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
     kern_ev = list(kern_ev.values())
     call_ev = list(call_ev.values()) if call_ev else None
@@ -247,6 +260,12 @@ def main():
         f"over {len(kern_ms)} sampled steps "
         f"(median {np.median(kern_ms) * 1e3:.1f})"
         + (f", decode call {call_ms.mean() * 1e3:.1f} us" if call_ev else ""))
+
+    # Measured ceiling: a plain streaming read (kpa_stream_xor) of the same
+    # cache bytes, its launches timed like the decode kernel's (each stamps
+    # its own start and end), three workgroups per CU.
+    # (before the calibration copies, which a counter summary expects last)
+    stream_gbps = None if args.no_stream_read else stream_read_gbps(cache, dev)
 
     if args.copy_calibration > 0:
         # a plain device-to-device copy of known size, after the timed region,
@@ -260,11 +279,6 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration: 3 copies of {args.copy_calibration} MiB")
         del src, dst
-
-    # Measured ceiling: a plain streaming read (kpa_stream_xor) of the same
-    # cache bytes, its launches timed like the decode kernel's (each stamps
-    # its own start and end), three workgroups per CU.
-    stream_gbps = None if args.no_stream_read else stream_read_gbps(cache, dev)
 
     tokens = int(inp.ctx_len.sum().item())  # cached tokens attended per step (per query)
     value = tokens / (ms_per_step / 1e3)
@@ -472,6 +486,13 @@ def summarize_trace(args):
         lines.append(f"- rocprofv3, all {k} timed steps: decode kernel average {sum(timed) / k:.1f} us")
     if avg:
         lines.append(f"- rocprofv3 decode kernel average over every dispatch of the run: {avg:.1f} us")
+    if "stream_read_gbps" in rf:
+        lines.append(f"- streaming read of the same cache bytes (kpa_stream_xor, events): {rf['stream_read_gbps']} GB/s; "
+                     f"the decode kernel moves {rf['hbm_frac_of_stream_read']:.3f} of that rate")
+    srows = [r for r in rows if "stream_xor_kernel" in r["Name"]]
+    if srows:
+        lines.append(f"- rocprofv3 streaming-read kernel average: {float(srows[0]['AverageNs']) / 1e3:.1f} us "
+                     f"over {srows[0]['Calls']} dispatches")
     if args.plain_json:
         with open(args.plain_json) as f:
             plain = json.loads(f.read().strip().splitlines()[-1])
@@ -482,6 +503,9 @@ def summarize_trace(args):
                   + (f" ({100 * (pr['launch_us'] - avg) / avg:+.1f}% against rocprofv3's average)" if avg else ""),
                   f"- ms per step: {plain['ms_per_step']}",
                   f"- roofline: {pr['achieved']} {pr['unit']} of {pr['peak']} ({100 * pr['frac']:.1f}%), bound {pr['bound']}"]
+        if "stream_read_gbps" in pr:
+            lines.append(f"- streaming read of the same cache bytes: {pr['stream_read_gbps']} GB/s; the decode kernel "
+                         f"moves {pr['hbm_frac_of_stream_read']:.3f} of that rate")
     out = os.path.join(PROFILES, f"decode_kernels_{wl}.md")
     os.makedirs(PROFILES, exist_ok=True)
     with open(out, "w") as f:

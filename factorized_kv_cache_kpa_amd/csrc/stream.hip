@@ -16,16 +16,19 @@ __global__ void __launch_bounds__(kStreamThreads) stream_xor_kernel(const u32x4*
                                                                      int64_t share16, uint32_t* partial) {
     const int64_t lo = (int64_t)blockIdx.x * share16;
     const int64_t hi = min(lo + share16, n16);
+    constexpr int kRound = kStreamThreads * kStreamUnroll;
+    const int64_t full = hi > lo ? lo + (hi - lo) / kRound * kRound : lo;  // end of the whole rounds
     uint32_t acc = 0;
-    for (int64_t i = lo + threadIdx.x; i < hi; i += kStreamThreads * kStreamUnroll) {
+    for (int64_t i = lo + threadIdx.x; i < full; i += kRound) {
         u32x4 v[kStreamUnroll];
 #pragma unroll
-        for (int u = 0; u < kStreamUnroll; ++u) {
-            const int64_t k = i + u * kStreamThreads;
-            v[u] = k < hi ? __builtin_nontemporal_load(buf + k) : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int u = 0; u < kStreamUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * kStreamThreads);
 #pragma unroll
         for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+    for (int64_t i = full + threadIdx.x; i < hi; i += kStreamThreads) {  // the share's ragged end
+        const u32x4 v = __builtin_nontemporal_load(buf + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, x);
