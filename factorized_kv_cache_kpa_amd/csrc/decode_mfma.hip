@@ -155,6 +155,33 @@ __device__ __forceinline__ bf16x8 ld_f(const uint8_t* p) {
     else return ld16<bf16x8>(p);
 }
 
+// One wave's F factors of one tile in registers: key set (R_K ranks) and
+// value set (R_V ranks), KC 16-byte groups each.
+template <class S>
+struct FRegs {
+    bf16x8 fk[S::RK_][S::KC];
+    bf16x8 fv[S::RV_][S::KC];
+};
+
+// The F slice of wave iF: key-set lane (slot s, half) takes 8 features of
+// each 16-feature group; value-set lane (row l16, slot group g16) takes 8
+// slots of one feature row.
+template <class S>
+__device__ __forceinline__ void load_f_regs(const uint8_t* tile, int64_t offFK, int64_t offFV, int iF, int half, int s,
+                                            int l16, int g16, FRegs<S>& f) {
+    constexpr int PF = S::PF_, QF = S::QF_;
+#pragma unroll
+    for (int r = 0; r < S::RK_; ++r)
+#pragma unroll
+        for (int kc = 0; kc < S::KC; ++kc)
+            f.fk[r][kc] = ld_f<S>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + 2 * kc + half) * 512 + s * 16);
+#pragma unroll
+    for (int r = 0; r < S::RV_; ++r)
+#pragma unroll
+        for (int nb = 0; nb < S::KC; ++nb)
+            f.fv[r][nb] = ld_f<S>(tile + offFV + ((int64_t)((r * PF + iF) * QF + 16 * nb + l16) * 32 + 8 * g16) * 2);
+}
+
 // G32: convert the bf16 G factors of one tile (the DMA stage, layout as
 // above) to the float32 layout every wave reads.  Each thread takes 16-byte
 // chunks (8 values) of the stage; key chunk (c, slot) holds elements 8c ..
@@ -286,10 +313,38 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     }
 
     // One query per wave: the first tile goes in flight before the query is
-    // prepared (its latency hides the rotation's float64 arithmetic).  Its
-    // G blocks land in gbuf_a by DMA; its F slice is loaded into fa below,
-    // where the registers are declared.
+    // prepared (its latency hides the rotation's float64 arithmetic): its G
+    // blocks land in gbuf_a by DMA, its F slice in fa.  A dense query's
+    // elements (8 contiguous per lane and K step when F = B) are requested
+    // just before: loads complete in order, so the prologue's wait for them
+    // does not include the tile.
+    FRegs<S> fa, fb;
     constexpr bool kEarly = NQW == 1;
+    constexpr bool kQPre = kEarly && S::F_IS_B_;
+    f32x4 q_pre[MB32][KC][2];
+    int qpos_pre = 0;  // this thread's first rotary angle's query position
+    if constexpr (kEarly) {
+        const int e = threadIdx.x;
+        if (e < S::QPW * (S::QROT / 2))
+            qpos_pre = P.q_pos[(int64_t)b * P.n_q + min(qwg * S::QPW + e / (S::QROT / 2), P.n_q - 1)];
+    }
+    if constexpr (kQPre) {
+        if (P.a_q == nullptr) {
+            const int64_t qrow = (int64_t)b * P.n_q + min(n0, P.n_q - 1);
+#pragma unroll
+            for (int mb = 0; mb < MB32; ++mb) {
+                const int R = mb * 32 + s;
+                const bool row_ok = kFull32 || R < M;
+                const int iG = row_ok ? R / QG : 0, jG = row_ok ? R % QG : 0;
+                const float* src = P.q + (qrow * S::H + S::head(iG, iF)) * S::DH + S::feat(jG, 8 * half);
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    q_pre[mb][kc][0] = *reinterpret_cast<const f32x4*>(src + 16 * kc);
+                    q_pre[mb][kc][1] = *reinterpret_cast<const f32x4*>(src + 16 * kc + 4);
+                }
+            }
+        }
+    }
     int early_first = 0, early_last = 0;
     if constexpr (kEarly) {
         int vis_e = 0;
@@ -300,6 +355,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
             const uint8_t* tile = P.cache + (int64_t)b * L.n_tiles * L.tile_bytes +
                                   (int64_t)(early_first / kTileSlots) * L.tile_bytes;
             dma_g_blocks<S>(tile + L.off[S::SET_GK], tile + L.off[S::SET_GV], gbuf_a, wave, lane);
+            load_f_regs<S>(tile, L.off[S::SET_FK], L.off[S::SET_FV], iF, half, s, l16, g16, fa);
         }
     }
 
@@ -309,7 +365,8 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
         const int n = min(qwg * S::QPW + nq, P.n_q - 1);
         const double theta = exp2(-(2.0 * m / S::QROT) * log2((double)P.d.rope_base));
         double sn, c;
-        sincos((double)P.q_pos[(int64_t)b * P.n_q + n] * theta, &sn, &c);
+        const int qp = kEarly && e == (int)threadIdx.x ? qpos_pre : P.q_pos[(int64_t)b * P.n_q + n];
+        sincos((double)qp * theta, &sn, &c);
         cs_tab[nq][m][0] = (float)c;
         cs_tab[nq][m][1] = (float)sn;
     }
@@ -334,7 +391,15 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                 // same 8), (jG ^ 1, jF) when F = A
                 const int jF0 = 16 * kc + 8 * half;
                 float xs[8], ys[8];
-                query_group8<S>(P, qrow, iG, iF, jG, jF0, xs);
+                if (kQPre && P.a_q == nullptr) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        xs[k] = q_pre[mb][kc][0][k];
+                        xs[4 + k] = q_pre[mb][kc][1][k];
+                    }
+                } else {
+                    query_group8<S>(P, qrow, iG, iF, jG, jF0, xs);
+                }
                 if constexpr (!S::F_IS_B_) query_group8<S>(P, qrow, iG, iF, jG ^ 1, jF0, ys);
                 float v[8];
 #pragma unroll
@@ -400,21 +465,9 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     // At the top of each tile one wait for everything issued a tile earlier
     // and one barrier (all G blocks landed; the other buffer is free).
     constexpr int KB = S::GK_BLOCKS;
-    struct FRegs {
-        bf16x8 fk[RK][KC];
-        bf16x8 fv[RV][KC];
-    };
+    using FRegs = kpa::FRegs<S>;
     auto load_f = [&](const uint8_t* tile, FRegs& f) {
-#pragma unroll
-        for (int r = 0; r < RK; ++r)
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc)
-                f.fk[r][kc] = ld_f<S>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + 2 * kc + half) * 512 + s * 16);
-#pragma unroll
-        for (int r = 0; r < RV; ++r)
-#pragma unroll
-            for (int nb = 0; nb < KC; ++nb)
-                f.fv[r][nb] = ld_f<S>(tile + offFV + ((int64_t)((r * PF + iF) * QF + 16 * nb + l16) * 32 + 8 * g16) * 2);
+        load_f_regs<S>(tile, offFK, offFV, iF, half, s, l16, g16, f);
     };
     auto issue = [&](const uint8_t* tile, uint8_t* gdst, FRegs& f) {
         dma_g_blocks<S>(tile + offGK, tile + offGV, gdst, wave, lane);
@@ -635,11 +688,8 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
         else values(std::false_type{});
     };
 
-    FRegs fa, fb;
     const uint8_t* t0 = seq + (int64_t)(first / kTileSlots) * L.tile_bytes;
-    if constexpr (kEarly) {
-        if (first < last) load_f(t0, fa);  // the G blocks are on their way already
-    } else {
+    if constexpr (!kEarly) {
         if (first < last) issue(t0, gbuf_a, fa);
     }
     // Fused append (kpa_append_decode, single-query kernels; the host runs
