@@ -702,8 +702,13 @@ def sweep_flashtpa(args):
                 def decode():
                     kpa.kpa_decode(dims, cache, nb, ctx, ctx_len, ctx, q, q_pos, out, lse, ws)
 
-                for _ in range(3):
+                # at least 30 ms of calls before timing (clocks settle; no idle gap after)
+                t_w, n_w = time.perf_counter(), 0
+                while n_w < 3 or time.perf_counter() - t_w < 0.03:
                     decode()
+                    n_w += 1
+                    if n_w % 20 == 0:
+                        torch.cuda.synchronize()
                 reps = 10
                 kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
                 cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
