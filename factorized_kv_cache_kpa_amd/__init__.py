@@ -23,6 +23,12 @@ KPA_BF16 = 1
 KPA_DEV_SLOT_OUT_OF_RANGE = 1
 KPA_DEV_NEGATIVE_POSITION = 2
 KPA_DEV_CTX_OUT_OF_RANGE = 4
+# build limits (include/kpa.h)
+KPA_MAX_HEADS = 128
+KPA_MAX_HEAD_DIM = 256
+KPA_MAX_RANK = 16
+KPA_MAX_HD = 8192
+KPA_MAX_NQ = 64
 TILE_SLOTS = 32
 
 _lib = None

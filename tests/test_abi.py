@@ -185,3 +185,30 @@ def test_kernel_timing_hook_needs_both_events_or_none():
     st = lib.kpa_decode(ctypes.byref(dims), FAKE, 1, 64, FAKE, 128, FAKE, FAKE, FAKE, None, None, 0, 0, None, None)
     assert st != 0
     assert lib.kpa_time_next_decode_kernel(None, None) == 0
+
+
+def test_binding_constants_match_the_header():
+    import os
+    import re
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "kpa.h")).read()
+    defines = dict(re.findall(r"#define (KPA_\w+) (\d+)u?", text))
+    for name in ("KPA_MAX_HEADS", "KPA_MAX_HEAD_DIM", "KPA_MAX_RANK", "KPA_MAX_HD", "KPA_MAX_NQ",
+                 "KPA_DEV_SLOT_OUT_OF_RANGE", "KPA_DEV_NEGATIVE_POSITION", "KPA_DEV_CTX_OUT_OF_RANGE"):
+        assert int(defines[name]) == getattr(kpa, name), name
+
+
+def test_limits_are_enforced():
+    lib = kpa.load()
+    ok = kpa.make_dims(4, 8, 16, 16, kpa.KPA_MAX_RANK, kpa.KPA_MAX_RANK)  # h d_h = 8192 exactly
+    assert lib.kpa_cache_layout(ctypes.byref(ok), 1, 32, None) == -2  # dims accepted; then the NULL output
+    for bad in (kpa.make_dims(4, 8, 16, 16, kpa.KPA_MAX_RANK + 1, 1),   # rank
+                kpa.make_dims(16, 9, 8, 8, 1, 1),                        # h = 144 > 128
+                kpa.make_dims(2, 2, 32, 16, 1, 1),                       # d_h = 512 > 256
+                kpa.make_dims(8, 8, 16, 16, 1, 1)):                      # h d_h = 16384 > 8192
+        assert lib.kpa_cache_layout(ctypes.byref(bad), 1, 32, None) == -1
+    d = ctypes.byref(kpa.make_dims(4, 4, 8, 16, 2, 2))
+    big = 1 << 30
+    assert lib.kpa_decode_multiq(d, FAKE, 1, 64, FAKE, 64, kpa.KPA_MAX_NQ + 1, 1, FAKE, FAKE, FAKE, None, FAKE,
+                                 big, 0, None, None) == -7
+    assert lib.kpa_decode_multiq(d, FAKE, 1025, 64, FAKE, 64, 64, 1, FAKE, FAKE, FAKE, None, FAKE,
+                                 big, 0, None, None) == -7  # batch * n_q > 65535
