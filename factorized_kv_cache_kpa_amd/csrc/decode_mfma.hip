@@ -858,13 +858,15 @@ struct MfmaKernel {
 // (F = the factor with feature dimension 16, 32 or 64: B for the first three
 // and the last, A for the two multi-query shapes), R_K, R_V, F is B, queries
 // per wave, query subgroups, waves/SIMD, G factors converted to float32 in
-// LDS once per workgroup (the two shapes with the most G values per byte).
+// LDS once per workgroup (long_512k's shape: the most G values per byte; on
+// the multi-query shape the conversion measured no faster, needs 13 spilled
+// registers instead of 3, and some MI355X boxes ran it 10% slower).
 const MfmaKernel kKernels[] = {
     KPA_MFMA_ENTRY(4, 4, 8, 16, 2, 2, false, 4, 8, 4, 16, 2, 2, true, 1, 1, 3),
     KPA_MFMA_ENTRY(4, 4, 8, 16, 1, 1, false, 4, 8, 4, 16, 1, 1, true, 1, 1, 2),
     KPA_MFMA_ENTRY(8, 4, 8, 16, 2, 4, false, 8, 8, 4, 16, 2, 4, true, 1, 1, 2, true),
     KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, false, 8, 8, 4, 16, 4, 4, false, 1, 1, 1),
-    KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, true, 8, 8, 4, 16, 4, 4, false, 2, 2, 2, true),
+    KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, true, 8, 8, 4, 16, 4, 4, false, 2, 2, 2),
     // TPA split (A: h x 1, B: 1 x d_h): G = A with feature dimension 1, F = B
     KPA_MFMA_ENTRY(12, 1, 1, 64, 2, 2, false, 12, 1, 1, 64, 2, 2, true, 1, 1, 1),
     // FlashTPA's benchmark shapes: d_h = 64, R_K = R_V = 1, h = 16 / 32 / 48
