@@ -51,7 +51,7 @@ constexpr int kXcds = 8;  // workgroups are dealt to the 8 XCDs round-robin
 
 constexpr int pow2_at_least(int x) { return x <= 1 ? 1 : 2 * pow2_at_least((x + 1) / 2); }
 
-template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int NQW, int NQG, int MW, bool G32 = false>
+template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int NQW, int NQG, int MW>
 struct Cfg {
     static constexpr int PG_ = PG, QG_ = QG, PF_ = PF, QF_ = QF, RK_ = RK, RV_ = RV;
     static constexpr bool F_IS_B_ = F_IS_B;
@@ -80,16 +80,6 @@ struct Cfg {
     static constexpr int GK_BLOCKS = (GK_BYTES + 1023) / 1024;
     static constexpr int GV_BLOCKS = (GV_BYTES + 1023) / 1024;
     static constexpr int G_BLOCKS = GK_BLOCKS + GV_BLOCKS;
-    // G32: the waves convert each tile's G factors to float32 once, into a
-    // second LDS buffer that every wave then reads (instead of each wave
-    // unpacking the bf16 values itself).  Key set: element e, slot s at float
-    // ((e/4)*32 + s)*4 + e%4.  Value set: element row e of 32 slots (128 B);
-    // its 16-byte chunk c (slots 4c .. 4c+3) sits at chunk c ^ (e % 8).
-    static constexpr bool G32_ = G32;
-    static constexpr int GK32_BYTES = RK * M * 32 * 4;
-    static constexpr int GV32_BYTES = RV * M * 32 * 4;
-    static_assert(!G32 || (GK_BYTES % 1024 == 0 && GV_BYTES % 1024 == 0 && (RK * M) % 8 == 0),
-                  "the float32 staging takes whole DMA blocks of 8-element chunks");
     // softmax: NQW*PG (query, head) rows per wave, padded to a power of two,
     // spread over 64 lanes
     static constexpr int ROWS = NQW * PG;
@@ -182,44 +172,6 @@ __device__ __forceinline__ void load_f_regs(const uint8_t* tile, int64_t offFK, 
             f.fv[r][nb] = ld_f<S>(tile + offFV + ((int64_t)((r * PF + iF) * QF + 16 * nb + l16) * 32 + 8 * g16) * 2);
 }
 
-// G32: convert the bf16 G factors of one tile (the DMA stage, layout as
-// above) to the float32 layout every wave reads.  Each thread takes 16-byte
-// chunks (8 values) of the stage; key chunk (c, slot) holds elements 8c ..
-// 8c+7 of that slot, value chunk q of row e holds slots 8g .. 8g+7 with
-// g = q ^ ((e >> 1) & 3).  Consecutive threads write consecutive 16-byte
-// words (key set) or distinct chunks of two rows (value set): no bank
-// conflicts.
-template <class S>
-__device__ __forceinline__ void convert_g(const uint8_t* stage, uint8_t* g32) {
-    constexpr int NK = S::GK_BYTES / 16, N = NK + S::GV_BYTES / 16, T = S::WAVES * 64;
-#pragma unroll
-    for (int k = 0; k < (N + T - 1) / T; ++k) {
-        const int idx = (int)threadIdx.x + k * T;
-        if (N % T != 0 && idx >= N) break;
-        const u32x4 u = *reinterpret_cast<const u32x4*>(stage + idx * 16);
-        f32x4 lo, hi;
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-            lo[2 * w] = __uint_as_float(u[w] << 16);
-            lo[2 * w + 1] = __uint_as_float(u[w] & 0xffff0000u);
-            hi[2 * w] = __uint_as_float(u[2 + w] << 16);
-            hi[2 * w + 1] = __uint_as_float(u[2 + w] & 0xffff0000u);
-        }
-        uint8_t *d0, *d1;
-        if (idx < NK) {
-            d0 = g32 + (idx >> 5) * 1024 + (idx & 31) * 16;
-            d1 = d0 + 512;
-        } else {
-            const int j = idx - NK, e = j >> 2, g = (j & 3) ^ ((e >> 1) & 3);
-            uint8_t* row = g32 + S::GK32_BYTES + e * 128;
-            d0 = row + (((2 * g) ^ (e & 7)) * 16);
-            d1 = row + (((2 * g + 1) ^ (e & 7)) * 16);
-        }
-        *reinterpret_cast<f32x4*>(d0) = lo;
-        *reinterpret_cast<f32x4*>(d1) = hi;
-    }
-}
-
 // Query elements (iG, iF, jG, jF0 .. jF0 + 7) of row `row`, unrotated.  Dense:
 // two 16-byte loads.  Factored ((1/R_Q) sum_r A^Q_r (x) B^Q_r): per rank one
 // element of the G-side factor times 8 consecutive elements of the F-side
@@ -278,9 +230,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     // two separate LDS objects (not one 2-D array) so the compiler can tell the
     // buffer being filled by DMA from the one being read
     __shared__ __attribute__((aligned(1024))) uint8_t gbuf_a[S::G_BLOCKS * 1024];
-    // with G32, gbuf_a is the bf16 stage and gbuf_b the float32 copy
-    __shared__ __attribute__((aligned(1024))) uint8_t gbuf_b[S::G32_ ? S::GK32_BYTES + S::GV32_BYTES
-                                                                     : S::G_BLOCKS * 1024];
+    __shared__ __attribute__((aligned(1024))) uint8_t gbuf_b[S::G_BLOCKS * 1024];
 
     const int lane = threadIdx.x & 63;
     const int wave = S::WAVES == 1 ? 0 : (int)(threadIdx.x >> 6);
@@ -499,14 +449,8 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                     const int R0 = mb * 32 + 8 * a + 4 * half;
                     if (kFull32 || R0 < M) {
                         const int e0 = r * M + R0;  // four consecutive elements in one 16-byte chunk
-                        if constexpr (S::G32_) {
-                            const f32x4 gk = *reinterpret_cast<const f32x4*>(gcur + ((e0 >> 2) * 32 + s) * 16);
-#pragma unroll
-                            for (int bb = 0; bb < 4; ++bb) g[a][bb] = gk[bb];
-                        } else {
-                            const uint2 gk = *reinterpret_cast<const uint2*>(gcur + (e0 >> 3) * 512 + s * 16 + (e0 & 7) * 2);
-                            unpack_bf16x4(gk, g[a][0], g[a][1], g[a][2], g[a][3]);
-                        }
+                        const uint2 gk = *reinterpret_cast<const uint2*>(gcur + (e0 >> 3) * 512 + s * 16 + (e0 & 7) * 2);
+                        unpack_bf16x4(gk, g[a][0], g[a][1], g[a][2], g[a][3]);
                     } else {
                         g[a][0] = g[a][1] = g[a][2] = g[a][3] = 0.f;
                     }
@@ -652,18 +596,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                     float gvf[8];
                     if (row_ok) {
                         const int e = r * M + R_row;  // element row of the value set
-                        if constexpr (S::G32_) {
-                            const uint8_t* vrow = gcur + S::GK32_BYTES + e * 128;
-                            const f32x4 lo = *reinterpret_cast<const f32x4*>(vrow + (((2 * g16) ^ (e & 7)) * 16));
-                            const f32x4 hi = *reinterpret_cast<const f32x4*>(vrow + (((2 * g16 + 1) ^ (e & 7)) * 16));
-#pragma unroll
-                            for (int k = 0; k < 4; ++k) {
-                                gvf[k] = lo[k];
-                                gvf[4 + k] = hi[k];
-                            }
-                        } else {
-                            unpack_bf16x8(*reinterpret_cast<const bf16x8*>(gvbase + e * 64 + ((g16 ^ ((e >> 1) & 3)) * 16)), gvf);
-                        }
+                        unpack_bf16x8(*reinterpret_cast<const bf16x8*>(gvbase + e * 64 + ((g16 ^ ((e >> 1) & 3)) * 16)), gvf);
                     } else {
 #pragma unroll
                         for (int k = 0; k < 8; ++k) gvf[k] = 0.f;
@@ -726,34 +659,6 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
             }
         }
     }
-    if constexpr (S::G32_) {
-        // One bf16 stage (gbuf_a) and one float32 copy (gbuf_b).  Per tile:
-        // wait for the tile's loads; barrier (stage complete, every wave done
-        // reading the previous copy); issue the next tile's F loads (their
-        // registers are free), so that bytes stay in flight while the waves
-        // convert; convert; barrier (copy complete, stage free); issue the
-        // next tile's G DMA; compute.
-        auto stage_tile = [&](const uint8_t* next, FRegs& fnext) {
-            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            if (next) load_f(next, fnext);
-            convert_g<S>(gbuf_a, gbuf_b);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            if (next) dma_g_blocks<S>(next + offGK, next + offGV, gbuf_a, wave, lane);
-        };
-        for (int s0 = first; s0 < last; s0 += 2 * kTileSlots) {
-            const uint8_t* tile = seq + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
-            stage_tile(s0 + kTileSlots < last ? tile + L.tile_bytes : nullptr, fb);
-            process(s0, gbuf_b, fa);
-            if (s0 + kTileSlots >= last) break;
-            stage_tile(s0 + 2 * kTileSlots < last ? tile + 2 * L.tile_bytes : nullptr, fa);
-            process(s0 + kTileSlots, gbuf_b, fb);
-        }
-    } else
     for (int s0 = first; s0 < last; s0 += 2 * kTileSlots) {
         // tile s0: data in gbuf_a and fa
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the DMA and loads issued one tile ago
@@ -857,14 +762,11 @@ struct MfmaKernel {
 // Shapes with a matrix-core instantiation.  Cfg arguments: PG, QG, PF, QF
 // (F = the factor with feature dimension 16, 32 or 64: B for the first three
 // and the last, A for the two multi-query shapes), R_K, R_V, F is B, queries
-// per wave, query subgroups, waves/SIMD, G factors converted to float32 in
-// LDS once per workgroup (long_512k's shape: the most G values per byte; on
-// the multi-query shape the conversion measured no faster, needs 13 spilled
-// registers instead of 3, and some MI355X boxes ran it 10% slower).
+// per wave, query subgroups, waves/SIMD.
 const MfmaKernel kKernels[] = {
     KPA_MFMA_ENTRY(4, 4, 8, 16, 2, 2, false, 4, 8, 4, 16, 2, 2, true, 1, 1, 3),
     KPA_MFMA_ENTRY(4, 4, 8, 16, 1, 1, false, 4, 8, 4, 16, 1, 1, true, 1, 1, 2),
-    KPA_MFMA_ENTRY(8, 4, 8, 16, 2, 4, false, 8, 8, 4, 16, 2, 4, true, 1, 1, 2, true),
+    KPA_MFMA_ENTRY(8, 4, 8, 16, 2, 4, false, 8, 8, 4, 16, 2, 4, true, 1, 1, 2),
     KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, false, 8, 8, 4, 16, 4, 4, false, 1, 1, 1),
     KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, true, 8, 8, 4, 16, 4, 4, false, 2, 2, 2),
     // TPA split (A: h x 1, B: 1 x d_h): G = A with feature dimension 1, F = B
