@@ -265,9 +265,11 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
     // One query per wave: the first tile goes in flight before the query is
     // prepared (its latency hides the rotation's float64 arithmetic): its G
     // blocks land in gbuf_a by DMA, its F slice in fa.  A dense query's
-    // elements (8 contiguous per lane and K step when F = B) are requested
-    // just before: loads complete in order, so the prologue's wait for them
-    // does not include the tile.
+    // elements (8 contiguous per lane and K step when F = B) and the query
+    // positions are requested just before.  Loads complete in order, so the
+    // prologue's wait for them need not cover the F loads; it still covers
+    // the G blocks, whose inline-asm DMA the compiler's wait counts cannot
+    // see.
     FRegs<S> fa, fb;
     constexpr bool kEarly = NQW == 1;
     constexpr bool kQPre = kEarly && S::F_IS_B_;
