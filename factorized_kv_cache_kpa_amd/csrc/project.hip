@@ -28,6 +28,69 @@
 namespace kpa {
 namespace {
 
+// Epilogue shared by both kernels: four consecutive stacked rows fb .. fb+3
+// (fb a multiple of 4) of one token (sequence b, cache slot `slot`, position
+// pos) go to the cache.  Stacked rows: B^K [0, n1), A^K [n1, n10), A^V
+// [n10, n102), B^V [n102, F).  A B^K row pair (even, odd) is rotated in
+// float64 ([KPA] Def. 2.3) and every value is rounded once to the cache type.
+// The recorder lane (one per token) writes the position and reports a slot
+// out of range or a negative position; such a token is not stored.
+template <bool kF32>
+__device__ __forceinline__ void store_rows4(const ProjectParams& P, int b, int slot, int pos, int fb, const float* v,
+                                            bool recorder) {
+    if (slot < 0 || slot >= P.capacity || pos < 0) {
+        if (recorder && P.dev_status) {
+            uint32_t bits = 0;
+            if (slot < 0 || slot >= P.capacity) bits |= KPA_DEV_SLOT_OUT_OF_RANGE;
+            if (pos < 0) bits |= KPA_DEV_NEGATIVE_POSITION;
+            atomicOr(P.dev_status, bits);
+        }
+        return;
+    }
+    const Layout& L = P.L;
+    const int F = P.n_feat;
+    uint8_t* tile_base = P.cache + ((int64_t)b * L.n_tiles + slot / kTileSlots) * L.tile_bytes;
+    const int ts = slot % kTileSlots;
+    const int n1 = L.elems[1], n10 = n1 + L.elems[0], n102 = n10 + L.elems[2];
+    const int q2 = P.d.q2;
+    const double log2_base = log2((double)P.d.rope_base);
+    auto put = [&](int c, int e, float val) {
+        if constexpr (kF32)
+            store_elem<float>(tile_base + elem_offset(L, c, e, ts), val);
+        else
+            store_elem<uint16_t>(tile_base + elem_offset(L, c, e, ts), f32_to_bf16_rne(val));
+    };
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int fr = fb + j;
+        if (fr >= F) break;
+        if (fr < n1) {
+            // B^K: rows fr (even) and fr + 1 form one RoPE pair (n1 is even)
+            if (j % 2 == 0) {
+                double y0, y1;
+                rope_pair((double)v[j], (double)v[j + 1], pos, (fr % q2) / 2, q2, log2_base, y0, y1);
+                if constexpr (kF32) {
+                    store_elem<float>(tile_base + elem_offset(L, 1, fr, ts), (float)y0);
+                    store_elem<float>(tile_base + elem_offset(L, 1, fr + 1, ts), (float)y1);
+                } else {
+                    store_elem<uint16_t>(tile_base + elem_offset(L, 1, fr, ts), f64_to_bf16_rne(y0));
+                    store_elem<uint16_t>(tile_base + elem_offset(L, 1, fr + 1, ts), f64_to_bf16_rne(y1));
+                }
+            }
+        } else if (fr < n10) {
+            put(0, fr - n1, v[j]);
+        } else if (fr < n102) {
+            put(2, fr - n10, v[j]);
+        } else {
+            put(3, fr - n102, v[j]);
+        }
+    }
+    if (recorder) {
+        int32_t* positions = reinterpret_cast<int32_t*>(P.cache + L.positions_off);
+        positions[(int64_t)b * L.n_tiles * kTileSlots + slot] = pos;
+    }
+}
+
 template <bool kF32, int NW>
 __global__ void __launch_bounds__(NW * 64) project_append_kernel(ProjectParams P) {
     __shared__ float part[NW][16][64];
@@ -96,60 +159,140 @@ __global__ void __launch_bounds__(NW * 64) project_append_kernel(ProjectParams P
         v[j] = s;
     }
     if (!t_ok) return;
-    const int b = tb;
     // one lane per token reports and records (the workgroup of the first rows)
-    const bool recorder = blockIdx.x == 0 && wave == 0 && hi == 0;
-    if (slot < 0 || slot >= P.capacity || pos < 0) {
-        if (recorder && P.dev_status) {
-            uint32_t bits = 0;
-            if (slot < 0 || slot >= P.capacity) bits |= KPA_DEV_SLOT_OUT_OF_RANGE;
-            if (pos < 0) bits |= KPA_DEV_NEGATIVE_POSITION;
-            atomicOr(P.dev_status, bits);
-        }
-        return;
-    }
-    const Layout& L = P.L;
-    uint8_t* tile_base = P.cache + ((int64_t)b * L.n_tiles + slot / kTileSlots) * L.tile_bytes;
-    const int ts = slot % kTileSlots;
-    // stacked rows: B^K [0, n1), A^K [n1, n10), A^V [n10, n102), B^V [n102, F)
-    const int n1 = L.elems[1], n10 = n1 + L.elems[0], n102 = n10 + L.elems[2];
-    const int q2 = P.d.q2;
-    const double log2_base = log2((double)P.d.rope_base);
-    const int fb = blockIdx.x * 32 + 8 * wave + 4 * hi;  // row of v[0]; a multiple of 4
-    auto put = [&](int c, int e, float val) {
-        if constexpr (kF32)
-            store_elem<float>(tile_base + elem_offset(L, c, e, ts), val);
-        else
-            store_elem<uint16_t>(tile_base + elem_offset(L, c, e, ts), f32_to_bf16_rne(val));
-    };
+    store_rows4<kF32>(P, tb, slot, pos, blockIdx.x * 32 + 8 * wave + 4 * hi, v,
+                      blockIdx.x == 0 && wave == 0 && hi == 0);
+}
+
+// Prefill-sized token counts: an LDS-tiled GEMM.  One workgroup (4 waves)
+// computes 128 stacked rows x 128 tokens, d_model in steps of 64.  Each step's
+// operands (128 weight rows and 128 token rows of 64 bf16, 16 KB each) go
+// HBM -> LDS by direct DMA, double-buffered, one step ahead; wave (wm, wn)
+// then multiplies its 64 x 64 quarter as 2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16, operands read from LDS.  In LDS a row is 128 B
+// (eight 16-byte chunks); chunk c of row r sits at position c ^ ((r >> 1) & 7)
+// so that the 32 rows one operand read touches spread over the banks (the
+// DMA lane that fills a position fetches the chunk that belongs there).
+// Rows past F and tokens past the end read the last valid row; their
+// outputs are not stored.  The epilogue is the small kernel's.
+constexpr int kTB = 128;   // rows and tokens per workgroup
+constexpr int kTK = 64;    // d_model per step
+constexpr int kTileOpBytes = kTB * kTK * 2;
+constexpr int kTiledMinTokens = 1024;
+constexpr int kXcdCount = 8;  // MI355X: workgroups dealt to 8 XCDs round-robin
+
+template <bool kF32>
+__global__ void __launch_bounds__(256, 2) project_tiled_kernel(ProjectParams P) {
+    // two steps' operands; after the GEMM, the 128 x 128 float32 result tile
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kTileOpBytes];
+    uint8_t* const sa0 = lds;
+    uint8_t* const sa1 = lds + kTileOpBytes;
+    uint8_t* const sb0 = lds + 2 * kTileOpBytes;
+    uint8_t* const sb1 = lds + 3 * kTileOpBytes;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int F = P.n_feat, T = P.n_tok, K = P.d_model;
+    // Workgroup -> (row tile, token tile), XCD-aware: the hardware deals
+    // workgroup L to XCD L % 8, and XCD x takes a contiguous range of the work
+    // items, token tile major, row tile minor.  The row tiles of one token
+    // tile then run side by side on one XCD and read its token rows through
+    // that XCD's L2, not once per row tile from HBM.
+    const int n_rt = (F + kTB - 1) / kTB, n_tt = (T + kTB - 1) / kTB;
+    const int total = n_rt * n_tt, xcd = blockIdx.x % kXcdCount, k_in = blockIdx.x / kXcdCount;
+    const int item = xcd * (total / kXcdCount) + min(xcd, total % kXcdCount) + k_in;
+    const int f0 = (item % n_rt) * kTB, t0 = (item / n_rt) * kTB;
+
+    // DMA plan: 16 instructions of 1 KB per operand and step, 4 per wave; the
+    // instruction d fills rows 8d .. 8d+7, lane i row 8d + i/8, position i%8
+    const uint8_t* arow[4];
+    const uint8_t* brow[4];
+    int chunk[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int fr = fb + j;
-        if (fr >= F) break;
-        if (fr < n1) {
-            // B^K: rows fr (even) and fr + 1 form one RoPE pair (n1 is even)
-            if (j % 2 == 0) {
-                double y0, y1;
-                rope_pair((double)v[j], (double)v[j + 1], pos, (fr % q2) / 2, q2, log2_base, y0, y1);
-                if constexpr (kF32) {
-                    store_elem<float>(tile_base + elem_offset(L, 1, fr, ts), (float)y0);
-                    store_elem<float>(tile_base + elem_offset(L, 1, fr + 1, ts), (float)y1);
-                } else {
-                    store_elem<uint16_t>(tile_base + elem_offset(L, 1, fr, ts), f64_to_bf16_rne(y0));
-                    store_elem<uint16_t>(tile_base + elem_offset(L, 1, fr + 1, ts), f64_to_bf16_rne(y1));
-                }
-            }
-        } else if (fr < n10) {
-            put(0, fr - n1, v[j]);
-        } else if (fr < n102) {
-            put(2, fr - n10, v[j]);
-        } else {
-            put(3, fr - n102, v[j]);
-        }
+    for (int u = 0; u < 4; ++u) {
+        const int d = wave * 4 + u, r = 8 * d + (lane >> 3);
+        chunk[u] = (lane & 7) ^ ((r >> 1) & 7);
+        arow[u] = reinterpret_cast<const uint8_t*>(P.w + (int64_t)min(f0 + r, F - 1) * K);
+        brow[u] = reinterpret_cast<const uint8_t*>(P.x + (int64_t)min(t0 + r, T - 1) * K);
     }
-    if (recorder) {
-        int32_t* positions = reinterpret_cast<int32_t*>(P.cache + L.positions_off);
-        positions[(int64_t)b * L.n_tiles * kTileSlots + slot] = pos;
+    auto issue = [&](int k0, uint8_t* sa, uint8_t* sb) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int d = wave * 4 + u;
+            dma_to_lds16(arow[u] + (int64_t)k0 * 2 + chunk[u] * 16, lds_addr(sa + d * 1024));
+            dma_to_lds16(brow[u] + (int64_t)k0 * 2 + chunk[u] * 16, lds_addr(sb + d * 1024));
+        }
+    };
+
+    // the epilogue's token of this thread (t0 + threadIdx.x % 128): its slot
+    // and position are read now, their latency hidden by the GEMM
+    const int tk = threadIdx.x % kTB, t_ep = t0 + tk;
+    const bool t_ok = t_ep < T;
+    const int tb = t_ok ? t_ep / P.n_new : 0;
+    const int slot = t_ok ? P.slot0[tb] + t_ep % P.n_new : -1;
+    const int pos = t_ok ? P.positions[t_ep] : -1;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    // operand reads: row m of a block, chunk kc (0 .. 7) of the step
+    auto rd = [&](const uint8_t* buf, int m, int kc) {
+        return ld_lds16(reinterpret_cast<const uint16_t*>(buf + m * 128 + ((kc ^ ((m >> 1) & 7)) * 16)));
+    };
+    auto compute = [&](const uint8_t* sa, const uint8_t* sb) {
+#pragma unroll
+        for (int kk = 0; kk < kTK / 16; ++kk) {
+            const int kc = 2 * kk + hi;  // this lane's 8 of the step's 16
+            bf16x8 a[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = rd(sa, wm * 64 + 32 * i + l32, kc);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bv[j] = rd(sb, wn * 64 + 32 * j + l32, kc);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bv[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    const int nk = K / kTK;
+    issue(0, sa0, sb0);
+    for (int kt = 0; kt < nk; kt += 2) {
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this step's DMA
+        __syncthreads();                     // ... every wave's; the other buffers are free
+        if (kt + 1 < nk) issue((kt + 1) * kTK, sa1, sb1);
+        compute(sa0, sb0);
+        if (kt + 1 >= nk) break;
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();
+        if (kt + 2 < nk) issue((kt + 2) * kTK, sa0, sb0);
+        compute(sa1, sb1);
+    }
+
+    // epilogue through LDS: block (i, j) register r holds row 32 i + 8 (r / 4)
+    // + 4 hi + r % 4 of the wave's quarter, for token column 32 j + lane % 32
+    __syncthreads();  // every wave is done with the last step's operands
+    float* const tile = reinterpret_cast<float*>(lds);  // [128 rows][128 tokens]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                tile[(wm * 64 + 32 * i + 8 * (r / 4) + 4 * hi + r % 4) * kTB + wn * 64 + 32 * j + l32] = acc[i][j][r];
+    __syncthreads();
+    if (!t_ok) return;
+    // each thread: its token, row groups 4g .. 4g+3 for g = threadIdx.x / 128, +2, ...
+#pragma unroll 1
+    for (int g = threadIdx.x / kTB; g < kTB / 4; g += 256 / kTB) {
+        const int fb = f0 + 4 * g;
+        if (fb >= F) break;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = tile[(4 * g + r) * kTB + tk];
+        store_rows4<kF32>(P, tb, slot, pos, fb, v, f0 == 0 && g == 0);
     }
 }
 
@@ -165,7 +308,18 @@ void launch_nw(const ProjectParams& P, hipStream_t s, const KernelEvents& ev) {
 }  // namespace
 
 // d_model is a multiple of 64; each wave's share must be a multiple of 16.
+// From 1024 tokens on, the LDS-tiled kernel (a 128 x 128 tile per
+// workgroup); below, the small kernel, whose 32 x 32 tiles give enough
+// workgroups at decode-step token counts.
 hipError_t launch_project_append(const ProjectParams& P, hipStream_t s, const KernelEvents& ev) {
+    if (P.n_tok >= kTiledMinTokens) {
+        const dim3 grid(((P.n_feat + kTB - 1) / kTB) * ((P.n_tok + kTB - 1) / kTB));
+        if (P.d.dtype == KPA_F32)
+            hipExtLaunchKernelGGL(project_tiled_kernel<true>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, P);
+        else
+            hipExtLaunchKernelGGL(project_tiled_kernel<false>, grid, dim3(256), 0, s, ev.start, ev.stop, 0, P);
+        return hipGetLastError();
+    }
     if (P.d_model % (16 * 16) == 0 && P.d_model >= 1024)
         launch_nw<16>(P, s, ev);
     else if (P.d_model % (8 * 16) == 0 && P.d_model >= 512)

@@ -2,8 +2,10 @@
 ([KPA] Eq. (5), one stacked weight) written straight into the cache, against
 the float64 oracle's projection and rotation.
 
-Each stored value must lie within half a unit in the last place of the cache
-type (bf16: 8 significant bits) plus the float32 accumulation bound
+Decode-step token counts run the small kernel (32 x 32 tiles); from 1024
+tokens on, the LDS-tiled one.  Each stored value must lie within half a unit
+in the last place of the cache type (bf16: 8 significant bits) plus the
+float32 accumulation bound
 d_model * 2^-24 * sum_c |w x| of the exact float64 value.  Slots the call does
 not own stay untouched, positions are recorded, and an out-of-range slot is
 flagged and skipped.  An end-to-end case decodes over a projected cache and
@@ -59,6 +61,12 @@ SHAPES = [
     ("tpa_degenerate", 16, 1, 768, 32),  # 304 factor rows: a partial row block
     ("tiny_f32", 2, 7, 64, 16),          # float32 cache
     ("flashtpa_h48", 3, 2, 3072, 36),
+    # from 1024 tokens on, the LDS-tiled kernel (128 rows x 128 tokens per workgroup)
+    ("kpa_32k", 4, 600, 2048, 640),      # 2400 tokens: a ragged token tile
+    ("tpa_degenerate", 3, 700, 768, 704),  # F = 304: a partial row tile
+    ("tiny_f32", 2, 600, 64, 640),       # float32 cache, one d_model step, F = 64
+    ("long_512k", 1, 1024, 4096, 1024),  # exactly the threshold
+    ("multiq_16", 1, 1030, 4096, 1040),
 ]
 
 
@@ -128,13 +136,14 @@ def test_out_of_range_slot_is_flagged_and_skipped(gpu_lib):
     assert torch.equal(cache, before)
 
 
-def test_decode_over_a_projected_cache_matches_oracle(gpu_lib):
+@pytest.mark.parametrize("ctx", [300, 600])  # 600 tokens, 1200 in all: the tiled kernel
+def test_decode_over_a_projected_cache_matches_oracle(gpu_lib, ctx):
     """End to end: every context token projected from its hidden state into
     the cache, then the decode; the oracle decodes the float64 projected
     factors (the cache rounds them once to bf16, 2^-9 relative)."""
     cfg = CONFIGS["kpa_32k"]
     dims = dims_of(cfg)
-    batch, ctx, d_model = 2, 300, 512
+    batch, d_model = 2, 512
     x, w = _inputs(cfg, batch, ctx, d_model, seed=44)
     positions = torch.arange(ctx, dtype=torch.int32).repeat(batch, 1).contiguous()
     cache = kpa.alloc_cache(dims, batch, ctx)
@@ -142,7 +151,7 @@ def test_decode_over_a_projected_cache_matches_oracle(gpu_lib):
                            torch.zeros(batch, dtype=torch.int32).cuda(), n_new=ctx)
     g = torch.Generator().manual_seed(45)
     q = torch.randn((batch, 1, cfg.h, cfg.d_h), generator=g)
-    ctx_len = torch.tensor([ctx, 217], dtype=torch.int32)
+    ctx_len = torch.tensor([ctx, ctx - 83], dtype=torch.int32)
     q_pos = (ctx_len - 1).view(batch, 1).to(torch.int32)
     out = torch.empty((batch, cfg.h, cfg.d_h), device="cuda")
     lse = torch.empty((batch, cfg.h), device="cuda")
