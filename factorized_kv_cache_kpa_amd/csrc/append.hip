@@ -1,10 +1,21 @@
-// kpa_cache_append kernel: one block per (new token, sequence) writes the
-// token's factors into the tiled cache (B^K rotated at write time; the
-// per-token work and its citations are in kpa_append.hpp).
+// kpa_cache_append kernels (B^K rotated at write time; the per-token work
+// and its citations are in kpa_append.hpp).
+//  * append_tile_kernel: one workgroup per (32-slot cache tile, sequence) the
+//    new tokens touch.  The float64 angle of each (token, rotary pair index)
+//    is computed once (a B^K row of every rank and head row shares it), the
+//    feature-chunk sets are written as whole 16-byte chunks and the value
+//    sets slot-contiguous, so a bulk append streams at memory speed.
+//  * append_kernel: one workgroup per (new token, sequence); for q2 > 64,
+//    whose angle table would not fit the tile kernel's LDS.
+// Both write the same bytes: the elements of the new tokens' slots and their
+// positions (never the padding of a chunk), with the same float64 rotation.
 #include "kpa_append.hpp"
 
 namespace kpa {
 namespace {
+
+constexpr int kMaxTilePairs = 32;  // q2 / 2 the tile kernel's angle table holds
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 template <bool kF32>
 __global__ void __launch_bounds__(256) append_kernel(AppendParams P) {
@@ -12,10 +23,130 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams P) {
                        blockDim.x);
 }
 
+__device__ __forceinline__ int floor_div32(int x) {
+    return x >= 0 ? x / kTileSlots : -((-x + kTileSlots - 1) / kTileSlots);
+}
+
+template <bool kF32>
+__global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
+    using E = typename std::conditional<kF32, float, uint16_t>::type;
+    constexpr int PC = kChunkBytes / (int)sizeof(E);  // elements per 16-byte chunk
+    __shared__ double cs_tab[kTileSlots][kMaxTilePairs], sn_tab[kTileSlots][kMaxTilePairs];
+    __shared__ int pos_s[kTileSlots];
+    __shared__ int ok_s[kTileSlots];
+    const AppendInputs& in = P.in;
+    const Layout& L = P.L;
+    const int b = blockIdx.y;
+    const int s0 = in.slot0[b];
+    const int tile = floor_div32(s0) + (int)blockIdx.x;
+    const int base = tile * kTileSlots;  // slot of position 0 of this tile
+    // new tokens n in [n_lo, n_hi) fall in this tile, at t = s0 + n - base
+    const int n_lo = max(0, base - s0), n_hi = min(in.n_new, base + kTileSlots - s0);
+    if (n_lo >= n_hi) return;
+    const int tid = threadIdx.x;
+    if (tid < kTileSlots) {
+        const int n = base + tid - s0;
+        const bool mine = n >= n_lo && n < n_hi;
+        const int slot = base + tid;
+        const int pos = mine ? in.positions[(int64_t)b * in.n_new + n] : -1;
+        const bool ok = mine && slot >= 0 && slot < P.capacity && pos >= 0;
+        if (mine && !ok && P.dev_status) {
+            uint32_t bits = 0;
+            if (slot < 0 || slot >= P.capacity) bits |= KPA_DEV_SLOT_OUT_OF_RANGE;
+            if (pos < 0) bits |= KPA_DEV_NEGATIVE_POSITION;
+            atomicOr(P.dev_status, bits);
+        }
+        pos_s[tid] = pos;
+        ok_s[tid] = ok;
+    }
+    __syncthreads();
+    const int q2 = P.d.q2, half = q2 / 2;
+    const double log2_base = log2((double)P.d.rope_base);
+    for (int i = tid; i < kTileSlots * half; i += blockDim.x) {
+        const int t = i / half, m = i % half;
+        if (ok_s[t]) rope_angle(pos_s[t], m, q2, log2_base, sn_tab[t][m], cs_tab[t][m]);
+    }
+    __syncthreads();
+    if (tile < 0 || tile >= L.n_tiles) return;  // (then no token of it is ok)
+    uint8_t* tb = P.cache + ((int64_t)b * L.n_tiles + tile) * L.tile_bytes;
+    const int64_t tok0 = (int64_t)b * in.n_new + (base - s0);  // token index of position 0 of the tile
+
+    // feature-chunk sets: A^K copied, B^K rotated; one (chunk, slot) per step
+    for (int c = 0; c < 2; ++c) {
+        const int ne = L.elems[c], nch = (ne + PC - 1) / PC;
+        const E* src = reinterpret_cast<const E*>(c == 0 ? in.a_k : in.b_k);
+        for (int u = tid; u < nch * kTileSlots; u += blockDim.x) {
+            const int cc = u / kTileSlots, t = u % kTileSlots;
+            if (!ok_s[t]) continue;
+            const E* from = src + (tok0 + t) * ne + cc * PC;
+            const int cnt = min(PC, ne - cc * PC);
+            E v[PC];
+#pragma unroll
+            for (int k = 0; k < PC; ++k) v[k] = k < cnt ? from[k] : E(0);
+            if (c == 1) {
+                // pairs (2j, 2j+1) of the chunk; a chunk starts on a pair (PC even)
+#pragma unroll
+                for (int k = 0; k < PC; k += 2) {
+                    if (k >= cnt) break;
+                    const int m = ((cc * PC + k) % q2) / 2;
+                    double x0, x1;
+                    if constexpr (kF32) {
+                        x0 = v[k];
+                        x1 = v[k + 1];
+                    } else {
+                        x0 = bf16_to_f32(v[k]);
+                        x1 = bf16_to_f32(v[k + 1]);
+                    }
+                    double y0, y1;
+                    rope_rotate(x0, x1, sn_tab[t][m], cs_tab[t][m], y0, y1);
+                    if constexpr (kF32) {
+                        v[k] = (float)y0;
+                        v[k + 1] = (float)y1;
+                    } else {
+                        v[k] = f64_to_bf16_rne(y0);
+                        v[k + 1] = f64_to_bf16_rne(y1);
+                    }
+                }
+            }
+            uint8_t* to = tb + L.off[c] + (int64_t)cc * (kTileSlots * kChunkBytes) + t * kChunkBytes;
+            if (cnt == PC) {
+                *reinterpret_cast<u32x4_t*>(to) = __builtin_bit_cast(u32x4_t, v);
+            } else {
+#pragma unroll
+                for (int k = 0; k < PC; ++k)
+                    if (k < cnt) store_elem<E>(to + k * sizeof(E), v[k]);
+            }
+        }
+    }
+    // value-format sets (A^V, B^V): element rows of 32 slots
+    for (int c = 2; c < 4; ++c) {
+        const int ne = L.elems[c];
+        const E* src = reinterpret_cast<const E*>(c == 2 ? in.a_v : in.b_v);
+        for (int u = tid; u < ne * kTileSlots; u += blockDim.x) {
+            const int e = u / kTileSlots, t = u % kTileSlots;
+            if (ok_s[t])
+                store_elem<E>(tb + L.off[c] + ((int64_t)e * kTileSlots + t) * sizeof(E), src[(tok0 + t) * ne + e]);
+        }
+    }
+    if (tid < kTileSlots && ok_s[tid]) {
+        int32_t* positions = reinterpret_cast<int32_t*>(P.cache + L.positions_off);
+        positions[(int64_t)b * L.n_tiles * kTileSlots + base + tid] = pos_s[tid];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_append(const AppendParams& P, hipStream_t s) {
-    dim3 grid(P.in.n_new, P.batch);
+    if (P.d.q2 / 2 <= kMaxTilePairs) {
+        // the new tokens of a sequence touch at most ceil(n_new / 32) + 1 tiles
+        const dim3 grid((P.in.n_new + kTileSlots - 1) / kTileSlots + 1, P.batch);
+        if (P.d.dtype == KPA_F32)
+            hipLaunchKernelGGL(append_tile_kernel<true>, grid, dim3(256), 0, s, P);
+        else
+            hipLaunchKernelGGL(append_tile_kernel<false>, grid, dim3(256), 0, s, P);
+        return hipGetLastError();
+    }
+    const dim3 grid(P.in.n_new, P.batch);
     if (P.d.dtype == KPA_F32)
         hipLaunchKernelGGL(append_kernel<true>, grid, dim3(256), 0, s, P);
     else

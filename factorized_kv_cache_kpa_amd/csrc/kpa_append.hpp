@@ -20,15 +20,28 @@ namespace kpa {
 template <typename T>
 __device__ __forceinline__ void store_elem(uint8_t* p, T v) { *reinterpret_cast<T*>(p) = v; }
 
-// One RoPE pair of a B^K row, in float64: (x0, x1) at features (2m, 2m+1)
-// turned by pos * theta_m, theta_m = base^(-2m/q2).
-__device__ __forceinline__ void rope_pair(double x0, double x1, int pos, int m, int q2, double log2_base,
-                                          double& y0, double& y1) {
+// The RoPE angle of pair m at position pos, in float64: sin and cos of
+// pos * theta_m, theta_m = base^(-2m/q2).
+__device__ __forceinline__ void rope_angle(int pos, int m, int q2, double log2_base, double& sn, double& cs) {
     const double theta = exp2(-(2.0 * m / q2) * log2_base);
-    double sn, cs;
     sincos((double)pos * theta, &sn, &cs);
+}
+
+// (x0, x1) turned by that angle.  Products and sums stay separate roundings
+// (no fused multiply-add), so every kernel that rotates gets the same bits.
+__device__ __forceinline__ void rope_rotate(double x0, double x1, double sn, double cs, double& y0, double& y1) {
+#pragma clang fp contract(off)
     y0 = x0 * cs - x1 * sn;
     y1 = x0 * sn + x1 * cs;
+}
+
+// One RoPE pair of a B^K row, in float64: (x0, x1) at features (2m, 2m+1)
+// turned by pos * theta_m.
+__device__ __forceinline__ void rope_pair(double x0, double x1, int pos, int m, int q2, double log2_base,
+                                          double& y0, double& y1) {
+    double sn, cs;
+    rope_angle(pos, m, q2, log2_base, sn, cs);
+    rope_rotate(x0, x1, sn, cs, y0, y1);
 }
 
 // Slot of token n of sequence b (may be out of range; the writer checks).

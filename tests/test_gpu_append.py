@@ -97,3 +97,65 @@ def test_append_device_status_and_no_write(gpu_lib):
     assert np.all(sets[0][1, 10] == 0) and positions[1, 10] == 0
     assert positions[1, 11] == int(pos[1, 1])
     assert positions[2, cap - 1] == int(pos[2, 0])
+
+
+@pytest.mark.parametrize("name", ["kpa_32k", "tpa_degenerate", "tiny_f32"])
+def test_append_spanning_tiles_keeps_every_other_byte(gpu_lib, name):
+    """70 new tokens per sequence from slot0 = -5 (the first five rejected),
+    from a slot inside a tile, and running past the capacity: written slots
+    hold the tokens (copies bit-exact, B~^K within half an ulp of the float64
+    rotation), every other byte of the cache is unchanged."""
+    cfg = CONFIGS[name]
+    dims = dims_of(cfg)
+    nb, cap, n_new = 3, 160, 70
+    inp = make_inputs(cfg, seed=9, batch=nb, ctx=n_new, pos_offset=1000)
+    slot0 = torch.tensor([-5, 7, cap - 40], dtype=torch.int32)
+    cache = kpa.alloc_cache(dims, nb, cap)
+    cache.random_(0, 256)
+    before = cache.cpu().numpy().copy()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kpa.kpa_cache_append(dims, cache, nb, cap, inp.a_k.cuda(), inp.b_k.cuda(), inp.a_v.cuda(), inp.b_v.cuda(),
+                         inp.positions.cuda(), slot0.cuda(), n_new=n_new, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kpa.KPA_DEV_SLOT_OUT_OF_RANGE
+    lay = kpa.kpa_cache_layout(dims, nb, cap)
+    after = cache.cpu().numpy()
+    sets, pos = unpack(after, lay, dims, nb, cap)
+    old_sets, old_pos = unpack(before, lay, dims, nb, cap)
+    flat = lambda t: _bits(t).reshape(nb, n_new, -1)
+    written = np.zeros((nb, cap), bool)
+    ulp_bits = 23 if cfg.dtype == "f32" else 7
+    bk = inp.b_k.to(torch.float64).numpy()
+    for b in range(nb):
+        for n in range(n_new):
+            s = int(slot0[b]) + n
+            if not 0 <= s < cap:
+                continue
+            written[b, s] = True
+            for c, src in ((0, inp.a_k), (2, inp.a_v), (3, inp.b_v)):
+                np.testing.assert_array_equal(sets[c][b, s], flat(src)[b, n])
+            assert pos[b, s] == int(inp.positions[b, n])
+            want = kpa_ref.append_rotate(bk[b, n], int(inp.positions[b, n])).reshape(-1)
+            got = _to_f64(sets[1][b, s], cfg.dtype)
+            half_ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 1 - ulp_bits) * 0.5
+            assert np.all(np.abs(got - want) <= half_ulp * (1 + 1e-6) + 1e-300), (b, n)
+    # everything outside the written slots, padding included, keeps its bytes
+    mask = np.ones(after.shape, bool)
+    T, tb = lay["tile_slots"], lay["tile_bytes"]
+    es = lay["elem_bytes"]
+    for b in range(nb):
+        for s in np.nonzero(written[b])[0]:
+            base = (b * lay["n_tiles"] + s // T) * tb
+            t = s % T
+            for c in range(4):
+                e = np.arange(lay["comp_elems"][c])
+                if c < 2:
+                    per = 16 // es
+                    off = base + lay["comp_offset"][c] + (e // per) * (T * 16) + t * 16 + (e % per) * es
+                else:
+                    off = base + lay["comp_offset"][c] + (e * T + t) * es
+                for k in range(es):
+                    mask[off + k] = False
+            p = lay["positions_offset"] + (b * lay["n_tiles"] * T + s) * 4
+            mask[p:p + 4] = False
+    assert np.array_equal(after[mask], before[mask])

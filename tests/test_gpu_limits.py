@@ -33,6 +33,7 @@ CASES = [
     (_cfg("one_head", 1, 1, 8, 16, 2, 2), 3, 200, 1, True),
     (_cfg("one_pair_per_row", 4, 4, 64, 2, 2, 2), 2, 160, 1, False),   # q2 = 2
     (_cfg("ranks_1_3", 4, 4, 8, 16, 1, 3), 2, 140, 2, True),
+    (_cfg("wide_rotary", 2, 2, 1, 128, 1, 2), 2, 75, 1, True),         # q2 = 128: the per-token append
 ]
 
 
