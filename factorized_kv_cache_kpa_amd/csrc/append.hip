@@ -15,6 +15,7 @@ namespace kpa {
 namespace {
 
 constexpr int kMaxTilePairs = 32;  // q2 / 2 the tile kernel's angle table holds
+constexpr int kStageRowMax = 1024; // input rows (bytes) the tile kernel stages in LDS
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 template <bool kF32>
@@ -34,6 +35,7 @@ __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
     __shared__ double cs_tab[kTileSlots][kMaxTilePairs], sn_tab[kTileSlots][kMaxTilePairs];
     __shared__ int pos_s[kTileSlots];
     __shared__ int ok_s[kTileSlots];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kTileSlots * (kStageRowMax + kChunkBytes)];
     const AppendInputs& in = P.in;
     const Layout& L = P.L;
     const int b = blockIdx.y;
@@ -71,18 +73,52 @@ __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
     uint8_t* tb = P.cache + ((int64_t)b * L.n_tiles + tile) * L.tile_bytes;
     const int64_t tok0 = (int64_t)b * in.n_new + (base - s0);  // token index of position 0 of the tile
 
+    // The tile's tokens are consecutive rows of each input set.  A set whose
+    // rows are whole 16-byte chunks (at most 1 KB), from a 16-byte aligned
+    // input, is staged into LDS with coalesced 16-byte loads, one row per slot
+    // position (rows padded by 16 bytes so that the readers spread over the
+    // banks), then written out from there; any other set is read from global
+    // memory element by element.  (Staging several sets per phase, or the
+    // angles behind the first set's loads, measured slower.)
+    const int t_lo = s0 + n_lo - base, n_t = n_hi - n_lo;
+    auto stage_set = [&](const void* src_v, int ne) -> bool {
+        const int row = ne * (int)sizeof(E);
+        if (row % kChunkBytes != 0 || row > kStageRowMax || (reinterpret_cast<uintptr_t>(src_v) % kChunkBytes) != 0)
+            return false;
+        const uint8_t* src = static_cast<const uint8_t*>(src_v) + (tok0 + t_lo) * (int64_t)row;
+        const int per_row = row / kChunkBytes;
+        for (int i = tid; i < n_t * per_row; i += blockDim.x) {
+            const int r = i / per_row, ch = i % per_row;
+            *reinterpret_cast<u32x4_t*>(stage + (t_lo + r) * (row + kChunkBytes) + ch * kChunkBytes) =
+                *reinterpret_cast<const u32x4_t*>(src + (int64_t)i * kChunkBytes);
+        }
+        return true;
+    };
+
     // feature-chunk sets: A^K copied, B^K rotated; one (chunk, slot) per step
     for (int c = 0; c < 2; ++c) {
         const int ne = L.elems[c], nch = (ne + PC - 1) / PC;
-        const E* src = reinterpret_cast<const E*>(c == 0 ? in.a_k : in.b_k);
+        const void* srcv = c == 0 ? in.a_k : in.b_k;
+        __syncthreads();  // the previous set's readers are done with the stage
+        const bool staged = stage_set(srcv, ne);
+        __syncthreads();
+        const E* src = reinterpret_cast<const E*>(srcv);
+        const E* st = reinterpret_cast<const E*>(stage);
+        const int srow = ne + PC;  // staged row stride in elements
         for (int u = tid; u < nch * kTileSlots; u += blockDim.x) {
             const int cc = u / kTileSlots, t = u % kTileSlots;
             if (!ok_s[t]) continue;
-            const E* from = src + (tok0 + t) * ne + cc * PC;
             const int cnt = min(PC, ne - cc * PC);
             E v[PC];
+            if (staged) {
+                // whole chunks (the row is a multiple of 16 bytes)
+                const u32x4_t w = *reinterpret_cast<const u32x4_t*>(st + t * srow + cc * PC);
+                __builtin_memcpy(v, &w, sizeof(w));
+            } else {
+                const E* from = src + (tok0 + t) * ne + cc * PC;
 #pragma unroll
-            for (int k = 0; k < PC; ++k) v[k] = k < cnt ? from[k] : E(0);
+                for (int k = 0; k < PC; ++k) v[k] = k < cnt ? from[k] : E(0);
+            }
             if (c == 1) {
                 // pairs (2j, 2j+1) of the chunk; a chunk starts on a pair (PC even)
 #pragma unroll
@@ -110,7 +146,9 @@ __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
             }
             uint8_t* to = tb + L.off[c] + (int64_t)cc * (kTileSlots * kChunkBytes) + t * kChunkBytes;
             if (cnt == PC) {
-                *reinterpret_cast<u32x4_t*>(to) = __builtin_bit_cast(u32x4_t, v);
+                u32x4_t w;
+                __builtin_memcpy(&w, v, sizeof(w));
+                *reinterpret_cast<u32x4_t*>(to) = w;
             } else {
 #pragma unroll
                 for (int k = 0; k < PC; ++k)
@@ -121,11 +159,18 @@ __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
     // value-format sets (A^V, B^V): element rows of 32 slots
     for (int c = 2; c < 4; ++c) {
         const int ne = L.elems[c];
-        const E* src = reinterpret_cast<const E*>(c == 2 ? in.a_v : in.b_v);
+        const void* srcv = c == 2 ? in.a_v : in.b_v;
+        __syncthreads();
+        const bool staged = stage_set(srcv, ne);
+        __syncthreads();
+        const E* src = reinterpret_cast<const E*>(srcv);
+        const E* st = reinterpret_cast<const E*>(stage);
+        const int srow = ne + PC;
         for (int u = tid; u < ne * kTileSlots; u += blockDim.x) {
             const int e = u / kTileSlots, t = u % kTileSlots;
-            if (ok_s[t])
-                store_elem<E>(tb + L.off[c] + ((int64_t)e * kTileSlots + t) * sizeof(E), src[(tok0 + t) * ne + e]);
+            if (!ok_s[t]) continue;
+            const E val = staged ? st[t * srow + e] : src[(tok0 + t) * ne + e];
+            store_elem<E>(tb + L.off[c] + ((int64_t)e * kTileSlots + t) * sizeof(E), val);
         }
     }
     if (tid < kTileSlots && ok_s[tid]) {
