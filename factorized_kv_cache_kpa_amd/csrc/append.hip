@@ -4,7 +4,7 @@
 //    new tokens touch.  The float64 angle of each (token, rotary pair index)
 //    is computed once (a B^K row of every rank and head row shares it), the
 //    feature-chunk sets are written as whole 16-byte chunks and the value
-//    sets slot-contiguous, so a bulk append streams at memory speed.
+//    sets slot-contiguous.
 //  * append_kernel: one workgroup per (new token, sequence); for q2 > 64,
 //    whose angle table would not fit the tile kernel's LDS.
 // Both write the same bytes: the elements of the new tokens' slots and their
@@ -15,7 +15,11 @@ namespace kpa {
 namespace {
 
 constexpr int kMaxTilePairs = 32;  // q2 / 2 the tile kernel's angle table holds
-constexpr int kStageRowMax = 1024; // input rows (bytes) the tile kernel stages in LDS
+// input rows (bytes) the tile kernel stages in LDS: with the largest angle
+// table (32 pairs: 32 KB) the launch stays within 64 KB of dynamic LDS
+constexpr int kStageRowMax = 992;
+static_assert(2 * kTileSlots * kMaxTilePairs * 8 + kTileSlots * (kStageRowMax + kChunkBytes) <= 65536,
+              "the tile kernel's LDS fits 64 KB");
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 template <bool kF32>
@@ -32,10 +36,16 @@ template <bool kF32>
 __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
     using E = typename std::conditional<kF32, float, uint16_t>::type;
     constexpr int PC = kChunkBytes / (int)sizeof(E);  // elements per 16-byte chunk
-    __shared__ double cs_tab[kTileSlots][kMaxTilePairs], sn_tab[kTileSlots][kMaxTilePairs];
+    // LDS, sized by the launch for these dims: the angle table (cos, sin per
+    // slot position and pair index), then the stage (32 rows of the longest
+    // staged set, each padded by 16 bytes)
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
     __shared__ int pos_s[kTileSlots];
     __shared__ int ok_s[kTileSlots];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[kTileSlots * (kStageRowMax + kChunkBytes)];
+    const int half_pairs = P.d.q2 / 2;  // (at most kMaxTilePairs: the launch checks)
+    double* const cs_tab = reinterpret_cast<double*>(dyn);
+    double* const sn_tab = cs_tab + kTileSlots * half_pairs;
+    uint8_t* const stage = dyn + 2 * kTileSlots * half_pairs * sizeof(double);
     const AppendInputs& in = P.in;
     const Layout& L = P.L;
     const int b = blockIdx.y;
@@ -66,7 +76,7 @@ __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
     const double log2_base = log2((double)P.d.rope_base);
     for (int i = tid; i < kTileSlots * half; i += blockDim.x) {
         const int t = i / half, m = i % half;
-        if (ok_s[t]) rope_angle(pos_s[t], m, q2, log2_base, sn_tab[t][m], cs_tab[t][m]);
+        if (ok_s[t]) rope_angle(pos_s[t], m, q2, log2_base, sn_tab[t * half + m], cs_tab[t * half + m]);
     }
     __syncthreads();
     if (tile < 0 || tile >= L.n_tiles) return;  // (then no token of it is ok)
@@ -134,7 +144,7 @@ __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
                         x1 = bf16_to_f32(v[k + 1]);
                     }
                     double y0, y1;
-                    rope_rotate(x0, x1, sn_tab[t][m], cs_tab[t][m], y0, y1);
+                    rope_rotate(x0, x1, sn_tab[t * half + m], cs_tab[t * half + m], y0, y1);
                     if constexpr (kF32) {
                         v[k] = (float)y0;
                         v[k + 1] = (float)y1;
@@ -185,10 +195,17 @@ hipError_t launch_append(const AppendParams& P, hipStream_t s) {
     if (P.d.q2 / 2 <= kMaxTilePairs) {
         // the new tokens of a sequence touch at most ceil(n_new / 32) + 1 tiles
         const dim3 grid((P.in.n_new + kTileSlots - 1) / kTileSlots + 1, P.batch);
+        int row = 0;  // the longest row the kernel may stage
+        for (int c = 0; c < 4; ++c) {
+            const int r = P.L.elems[c] * P.L.elem_bytes;
+            if (r % kChunkBytes == 0 && r <= kStageRowMax) row = r > row ? r : row;
+        }
+        const size_t lds = 2 * (size_t)kTileSlots * (P.d.q2 / 2) * sizeof(double) +
+                           (size_t)kTileSlots * (row + kChunkBytes);
         if (P.d.dtype == KPA_F32)
-            hipLaunchKernelGGL(append_tile_kernel<true>, grid, dim3(256), 0, s, P);
+            hipLaunchKernelGGL(append_tile_kernel<true>, grid, dim3(256), lds, s, P);
         else
-            hipLaunchKernelGGL(append_tile_kernel<false>, grid, dim3(256), 0, s, P);
+            hipLaunchKernelGGL(append_tile_kernel<false>, grid, dim3(256), lds, s, P);
         return hipGetLastError();
     }
     const dim3 grid(P.in.n_new, P.batch);
