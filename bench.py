@@ -78,7 +78,7 @@ def parse():
     ap.add_argument("--plain-json", default=None, help="JSON line of the same command run without the profiler")
     ap.add_argument("--summarize-pmc", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--copy-mib", type=int, default=256)
-    ap.add_argument("--sweep", choices=["flashtpa", "project"], default=None,
+    ap.add_argument("--sweep", choices=["flashtpa", "project", "append"], default=None,
                     help="time the decode over FlashTPA's benchmark shapes instead of one workload")
     ap.add_argument("--sweep-out", default=None, help="write the sweep table (markdown) here")
     ap.add_argument("--summarize-util", default=None, metavar="PMC_DIR",
@@ -97,6 +97,8 @@ def main():
         return summarize_util(args)
     if args.sweep == "project":
         return sweep_project(args)
+    if args.sweep == "append":
+        return sweep_append(args)
     if args.sweep:
         return sweep_flashtpa(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -635,6 +637,81 @@ def sweep_project(args):
     for name, d_model, n_feat, m, kern, gbs, tfl, tps, cpu in rows:
         lines.append(f"| {name} | {d_model} | {n_feat} | {m} | {kern:.1f} | {gbs:.0f} | {100 * gbs / HBM_PEAK_GBPS:.1f}% "
                      f"| {tfl:.1f} | {100 * tfl / 2500.0:.2f}% | {tps:.3e} | {cpu:.3e} |")
+    table = "\n".join(lines)
+    print(table)
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write(table + "\n")
+
+
+def sweep_append(args):
+    """kpa_cache_append for every configuration: the decode step's new tokens
+    (n_q per sequence) and a bulk fill of min(8192, ctx) tokens per sequence,
+    for the configuration's batch.  Factors are the seeded inputs of the
+    configuration (torch CPU generator), already on the GPU.  Time: stream
+    events around each call, which is one kernel (median of 10 after 30 ms of
+    untimed calls).  HBM bytes: the factors read and written once and the
+    positions read and written.  The CPU column is the float64 oracle's
+    append (the B^K rotation, NumPy) on a sample of at most 256 tokens."""
+    import numpy as np
+    import torch
+
+    import factorized_kv_cache_kpa_amd as kpa
+    from oracle import kpa_ref
+    from workloads import CONFIGS, make_inputs
+
+    kpa.load()
+    dev = "cuda"
+    rows = []
+    for name in ("tiny_f32", "tpa_degenerate", "kpa_32k", "long_512k", "multiq_16"):
+        cfg = CONFIGS[name]
+        dims = kpa.make_dims(cfg.p1, cfg.p2, cfg.q1, cfg.q2, cfg.r_k, cfg.r_v, dtype=cfg.dtype,
+                             rope_base=cfg.rope_base)
+        nb = cfg.batch
+        for n_new in (cfg.n_q, min(8192, cfg.ctx)):
+            inp = make_inputs(cfg, seed=0, batch=nb, ctx=n_new)
+            t = [x.contiguous().to(dev) for x in (inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions)]
+            slot0 = torch.zeros(nb, dtype=torch.int32, device=dev)
+            cache = kpa.alloc_cache(dims, nb, n_new, device=dev)
+
+            def call():
+                kpa.kpa_cache_append(dims, cache, nb, n_new, *t, slot0, n_new=n_new)
+
+            t_w, n_w = time.perf_counter(), 0
+            while n_w < 3 or time.perf_counter() - t_w < 0.03:
+                call()
+                n_w += 1
+                if n_w % 20 == 0:
+                    torch.cuda.synchronize()
+            reps = 10
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            torch.cuda.synchronize()
+            for a, b in ev:
+                a.record()
+                call()
+                b.record()
+            torch.cuda.synchronize()
+            us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+            m = nb * n_new
+            nbytes = m * (2 * cfg.bytes_per_token + 8)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            # CPU: the oracle's rotation of B^K (the copies are free) on a sample
+            ms = min(m, 256)
+            bk = inp.b_k.reshape(m, *inp.b_k.shape[2:])[:ms].to(torch.float64).numpy()
+            ps = inp.positions.reshape(-1)[:ms].numpy()
+            t0 = time.perf_counter()
+            for i in range(ms):
+                kpa_ref.append_rotate(bk[i], int(ps[i]), cfg.rope_base)
+            cpu_tps = ms / (time.perf_counter() - t0)
+            rows.append((name, nb, n_new, us, gbs, m / (us * 1e-6), cpu_tps))
+            log(f"{name} {nb} x {n_new} tokens: {us:.1f} us, {gbs:.0f} GB/s")
+            del cache, t
+            torch.cuda.empty_cache()
+    lines = ["| config | sequences | new tokens each | call us | GB/s | of 8 TB/s | tokens/s | CPU oracle tokens/s |",
+             "|---|---|---|---|---|---|---|---|"]
+    for name, nb, n_new, us, gbs, tps, cpu in rows:
+        lines.append(f"| {name} | {nb} | {n_new} | {us:.1f} | {gbs:.0f} | {100 * gbs / HBM_PEAK_GBPS:.1f}% | "
+                     f"{tps:.3e} | {cpu:.3e} |")
     table = "\n".join(lines)
     print(table)
     if args.sweep_out:
