@@ -241,34 +241,38 @@ __global__ void __launch_bounds__(256, 2) project_tiled_kernel(ProjectParams P) 
     auto rd = [&](const uint8_t* buf, int m, int kc) {
         return ld_lds16(reinterpret_cast<const uint16_t*>(buf + m * 128 + ((kc ^ ((m >> 1) & 7)) * 16)));
     };
+    // The whole step's operands are read first (16 reads, 64 registers), so
+    // the LDS latency of a later K slice hides behind the earlier slices'
+    // MFMAs instead of stalling every slice.
     auto compute = [&](const uint8_t* sa, const uint8_t* sb) {
+        bf16x8 a[kTK / 16][2], bv[kTK / 16][2];
 #pragma unroll
         for (int kk = 0; kk < kTK / 16; ++kk) {
             const int kc = 2 * kk + hi;  // this lane's 8 of the step's 16
-            bf16x8 a[2], bv[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = rd(sa, wm * 64 + 32 * i + l32, kc);
+            for (int i = 0; i < 2; ++i) a[kk][i] = rd(sa, wm * 64 + 32 * i + l32, kc);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bv[j] = rd(sb, wn * 64 + 32 * j + l32, kc);
+            for (int j = 0; j < 2; ++j) bv[kk][j] = rd(sb, wn * 64 + 32 * j + l32, kc);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+#pragma unroll
+        for (int kk = 0; kk < kTK / 16; ++kk)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bv[j], acc[i][j], 0, 0, 0);
-        }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk][i], bv[kk][j], acc[i][j], 0, 0, 0);
     };
+    // One exit from the K loop (the step's buffers chosen by its parity), so
+    // the accumulators stay in the same registers throughout.
     const int nk = K / kTK;
     issue(0, sa0, sb0);
-    for (int kt = 0; kt < nk; kt += 2) {
+    for (int kt = 0; kt < nk; ++kt) {
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this step's DMA
         __syncthreads();                     // ... every wave's; the other buffers are free
-        if (kt + 1 < nk) issue((kt + 1) * kTK, sa1, sb1);
-        compute(sa0, sb0);
-        if (kt + 1 >= nk) break;
-        __builtin_amdgcn_s_waitcnt(0x0f70);
-        __syncthreads();
-        if (kt + 2 < nk) issue((kt + 2) * kTK, sa0, sb0);
-        compute(sa1, sb1);
+        const bool odd = kt & 1;
+        if (kt + 1 < nk) issue((kt + 1) * kTK, odd ? sa0 : sa1, odd ? sb0 : sb1);
+        compute(odd ? sa1 : sa0, odd ? sb1 : sb0);
     }
 
     // epilogue through LDS: block (i, j) register r holds row 32 i + 8 (r / 4)
