@@ -29,6 +29,7 @@ KPA_MAX_HEAD_DIM = 256
 KPA_MAX_RANK = 16
 KPA_MAX_HD = 8192
 KPA_MAX_NQ = 64
+KPA_MAX_CAPACITY = 1 << 30
 TILE_SLOTS = 32
 
 _lib = None

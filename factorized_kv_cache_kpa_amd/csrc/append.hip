@@ -50,16 +50,18 @@ __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
     const Layout& L = P.L;
     const int b = blockIdx.y;
     const int s0 = in.slot0[b];
-    const int tile = floor_div32(s0) + (int)blockIdx.x;
-    const int base = tile * kTileSlots;  // slot of position 0 of this tile
+    // in 64 bits: s0 comes from device memory and may sit near the int32 limit
+    const int64_t tile = (int64_t)floor_div32(s0) + blockIdx.x;
+    const int64_t base = tile * kTileSlots;  // slot of position 0 of this tile
     // new tokens n in [n_lo, n_hi) fall in this tile, at t = s0 + n - base
-    const int n_lo = max(0, base - s0), n_hi = min(in.n_new, base + kTileSlots - s0);
+    const int n_lo = (int)max((int64_t)0, base - s0);
+    const int n_hi = (int)min((int64_t)in.n_new, base + kTileSlots - s0);
     if (n_lo >= n_hi) return;
     const int tid = threadIdx.x;
     if (tid < kTileSlots) {
-        const int n = base + tid - s0;
+        const int n = (int)(base + tid - s0);
         const bool mine = n >= n_lo && n < n_hi;
-        const int slot = base + tid;
+        const int64_t slot = base + tid;
         const int pos = mine ? in.positions[(int64_t)b * in.n_new + n] : -1;
         const bool ok = mine && slot >= 0 && slot < P.capacity && pos >= 0;
         if (mine && !ok && P.dev_status) {
@@ -90,7 +92,7 @@ __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
     // banks), then written out from there; any other set is read from global
     // memory element by element.  (Staging several sets per phase, or the
     // angles behind the first set's loads, measured slower.)
-    const int t_lo = s0 + n_lo - base, n_t = n_hi - n_lo;
+    const int t_lo = (int)(s0 + n_lo - base), n_t = n_hi - n_lo;
     auto stage_set = [&](const void* src_v, int ne) -> bool {
         const int row = ne * (int)sizeof(E);
         if (row % kChunkBytes != 0 || row > kStageRowMax || (reinterpret_cast<uintptr_t>(src_v) % kChunkBytes) != 0)

@@ -644,7 +644,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
         const int span = P.chunk_tiles * kTileSlots;
         bool owned = false, in_first = false;
         for (int n = 0; n < P.app.n_new; ++n) {
-            const int j = app_slot0 + n;
+            const int j = slot_add(app_slot0, n);
             const int owner = j < 0 ? 0 : min(j / span, P.n_split - 1);
             if (owner != split) continue;
             append_token<false>(P.d, L, P.cache_w, P.capacity, P.app, P.dev_status, b, n, threadIdx.x,

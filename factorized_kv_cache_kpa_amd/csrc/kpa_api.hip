@@ -50,7 +50,8 @@ int num_cus() {
 int check_decode_args(const kpa_dims* d, int32_t batch, int32_t capacity, int32_t max_ctx, int32_t n_q) {
     int st = check_dims(d);
     if (st != KPA_OK) return st;
-    if (batch < 0 || capacity < 0 || max_ctx < 0 || max_ctx > capacity) return KPA_ERR_INVALID_ARG;
+    if (batch < 0 || capacity < 0 || capacity > KPA_MAX_CAPACITY || max_ctx < 0 || max_ctx > capacity)
+        return KPA_ERR_INVALID_ARG;
     if (n_q < 1 || n_q > KPA_MAX_NQ) return KPA_ERR_INVALID_ARG;
     if ((int64_t)batch * n_q > 65535) return KPA_ERR_INVALID_ARG;
     return KPA_OK;
@@ -64,7 +65,7 @@ int kpa_cache_layout(const kpa_dims* dims, int32_t batch, int32_t capacity, kpa_
     int st = check_dims(dims);
     if (st != KPA_OK) return st;
     if (!out) return KPA_ERR_NULL_PTR;
-    if (batch < 0 || capacity < 0) return KPA_ERR_INVALID_ARG;
+    if (batch < 0 || capacity < 0 || capacity > KPA_MAX_CAPACITY) return KPA_ERR_INVALID_ARG;
     Layout L = make_layout(*dims, batch, capacity);
     out->version = KPA_LAYOUT_VERSION;
     out->tile_slots = kTileSlots;
@@ -92,7 +93,8 @@ int kpa_cache_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t c
                      uint32_t* dev_status, void* stream) {
     int st = check_dims(dims);
     if (st != KPA_OK) return st;
-    if (batch < 0 || capacity < 0 || n_new < 0 || batch > 65535) return KPA_ERR_INVALID_ARG;
+    if (batch < 0 || capacity < 0 || capacity > KPA_MAX_CAPACITY || n_new < 0 || batch > 65535)
+        return KPA_ERR_INVALID_ARG;
     if (batch == 0 || n_new == 0) return KPA_OK;
     if (!cache || !a_k || !b_k || !a_v || !b_v || !positions || !slot0) return KPA_ERR_NULL_PTR;
     if (!aligned(cache, 16)) return KPA_ERR_INVALID_ARG;
@@ -120,7 +122,8 @@ int kpa_project_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t
     t_kernel_events = KernelEvents{};
     int st = check_dims(dims);
     if (st != KPA_OK) return st;
-    if (batch < 0 || capacity < 0 || n_new < 0 || batch > 65535) return KPA_ERR_INVALID_ARG;
+    if (batch < 0 || capacity < 0 || capacity > KPA_MAX_CAPACITY || n_new < 0 || batch > 65535)
+        return KPA_ERR_INVALID_ARG;
     if (d_model <= 0 || d_model % 64 != 0 || d_model > (1 << 20)) return KPA_ERR_INVALID_ARG;
     if (batch == 0 || n_new == 0) return KPA_OK;
     const int64_t n_tok = (int64_t)batch * n_new;

@@ -45,7 +45,7 @@ __device__ __forceinline__ void rope_pair(double x0, double x1, int pos, int m, 
 }
 
 // Slot of token n of sequence b (may be out of range; the writer checks).
-__device__ __forceinline__ int append_slot(const AppendInputs& in, int b, int n) { return in.slot0[b] + n; }
+__device__ __forceinline__ int append_slot(const AppendInputs& in, int b, int n) { return slot_add(in.slot0[b], n); }
 
 // Token n of sequence b, written by threads tid = 0 .. nthr - 1 of the
 // calling workgroup (elements strided over them; B^K one rotation pair per

@@ -34,7 +34,7 @@ inline __host__ __device__ int64_t round_up(int64_t x, int64_t m) { return (x + 
 inline Layout make_layout(const kpa_dims& d, int32_t batch, int32_t capacity) {
     Layout L{};
     L.elem_bytes = d.dtype == KPA_F32 ? 4 : 2;
-    L.n_tiles = (capacity + kTileSlots - 1) / kTileSlots;
+    L.n_tiles = (int32_t)(((int64_t)capacity + kTileSlots - 1) / kTileSlots);
     L.elems[0] = d.r_k * d.p1 * d.q1;
     L.elems[1] = d.r_k * d.p2 * d.q2;
     L.elems[2] = d.r_v * d.p1 * d.q1;
@@ -94,6 +94,14 @@ struct AppendInputs {
     const int32_t* slot0;
     int32_t n_new;
 };
+
+// slot0 + n (n >= 0) for a slot0 read from device memory: a sum past the
+// int32 range saturates to INT32_MAX, which is past every capacity, so the
+// token is reported out of range instead of wrapping to a valid slot.
+__device__ __forceinline__ int slot_add(int slot0, int n) {
+    const int64_t s = (int64_t)slot0 + n;
+    return s > INT32_MAX ? INT32_MAX : (int)s;
+}
 
 struct AppendParams {
     kpa_dims d;

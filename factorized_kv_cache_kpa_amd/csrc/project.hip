@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(NW * 64) project_append_kernel(ProjectParams P
     // its slot and position are read now, their latency hidden by the GEMM
     const int tok = t;
     const int tb = t_ok ? tok / P.n_new : 0, tn = t_ok ? tok % P.n_new : 0;
-    const int slot = t_ok ? P.slot0[tb] + tn : -1;
+    const int slot = t_ok ? slot_add(P.slot0[tb], tn) : -1;
     const int pos = t_ok ? P.positions[tok] : -1;
     const int k0 = wave * kq;
     // The K order inside each block of 64 is permuted (the same for both
@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(256, 2) project_tiled_kernel(ProjectParams P) 
     const int tk = threadIdx.x % kTB, t_ep = t0 + tk;
     const bool t_ok = t_ep < T;
     const int tb = t_ok ? t_ep / P.n_new : 0;
-    const int slot = t_ok ? P.slot0[tb] + t_ep % P.n_new : -1;
+    const int slot = t_ok ? slot_add(P.slot0[tb], t_ep % P.n_new) : -1;
     const int pos = t_ok ? P.positions[t_ep] : -1;
 
     f32x16 acc[2][2];

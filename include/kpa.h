@@ -92,6 +92,9 @@ typedef struct {
 #define KPA_MAX_RANK 16       /* R_K, R_V */
 #define KPA_MAX_HD 8192       /* h * d_h */
 #define KPA_MAX_NQ 64         /* queries per sequence in kpa_decode_multiq */
+/* Slots per sequence (capacity); larger values return KPA_ERR_INVALID_ARG.
+ * 2^30 slots of the smallest token (8 bytes) already exceed one GPU's memory. */
+#define KPA_MAX_CAPACITY (1 << 30)
 
 /*
  * Cache buffer layout (KPA_LAYOUT_VERSION 1).  One cache holds `batch`
@@ -144,7 +147,8 @@ size_t kpa_cache_bytes(const kpa_dims* dims, int32_t batch, int32_t capacity);
  *       merged factor projection, [KPA] Eq. (5) and the text after it).
  *   positions [batch][n_new] int32, device: RoPE position of each new token.
  *   slot0 [batch] int32, device: slot of the first new token of sequence b;
- *       token n goes to slot slot0[b] + n.
+ *       token n goes to slot slot0[b] + n (a sum past the int32 range counts
+ *       as out of range, it does not wrap).
  *   dev_status: device uint32 word or NULL (KPA_DEV_SLOT_OUT_OF_RANGE,
  *       KPA_DEV_NEGATIVE_POSITION).
  * A^K, A^V, B^V are stored bit-exactly; B~^K = R^(2)(pos) B^K is computed in

@@ -212,3 +212,17 @@ def test_limits_are_enforced():
                                  big, 0, None, None) == -7
     assert lib.kpa_decode_multiq(d, FAKE, 1025, 64, FAKE, 64, 64, 1, FAKE, FAKE, FAKE, None, FAKE,
                                  big, 0, None, None) == -7  # batch * n_q > 65535
+
+
+def test_capacity_limit():
+    lib = kpa.load()
+    d = kpa.make_dims(4, 4, 8, 16, 2, 2)
+    info = kpa.kpa_cache_layout(d, 1, kpa.KPA_MAX_CAPACITY)
+    assert info["n_tiles"] == kpa.KPA_MAX_CAPACITY // 32
+    dp = ctypes.byref(d)
+    for cap in (kpa.KPA_MAX_CAPACITY + 1, 2 ** 31 - 1):
+        assert lib.kpa_cache_bytes(dp, 1, cap) == 0
+        assert lib.kpa_cache_append(dp, FAKE, 1, cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, None) == -7
+        assert lib.kpa_project_append(dp, FAKE, 1, cap, FAKE, 256, FAKE, FAKE, FAKE, 1, None, None) == -7
+        assert lib.kpa_decode(dp, FAKE, 1, cap, FAKE, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0, None,
+                              None) == -7

@@ -159,3 +159,29 @@ def test_append_spanning_tiles_keeps_every_other_byte(gpu_lib, name):
             p = lay["positions_offset"] + (b * lay["n_tiles"] * T + s) * 4
             mask[p:p + 4] = False
     assert np.array_equal(after[mask], before[mask])
+
+
+@pytest.mark.parametrize("n_new", [8, 40])
+def test_slot_near_the_int32_limit_is_flagged_not_wrapped(gpu_lib, n_new):
+    # sequence 0 starts 4 slots below 2^31: its slots lie past the capacity
+    # and, from the fifth token on, past the int32 range; none may wrap into
+    # the cache.  Sequence 1 is written as usual.
+    cfg = CONFIGS["kpa_32k"]
+    dims = dims_of(cfg)
+    nb, cap = 2, 64
+    inp = make_inputs(cfg, seed=6, batch=nb, ctx=n_new)
+    cache = kpa.alloc_cache(dims, nb, cap)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    slot0 = torch.tensor([2 ** 31 - 4, 3], dtype=torch.int32)
+    kpa.kpa_cache_append(dims, cache, nb, cap, inp.a_k.cuda(), inp.b_k.cuda(), inp.a_v.cuda(),
+                         inp.b_v.cuda(), inp.positions.cuda(), slot0.cuda(), n_new=n_new, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kpa.KPA_DEV_SLOT_OUT_OF_RANGE
+    lay = kpa.kpa_cache_layout(dims, nb, cap)
+    sets, positions = unpack(cache.cpu().numpy(), lay, dims, nb, cap)
+    for c in range(4):
+        assert not np.any(sets[c][0]), f"set {c} of sequence 0 was written"
+    assert not np.any(positions[0])
+    assert np.array_equal(positions[1, 3:3 + n_new], inp.positions[1].numpy())
+    assert np.array_equal(sets[0][1, 3:3 + n_new].reshape(n_new, -1),
+                          _bits(inp.a_k[1]).reshape(n_new, -1))

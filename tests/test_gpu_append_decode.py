@@ -234,3 +234,20 @@ def test_fused_step_writes_tokens_past_the_context(gpu_lib, name, batch, ctx, n_
                                inp.q, inp.q_pos, causal=True)
     assert_close(res[1][0].astype(np.float64), res[1][1].astype(np.float64), ro, rl, cfg.dtype,
                  f"{name} step with tokens past the context")
+
+
+def test_fused_step_flags_a_slot_near_the_int32_limit_like_the_append(gpu_lib):
+    # sequence 0's four new tokens start 2 slots below 2^31 (the last two
+    # slots past the int32 range): all skipped and flagged on both paths
+    cfg = CONFIGS["kpa_32k"]
+    inp = make_inputs(cfg, seed=29, batch=2, ctx=400)
+    dims = dims_of(cfg)
+    cache_seq, cache_fused = _stale_copy(inp, dims, 400, 4, seed=29)
+    bad = torch.tensor([2 ** 31 - 2, 396], dtype=torch.int32, device="cuda")
+    res = []
+    for cache, fused in ((cache_seq, False), (cache_fused, True)):
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        res.append(_step(inp, dims, cache, 400, 4, fused, status=status, slot0=bad) + (int(status.item()),))
+    assert torch.equal(cache_seq, cache_fused)
+    assert res[0][2] == res[1][2] == 1  # KPA_DEV_SLOT_OUT_OF_RANGE
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])

@@ -136,6 +136,27 @@ def test_out_of_range_slot_is_flagged_and_skipped(gpu_lib):
     assert torch.equal(cache, before)
 
 
+def test_slot_near_the_int32_limit_is_flagged_not_wrapped(gpu_lib):
+    # sequence 0's three tokens start 2 slots below 2^31 (the third past the
+    # int32 range): skipped and flagged; sequence 1's tokens are written
+    cfg = CONFIGS["kpa_32k"]
+    dims = dims_of(cfg)
+    x, w = _inputs(cfg, 2, 3, 256, seed=44)
+    cache = kpa.alloc_cache(dims, 2, 32)
+    before = cache.clone()
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pos = torch.tensor([[0, 1, 2], [7, 8, 9]], dtype=torch.int32).cuda()
+    kpa.kpa_project_append(dims, cache, 2, 32, x.cuda(), w.cuda(), pos,
+                           torch.tensor([2 ** 31 - 2, 5], dtype=torch.int32).cuda(), n_new=3, dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 1  # KPA_DEV_SLOT_OUT_OF_RANGE
+    lay = kpa.kpa_cache_layout(dims, 2, 32)
+    tb = lay["tile_bytes"]
+    assert torch.equal(cache[:tb], before[:tb])  # sequence 0's one tile
+    p = cache[lay["positions_offset"]:].cpu().numpy().view(np.int32).reshape(2, 32)
+    assert not np.any(p[0]) and list(p[1, 5:8]) == [7, 8, 9]
+
+
 @pytest.mark.parametrize("ctx", [300, 600])  # 600 tokens, 1200 in all: the tiled kernel
 def test_decode_over_a_projected_cache_matches_oracle(gpu_lib, ctx):
     """End to end: every context token projected from its hidden state into
