@@ -78,7 +78,7 @@ def parse():
     ap.add_argument("--plain-json", default=None, help="JSON line of the same command run without the profiler")
     ap.add_argument("--summarize-pmc", nargs=2, default=None, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--copy-mib", type=int, default=256)
-    ap.add_argument("--sweep", choices=["flashtpa", "project", "append"], default=None,
+    ap.add_argument("--sweep", choices=["flashtpa", "headsplit", "project", "append"], default=None,
                     help="time the decode over FlashTPA's benchmark shapes instead of one workload")
     ap.add_argument("--sweep-out", default=None, help="write the sweep table (markdown) here")
     ap.add_argument("--summarize-util", default=None, metavar="PMC_DIR",
@@ -97,6 +97,8 @@ def main():
         return summarize_util(args)
     if args.sweep == "project":
         return sweep_project(args)
+    if args.sweep == "headsplit":
+        return sweep_headsplit(args)
     if args.sweep == "append":
         return sweep_append(args)
     if args.sweep:
@@ -736,6 +738,76 @@ def cpu_baseline_project(cfg, x, w, positions, max_tokens=256):
     return ms / (time.perf_counter() - t0)
 
 
+def _time_decode_shape(kpa, cfg, g, dev):
+    """Fill a cache of cfg's shape (factors drawn on the GPU with cfg's
+    deviations, written by kpa_cache_append in chunks), then time kpa_decode
+    of one query per sequence at the last position: medians of 10 calls after
+    at least 30 ms of untimed ones.  Returns (kernel us, call us, kernel GB/s)."""
+    import numpy as np
+    import torch
+
+    nb, ctx = cfg.batch, cfg.ctx
+    dims = kpa.make_dims(cfg.p1, cfg.p2, cfg.q1, cfg.q2, cfg.r_k, cfg.r_v, dtype=cfg.dtype)
+    cache = kpa.alloc_cache(dims, nb, ctx, device=dev)
+    chunk = 8192
+    for s0 in range(0, ctx, chunk):
+        n = min(chunk, ctx - s0)
+
+        def draw(r, p, q, sd):
+            return (torch.randn((nb, n, r, p, q), generator=g, device=dev) * sd).to(torch.bfloat16)
+
+        pos = torch.arange(s0, s0 + n, dtype=torch.int32, device=dev).repeat(nb, 1).contiguous()
+        kpa.kpa_cache_append(dims, cache, nb, ctx, draw(cfg.r_k, cfg.p1, cfg.q1, cfg.sigma_a),
+                             draw(cfg.r_k, cfg.p2, cfg.q2, cfg.sigma_b), draw(cfg.r_v, cfg.p1, cfg.q1, cfg.sigma_a),
+                             draw(cfg.r_v, cfg.p2, cfg.q2, cfg.sigma_b), pos,
+                             torch.full((nb,), s0, dtype=torch.int32, device=dev), n_new=n)
+    h, dh = cfg.h, cfg.d_h
+    q = torch.randn((nb, h, dh), generator=g, device=dev)
+    q_pos = torch.full((nb,), ctx - 1, dtype=torch.int32, device=dev)
+    ctx_len = torch.full((nb,), ctx, dtype=torch.int32, device=dev)
+    out = torch.empty((nb, h, dh), device=dev)
+    lse = torch.empty((nb, h), device=dev)
+    ws = kpa.alloc_workspace(dims, nb, ctx, device=dev)
+
+    def decode():
+        kpa.kpa_decode(dims, cache, nb, ctx, ctx_len, ctx, q, q_pos, out, lse, ws)
+
+    # at least 30 ms of calls before timing (clocks settle; no idle gap after)
+    t_w, n_w = time.perf_counter(), 0
+    while n_w < 3 or time.perf_counter() - t_w < 0.03:
+        decode()
+        n_w += 1
+        if n_w % 20 == 0:
+            torch.cuda.synchronize()
+    reps = 10
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in kev + cev:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for k in range(reps):
+        kpa.kpa_time_next_decode_kernel(*kev[k])
+        cev[k][0].record()
+        decode()
+        cev[k][1].record()
+    torch.cuda.synchronize()
+    kern = float(np.median([a.elapsed_time(b) for a, b in kev])) * 1e3
+    call = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
+    gbs = (nb * ctx * cfg.bytes_per_token) / (kern * 1e-6) / 1e9
+    del cache, ws
+    torch.cuda.empty_cache()
+    return kern, call, gbs
+
+
+def _write_table(args, lines):
+    table = "\n".join(lines)
+    print(table)
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            f.write(table + "\n")
+
+
 def sweep_flashtpa(args):
     """Decode kernel time over FlashTPA's benchmark grid (TPA split, d_h = 64,
     R_K = R_V = 1; heads x batch x sequence length).  Factors and queries are
@@ -743,7 +815,6 @@ def sweep_flashtpa(args):
     are parity-tested at small sizes); the cache is filled by kpa_cache_append
     before timing.  One line per shape: kernel and whole-call time (decode +
     merge), cached tokens/s and the kernel's HBM roofline fraction."""
-    import numpy as np
     import torch
 
     import factorized_kv_cache_kpa_amd as kpa
@@ -756,67 +827,43 @@ def sweep_flashtpa(args):
     for h in FLASHTPA_HEADS:
         for nb in FLASHTPA_BATCHES:
             for ctx in FLASHTPA_SEQS:
-                cfg = flashtpa_config(h, nb, ctx)
-                dims = kpa.make_dims(cfg.p1, cfg.p2, cfg.q1, cfg.q2, cfg.r_k, cfg.r_v, dtype=cfg.dtype)
-                cache = kpa.alloc_cache(dims, nb, ctx, device=dev)
-                chunk = 8192
-                for s0 in range(0, ctx, chunk):
-                    n = min(chunk, ctx - s0)
-
-                    def draw(p, q):
-                        return (torch.randn((nb, n, 1, p, q), generator=g, device=dev) * 0.125).to(torch.bfloat16)
-
-                    pos = torch.arange(s0, s0 + n, dtype=torch.int32, device=dev).repeat(nb, 1).contiguous()
-                    kpa.kpa_cache_append(dims, cache, nb, ctx, draw(h, 1), draw(1, 64), draw(h, 1), draw(1, 64), pos,
-                                         torch.full((nb,), s0, dtype=torch.int32, device=dev), n_new=n)
-                q = torch.randn((nb, h, 64), generator=g, device=dev)
-                q_pos = torch.full((nb,), ctx - 1, dtype=torch.int32, device=dev)
-                ctx_len = torch.full((nb,), ctx, dtype=torch.int32, device=dev)
-                out = torch.empty((nb, h, 64), device=dev)
-                lse = torch.empty((nb, h), device=dev)
-                ws = kpa.alloc_workspace(dims, nb, ctx, device=dev)
-
-                def decode():
-                    kpa.kpa_decode(dims, cache, nb, ctx, ctx_len, ctx, q, q_pos, out, lse, ws)
-
-                # at least 30 ms of calls before timing (clocks settle; no idle gap after)
-                t_w, n_w = time.perf_counter(), 0
-                while n_w < 3 or time.perf_counter() - t_w < 0.03:
-                    decode()
-                    n_w += 1
-                    if n_w % 20 == 0:
-                        torch.cuda.synchronize()
-                reps = 10
-                kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-                cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-                for a, b in kev + cev:
-                    a.record()
-                    b.record()
-                torch.cuda.synchronize()
-                for k in range(reps):
-                    kpa.kpa_time_next_decode_kernel(*kev[k])
-                    cev[k][0].record()
-                    decode()
-                    cev[k][1].record()
-                torch.cuda.synchronize()
-                kern = float(np.median([a.elapsed_time(b) for a, b in kev])) * 1e3
-                call = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
-                tokens = nb * ctx
-                gbs = (tokens * cfg.bytes_per_token) / (kern * 1e-6) / 1e9
-                rows.append((h, nb, ctx, kern, call, tokens / (call * 1e-6), gbs))
+                kern, call, gbs = _time_decode_shape(kpa, flashtpa_config(h, nb, ctx), g, dev)
+                rows.append((h, nb, ctx, kern, call, nb * ctx / (call * 1e-6), gbs))
                 log(f"h={h} batch={nb} seq={ctx}: kernel {kern:.1f} us, call {call:.1f} us, {gbs:.0f} GB/s")
-                del cache, ws
-                torch.cuda.empty_cache()
     lines = ["| h | batch | seq | decode kernel us | call (kernel + merge) us | cached tokens/s | kernel GB/s | of 8 TB/s |",
              "|---|---|---|---|---|---|---|---|"]
     for h, nb, ctx, kern, call, tps, gbs in rows:
         lines.append(f"| {h} | {nb} | {ctx} | {kern:.1f} | {call:.1f} | {tps:.3e} | {gbs:.0f} | "
                      f"{100 * gbs / HBM_PEAK_GBPS:.1f}% |")
-    table = "\n".join(lines)
-    print(table)
-    if args.sweep_out:
-        with open(args.sweep_out, "w") as f:
-            f.write(table + "\n")
+    _write_table(args, lines)
+
+
+def sweep_headsplit(args):
+    """Decode over the head splits the KPA page ablates (h = p1 x p2, d1 = d2
+    = 8, R_K = R_V = 2): 16 sequences of 32768 cached tokens each, one query
+    per sequence, factors drawn on the GPU (each split is parity-tested at
+    small sizes).  One line per split: the kernel path, kernel and whole-call
+    time, cached tokens/s and the kernel's HBM roofline fraction."""
+    import torch
+
+    import factorized_kv_cache_kpa_amd as kpa
+    from workloads import SWEEP_SHAPES, headsplit_config
+
+    kpa.load()
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(0)
+    nb, ctx = 16, 32768
+    lines = ["| split (h1 x h2) | h | bytes/token | path | decode kernel us | call (kernel + merge) us | cached tokens/s "
+             "| kernel GB/s | of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for p1, p2 in SWEEP_SHAPES:
+        cfg = headsplit_config(p1, p2, nb, ctx)
+        dims = kpa.make_dims(cfg.p1, cfg.p2, cfg.q1, cfg.q2, cfg.r_k, cfg.r_v, dtype=cfg.dtype)
+        path = kpa.kpa_decode_path(dims, 1)
+        kern, call, gbs = _time_decode_shape(kpa, cfg, g, dev)
+        log(f"split {p1}x{p2}: {path}, kernel {kern:.1f} us, call {call:.1f} us, {gbs:.0f} GB/s")
+        lines.append(f"| {p1} x {p2} | {cfg.h} | {cfg.bytes_per_token} | {path} | {kern:.1f} | {call:.1f} | "
+                     f"{nb * ctx / (call * 1e-6):.3e} | {gbs:.0f} | {100 * gbs / HBM_PEAK_GBPS:.1f}% |")
+    _write_table(args, lines)
 
 
 def summarize_util(args):

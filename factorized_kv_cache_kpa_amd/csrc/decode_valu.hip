@@ -33,8 +33,23 @@ __device__ __forceinline__ float load_factor(const uint8_t* p) {
     else return bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
 }
 
+// Byte offset of element e of set c for slot t inside a tile (the cache
+// layout's rule, with the element size fixed at compile time so that the
+// chunk arithmetic is shifts and masks).
 template <bool kF32>
-__global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P) {
+__device__ __forceinline__ int eoff(const Layout& L, int c, int e, int t) {
+    constexpr int ES = kF32 ? 4 : 2, PC = kChunkBytes / ES;
+    if (c < 2) return (int)L.off[c] + (e / PC) * (kTileSlots * kChunkBytes) + t * kChunkBytes + (e % PC) * ES;
+    return (int)L.off[c] + (e * kTileSlots + t) * ES;
+}
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4v;
+
+// kStage: each tile is first copied into LDS with 16-byte loads (when it fits
+// beside the query and score buffers), so that the many element reads of the
+// score and value loops are LDS reads instead of scattered global loads.
+template <bool kF32, bool kStage>
+__global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, int stage_off) {
     extern __shared__ float smem[];
     const kpa_dims& d = P.d;
     const Layout& L = P.L;
@@ -88,8 +103,20 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P) {
     const uint8_t* seq_base = P.cache + (int64_t)b * L.n_tiles * L.tile_bytes;
     const int es = L.elem_bytes;
     for (int s0 = first; s0 < last; s0 += kTileSlots) {
-        const uint8_t* tile = seq_base + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
+        const uint8_t* gtile = seq_base + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
         const int valid = (last - s0) < kTileSlots ? (last - s0) : kTileSlots;
+        const uint8_t* tile;
+        if constexpr (kStage) {
+            // (the previous tile's readers passed the barrier that ends the loop)
+            uint8_t* st = reinterpret_cast<uint8_t*>(smem) + stage_off;
+            const u32x4v* src = reinterpret_cast<const u32x4v*>(gtile);
+            u32x4v* dst = reinterpret_cast<u32x4v*>(st);
+            for (int v = tid; v < (int)(L.tile_bytes / kChunkBytes); v += kThreads) dst[v] = src[v];
+            __syncthreads();
+            tile = st;
+        } else {
+            tile = gtile;
+        }
 
         // 2. factor-space scores for every (head, slot) -------------------------
         for (int pi = tid; pi < h * kTileSlots; pi += kThreads) {
@@ -105,8 +132,8 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P) {
                     for (int j1 = 0; j1 < d.q1; ++j1) {
                         float w = 0.f;  // sum_j2 q'[i, j1, j2] B~^K_r[i2, j2]
                         for (int j2 = 0; j2 < d.q2; ++j2)
-                            w += qi[j1 * d.q2 + j2] * load_factor<kF32>(tile + elem_offset(L, 1, bk_row + j2, t));
-                        z += load_factor<kF32>(tile + elem_offset(L, 0, ak_row + j1, t)) * w;
+                            w += qi[j1 * d.q2 + j2] * load_factor<kF32>(tile + eoff<kF32>(L, 1, bk_row + j2, t));
+                        z += load_factor<kF32>(tile + eoff<kF32>(L, 0, ak_row + j1, t)) * w;
                     }
                 }
             }
@@ -145,8 +172,8 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P) {
                 const float* pi = zs + i * kTileSlots;
                 float sum = 0.f;
                 for (int r = 0; r < d.r_v; ++r) {
-                    const uint8_t* av = tile + elem_offset(L, 2, (r * d.p1 + i1) * d.q1 + j1, 0);
-                    const uint8_t* bv = tile + elem_offset(L, 3, (r * d.p2 + i2) * d.q2 + j2, 0);
+                    const uint8_t* av = tile + eoff<kF32>(L, 2, (r * d.p1 + i1) * d.q1 + j1, 0);
+                    const uint8_t* bv = tile + eoff<kF32>(L, 3, (r * d.p2 + i2) * d.q2 + j2, 0);
                     for (int t = 0; t < valid; ++t)
                         sum += pi[t] * load_factor<kF32>(av + t * es) * load_factor<kF32>(bv + t * es);
                 }
@@ -194,11 +221,26 @@ size_t decode_valu_smem(const kpa_dims& d) {
 
 hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
     dim3 grid(P.n_split, P.n_q, P.batch);
-    const size_t smem = decode_valu_smem(P.d);
-    if (P.d.dtype == KPA_F32)
-        hipExtLaunchKernelGGL(decode_valu_kernel<true>, grid, dim3(kThreads), smem, s, ev.start, ev.stop, 0, P);
-    else
-        hipExtLaunchKernelGGL(decode_valu_kernel<false>, grid, dim3(kThreads), smem, s, ev.start, ev.stop, 0, P);
+    const size_t base = (decode_valu_smem(P.d) + kChunkBytes - 1) / kChunkBytes * kChunkBytes;
+    const size_t staged = base + (size_t)P.L.tile_bytes;
+    const bool stage = staged <= 65536 && P.L.tile_bytes % kChunkBytes == 0;
+    const size_t smem = stage ? staged : decode_valu_smem(P.d);
+    const int off = (int)base;
+    if (P.d.dtype == KPA_F32) {
+        if (stage)
+            hipExtLaunchKernelGGL((decode_valu_kernel<true, true>), grid, dim3(kThreads), smem, s, ev.start, ev.stop, 0,
+                                  P, off);
+        else
+            hipExtLaunchKernelGGL((decode_valu_kernel<true, false>), grid, dim3(kThreads), smem, s, ev.start, ev.stop,
+                                  0, P, off);
+    } else {
+        if (stage)
+            hipExtLaunchKernelGGL((decode_valu_kernel<false, true>), grid, dim3(kThreads), smem, s, ev.start, ev.stop,
+                                  0, P, off);
+        else
+            hipExtLaunchKernelGGL((decode_valu_kernel<false, false>), grid, dim3(kThreads), smem, s, ev.start, ev.stop,
+                                  0, P, off);
+    }
     return hipGetLastError();
 }
 

@@ -242,6 +242,23 @@ def test_garbage_workspace_and_repeated_calls(gpu_lib, name, batch, ctx):
         assert_close(go, gl, ro, rl, cfg.dtype, f"{name} call {call}")
 
 
+@pytest.mark.parametrize("p1,p2", [(8, 2), (4, 4), (2, 8), (10, 2), (4, 5), (2, 10), (5, 5),
+                                   (6, 2), (4, 3), (3, 4), (2, 6)])
+def test_head_split_shapes_match_oracle(gpu_lib, p1, p2):
+    """The head splits the KPA page ablates (d1 = d2 = 8, R_K = R_V = 2):
+    ragged contexts over several chunks, automatic and forced chunk counts."""
+    from workloads import SWEEP_SHAPES, headsplit_config
+    assert (p1, p2) in SWEEP_SHAPES
+    cfg = headsplit_config(p1, p2, 3, 330)
+    inp = make_inputs(cfg, seed=20, ragged=True)  # lengths 274, 94, 127
+    dims = dims_of(cfg)
+    cache, cap = fill_cache(inp, dims)
+    ro, rl = _oracle(inp)
+    for s in (0, 3):
+        go, gl = run_decode(inp, dims, cache, cap, num_splits=s)
+        assert_close(go, gl, ro, rl, cfg.dtype, f"split {p1}x{p2} splits={s}")
+
+
 @pytest.mark.parametrize("h", [16, 32, 48])
 def test_flashtpa_shapes_match_oracle(gpu_lib, h):
     """FlashTPA's benchmark shapes (TPA split, d_h = 64, R_K = R_V = 1) on their

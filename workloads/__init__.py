@@ -5,8 +5,8 @@ problem shapes and draws random inputs.  Both the HIP path and the CPU oracle
 consume what it returns.
 """
 from .configs import (CONFIGS, FLASHTPA_BATCHES, FLASHTPA_HEADS, FLASHTPA_SEQS, SWEEP_SHAPES, Config,
-                      flashtpa_config)
+                      flashtpa_config, headsplit_config)
 from .gen import Inputs, make_inputs, make_query_factors
 
 __all__ = ["CONFIGS", "Config", "SWEEP_SHAPES", "FLASHTPA_HEADS", "FLASHTPA_SEQS", "FLASHTPA_BATCHES",
-           "flashtpa_config", "Inputs", "make_inputs", "make_query_factors"]
+           "flashtpa_config", "headsplit_config", "Inputs", "make_inputs", "make_query_factors"]

@@ -101,6 +101,14 @@ FLASHTPA_SEQS = (1 << 12, 1 << 14, 1 << 16, 1 << 19)
 FLASHTPA_BATCHES = (1, 4, 16)
 
 
+def headsplit_config(p1: int, p2: int, batch: int, ctx: int) -> Config:
+    """A head split of the KPA page's ablation: h = p1 x p2 heads, d1 = d2 = 8
+    (d_h = 64), R_K = R_V = 2, bf16 factors with sd 1/sqrt(8) per axis."""
+    s = 1.0 / math.sqrt(8)
+    return Config(f"split_{p1}x{p2}_b{batch}_s{ctx}", p1, p2, 8, 8, 2, 2, "bf16", batch=batch, ctx=ctx,
+                  sigma_a=s, sigma_b=s)
+
+
 def flashtpa_config(h: int, batch: int, ctx: int) -> Config:
     return Config(f"flashtpa_h{h}_b{batch}_s{ctx}", h, 1, 1, 64, 1, 1, "bf16", batch=batch, ctx=ctx,
                   sigma_a=0.125, sigma_b=0.125)
