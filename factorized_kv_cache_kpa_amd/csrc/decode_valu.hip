@@ -45,6 +45,26 @@ __device__ __forceinline__ int eoff(const Layout& L, int c, int e, int t) {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4v;
 
+// 8 consecutive elements (16 bytes of bf16 or 32 of float32, 16-byte aligned)
+template <bool kF32>
+__device__ __forceinline__ void load8(const uint8_t* p, float* v) {
+    if constexpr (kF32) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4v w = *reinterpret_cast<const u32x4v*>(p + 16 * h);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[4 * h + k] = __uint_as_float(w[k]);
+        }
+    } else {
+        const u32x4v w = *reinterpret_cast<const u32x4v*>(p);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    }
+}
+
 // kStage: each tile is first copied into LDS with 16-byte loads (when it fits
 // beside the query and score buffers), so that the many element reads of the
 // score and value loops are LDS reads instead of scattered global loads.
@@ -58,7 +78,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, i
     const int tid = threadIdx.x;
 
     float* qr = smem;                      // [h][dh] rotated, scaled query
-    float* zs = qr + h * dh;               // [h][32] scores, then probabilities
+    float* zs = qr + (h * dh + 3) / 4 * 4;  // [h][32] scores, then probabilities (16-byte aligned rows)
     float* m_run = zs + h * kTileSlots;    // [h] running max (log2 units)
     float* l_run = m_run + h;              // [h] running sum
     float* alpha = l_run + h;              // [h] rescale factor of this tile
@@ -118,7 +138,12 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, i
             tile = gtile;
         }
 
-        // 2. factor-space scores for every (head, slot) -------------------------
+        // 2.-3. factor-space scores for every (head, slot), then the online
+        // softmax per head: the 32 slots of a head sit in 32 consecutive lanes
+        // (h * 32 is a multiple of 32, so a lane group is all in or all out),
+        // which reduce their max and sum with shuffles.
+        constexpr int PC = kChunkBytes / (kF32 ? 4 : 2);  // elements per 16-byte chunk
+        const bool bk_chunks = d.q2 % PC == 0;            // B~^K rows are whole chunks
         for (int pi = tid; pi < h * kTileSlots; pi += kThreads) {
             const int i = pi / kTileSlots, t = pi % kTileSlots;
             float z = -INFINITY;
@@ -131,33 +156,47 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, i
                     const int ak_row = (r * d.p1 + i1) * d.q1;
                     for (int j1 = 0; j1 < d.q1; ++j1) {
                         float w = 0.f;  // sum_j2 q'[i, j1, j2] B~^K_r[i2, j2]
-                        for (int j2 = 0; j2 < d.q2; ++j2)
-                            w += qi[j1 * d.q2 + j2] * load_factor<kF32>(tile + eoff<kF32>(L, 1, bk_row + j2, t));
+                        const float* qj = qi + j1 * d.q2;
+                        if (bk_chunks) {
+                            for (int c = 0; c < d.q2; c += PC) {
+                                float bq[PC];
+                                const uint8_t* src = tile + eoff<kF32>(L, 1, bk_row + c, t);
+                                if constexpr (kF32) {
+                                    const u32x4v v4 = *reinterpret_cast<const u32x4v*>(src);
+#pragma unroll
+                                    for (int k = 0; k < 4; ++k) bq[k] = __uint_as_float(v4[k]);
+                                } else {
+                                    load8<false>(src, bq);
+                                }
+                                // q2 and d_h are multiples of 4 here: qj + c is 16-byte aligned
+#pragma unroll
+                                for (int k = 0; k < PC; k += 4) {
+                                    const float4 q4 = *reinterpret_cast<const float4*>(qj + c + k);
+                                    w += q4.x * bq[k] + q4.y * bq[k + 1] + q4.z * bq[k + 2] + q4.w * bq[k + 3];
+                                }
+                            }
+                        } else {
+                            for (int j2 = 0; j2 < d.q2; ++j2)
+                                w += qj[j2] * load_factor<kF32>(tile + eoff<kF32>(L, 1, bk_row + j2, t));
+                        }
                         z += load_factor<kF32>(tile + eoff<kF32>(L, 0, ak_row + j1, t)) * w;
                     }
                 }
             }
-            zs[i * kTileSlots + t] = z;
-        }
-        __syncthreads();
-
-        // 3. online softmax per head ---------------------------------------------
-        for (int i = tid; i < h; i += kThreads) {
-            float* zi = zs + i * kTileSlots;
-            float mx = -INFINITY;
-            for (int t = 0; t < kTileSlots; ++t) mx = fmaxf(mx, zi[t]);
+            float mx = z;
+            for (int o = kTileSlots / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
             const float m_old = m_run[i];
             const float m_new = fmaxf(m_old, mx);
             const float a = (m_new == -INFINITY) ? 1.f : exp2f(m_old - m_new);
-            float sum = 0.f;
-            for (int t = 0; t < kTileSlots; ++t) {
-                const float p = (zi[t] == -INFINITY) ? 0.f : exp2f(zi[t] - m_new);
-                zi[t] = p;
-                sum += p;
+            const float p = (z == -INFINITY) ? 0.f : exp2f(z - m_new);
+            float sum = p;
+            for (int o = kTileSlots / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+            zs[i * kTileSlots + t] = p;
+            if (t == 0) {  // (every lane of the group has read m_run[i] above)
+                alpha[i] = a;
+                m_run[i] = m_new;
+                l_run[i] = l_run[i] * a + sum;
             }
-            alpha[i] = a;
-            m_run[i] = m_new;
-            l_run[i] = l_run[i] * a + sum;
         }
         __syncthreads();
 
@@ -172,10 +211,21 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, i
                 const float* pi = zs + i * kTileSlots;
                 float sum = 0.f;
                 for (int r = 0; r < d.r_v; ++r) {
+                    // a value-set element's 32 slots are contiguous (64-byte aligned rows)
                     const uint8_t* av = tile + eoff<kF32>(L, 2, (r * d.p1 + i1) * d.q1 + j1, 0);
                     const uint8_t* bv = tile + eoff<kF32>(L, 3, (r * d.p2 + i2) * d.q2 + j2, 0);
-                    for (int t = 0; t < valid; ++t)
-                        sum += pi[t] * load_factor<kF32>(av + t * es) * load_factor<kF32>(bv + t * es);
+                    for (int t0 = 0; t0 < valid; t0 += 8) {
+                        float a8[8], b8[8];
+                        load8<kF32>(av + t0 * es, a8);
+                        load8<kF32>(bv + t0 * es, b8);
+                        // a head's 32 weights are a 128-byte aligned row
+                        const float4 p0 = *reinterpret_cast<const float4*>(pi + t0);
+                        const float4 p1 = *reinterpret_cast<const float4*>(pi + t0 + 4);
+                        const float p8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)  // slots past the context may hold anything
+                            if (t0 + k < valid) sum += p8[k] * a8[k] * b8[k];
+                    }
                 }
                 acc[k] = acc[k] * alpha[i] + sum;
             }
@@ -216,7 +266,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, i
 
 size_t decode_valu_smem(const kpa_dims& d) {
     const int h = d.p1 * d.p2, dh = d.q1 * d.q2;
-    return sizeof(float) * ((size_t)h * dh + (size_t)h * kTileSlots + 3 * (size_t)h + d.q2);
+    return sizeof(float) * (((size_t)h * dh + 3) / 4 * 4 + (size_t)h * kTileSlots + 3 * (size_t)h + d.q2);
 }
 
 hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
