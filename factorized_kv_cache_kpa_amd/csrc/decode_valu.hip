@@ -68,7 +68,16 @@ __device__ __forceinline__ void load8(const uint8_t* p, float* v) {
 // kStage: each tile is first copied into LDS with 16-byte loads (when it fits
 // beside the query and score buffers), so that the many element reads of the
 // score and value loops are LDS reads instead of scattered global loads.
-template <bool kF32, bool kStage>
+// Output element of accumulator k of thread tid.  kG4 (q2 a multiple of 4):
+// each thread owns runs of 4 consecutive outputs, which share the head and
+// j1, so the value loop forms p * A^V once for four B^V rows.
+template <bool kG4>
+__device__ __forceinline__ int out_index(int tid, int k) {
+    if constexpr (kG4) return 4 * (tid + (k / 4) * kThreads) + k % 4;
+    return tid + k * kThreads;
+}
+
+template <bool kF32, bool kStage, bool kG4>
 __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, int stage_off) {
     extern __shared__ float smem[];
     const kpa_dims& d = P.d;
@@ -201,6 +210,43 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, i
         __syncthreads();
 
         // 4. value accumulation in factor space ---------------------------------
+        if constexpr (kG4) {
+#pragma unroll
+            for (int g = 0; g < kMaxPerThread / 4; ++g) {
+                const int o0 = out_index<true>(tid, 4 * g);
+                if (o0 < h * dh) {
+                    const int i = o0 / dh, j = o0 % dh;
+                    const int i1 = i / d.p2, i2 = i % d.p2;
+                    const int j1 = j / d.q2, j20 = j % d.q2;  // outputs j20 .. j20 + 3
+                    const float* pi = zs + i * kTileSlots;
+                    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+                    for (int r = 0; r < d.r_v; ++r) {
+                        const uint8_t* av = tile + eoff<kF32>(L, 2, (r * d.p1 + i1) * d.q1 + j1, 0);
+                        const uint8_t* bv = tile + eoff<kF32>(L, 3, (r * d.p2 + i2) * d.q2 + j20, 0);
+                        for (int t0 = 0; t0 < valid; t0 += 8) {
+                            float a8[8];
+                            load8<kF32>(av + t0 * es, a8);
+                            const float4 p0 = *reinterpret_cast<const float4*>(pi + t0);
+                            const float4 p1 = *reinterpret_cast<const float4*>(pi + t0 + 4);
+                            const float p8[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+                            float pa[8];
+#pragma unroll
+                            for (int k = 0; k < 8; ++k) pa[k] = p8[k] * a8[k];
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                float b8[8];  // B^V element j20 + u: the next 32-slot row
+                                load8<kF32>(bv + (u * kTileSlots + t0) * es, b8);
+#pragma unroll
+                                for (int k = 0; k < 8; ++k)  // slots past the context may hold anything
+                                    if (t0 + k < valid) sum[u] += pa[k] * b8[k];
+                            }
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[4 * g + u] = acc[4 * g + u] * alpha[i] + sum[u];
+                }
+            }
+        } else {
 #pragma unroll
         for (int k = 0; k < kMaxPerThread; ++k) {
             const int o = tid + k * kThreads;
@@ -230,6 +276,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, i
                 acc[k] = acc[k] * alpha[i] + sum;
             }
         }
+        }
         __syncthreads();
     }
 
@@ -238,7 +285,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, i
     if (P.n_split == 1) {
 #pragma unroll
         for (int k = 0; k < kMaxPerThread; ++k) {
-            const int o = tid + k * kThreads;
+            const int o = out_index<kG4>(tid, k);
             if (o < h * dh) {
                 const int i = o / dh;
                 const float l = l_run[i];
@@ -252,7 +299,7 @@ __global__ void __launch_bounds__(kThreads) decode_valu_kernel(DecodeParams P, i
         const int64_t prow = row * P.n_split + split;
 #pragma unroll
         for (int k = 0; k < kMaxPerThread; ++k) {
-            const int o = tid + k * kThreads;
+            const int o = out_index<kG4>(tid, k);
             if (o < h * dh) P.part_o[prow * h * dh + o] = acc[k] * P.v_scale;
         }
         for (int i = tid; i < h; i += kThreads) {
@@ -269,28 +316,37 @@ size_t decode_valu_smem(const kpa_dims& d) {
     return sizeof(float) * (((size_t)h * dh + 3) / 4 * 4 + (size_t)h * kTileSlots + 3 * (size_t)h + d.q2);
 }
 
+template <bool kF32, bool kStage, bool kG4>
+void launch_valu_variant(const DecodeParams& P, dim3 grid, size_t smem, int off, hipStream_t s,
+                         const KernelEvents& ev) {
+    hipExtLaunchKernelGGL((decode_valu_kernel<kF32, kStage, kG4>), grid, dim3(kThreads), smem, s, ev.start, ev.stop, 0,
+                          P, off);
+}
+
+template <bool kF32>
+void launch_valu_dtype(const DecodeParams& P, dim3 grid, size_t smem, int off, bool stage, bool g4, hipStream_t s,
+                       const KernelEvents& ev) {
+    if (stage) {
+        if (g4) launch_valu_variant<kF32, true, true>(P, grid, smem, off, s, ev);
+        else launch_valu_variant<kF32, true, false>(P, grid, smem, off, s, ev);
+    } else {
+        if (g4) launch_valu_variant<kF32, false, true>(P, grid, smem, off, s, ev);
+        else launch_valu_variant<kF32, false, false>(P, grid, smem, off, s, ev);
+    }
+}
+
 hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
     dim3 grid(P.n_split, P.n_q, P.batch);
     const size_t base = (decode_valu_smem(P.d) + kChunkBytes - 1) / kChunkBytes * kChunkBytes;
     const size_t staged = base + (size_t)P.L.tile_bytes;
     const bool stage = staged <= 65536 && P.L.tile_bytes % kChunkBytes == 0;
+    const bool g4 = P.d.q2 % 4 == 0;
     const size_t smem = stage ? staged : decode_valu_smem(P.d);
     const int off = (int)base;
-    if (P.d.dtype == KPA_F32) {
-        if (stage)
-            hipExtLaunchKernelGGL((decode_valu_kernel<true, true>), grid, dim3(kThreads), smem, s, ev.start, ev.stop, 0,
-                                  P, off);
-        else
-            hipExtLaunchKernelGGL((decode_valu_kernel<true, false>), grid, dim3(kThreads), smem, s, ev.start, ev.stop,
-                                  0, P, off);
-    } else {
-        if (stage)
-            hipExtLaunchKernelGGL((decode_valu_kernel<false, true>), grid, dim3(kThreads), smem, s, ev.start, ev.stop,
-                                  0, P, off);
-        else
-            hipExtLaunchKernelGGL((decode_valu_kernel<false, false>), grid, dim3(kThreads), smem, s, ev.start, ev.stop,
-                                  0, P, off);
-    }
+    if (P.d.dtype == KPA_F32)
+        launch_valu_dtype<true>(P, grid, smem, off, stage, g4, s, ev);
+    else
+        launch_valu_dtype<false>(P, grid, smem, off, stage, g4, s, ev);
     return hipGetLastError();
 }
 
