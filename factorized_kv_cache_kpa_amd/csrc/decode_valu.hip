@@ -19,6 +19,10 @@
 //   5. writes either the final output or a partial (m, l, o) for the merge.
 // [KPA] = "Kronecker Product Attention: Memory-Efficient KV Compression via
 // Structured Factorization".
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "kpa_common.hpp"
 
 namespace kpa {
@@ -316,37 +320,88 @@ size_t decode_valu_smem(const kpa_dims& d) {
     return sizeof(float) * (((size_t)h * dh + 3) / 4 * 4 + (size_t)h * kTileSlots + 3 * (size_t)h + d.q2);
 }
 
+namespace {
+
+// The variant and LDS size a shape launches with: the tile is staged when it
+// fits in 64 KB beside the query and score buffers; outputs go in runs of
+// four when q2 is a multiple of 4.
+struct ValuChoice {
+    bool f32, stage, g4;
+    size_t smem;
+    int stage_off;
+};
+
+ValuChoice valu_choice(const kpa_dims& d) {
+    const Layout L = make_layout(d, 1, kTileSlots);  // the tile size depends on the dims only
+    ValuChoice c{};
+    c.f32 = d.dtype == KPA_F32;
+    const size_t base = (decode_valu_smem(d) + kChunkBytes - 1) / kChunkBytes * kChunkBytes;
+    const size_t staged = base + (size_t)L.tile_bytes;
+    c.stage = staged <= 65536 && L.tile_bytes % kChunkBytes == 0;
+    c.g4 = d.q2 % 4 == 0;
+    c.smem = c.stage ? staged : decode_valu_smem(d);
+    c.stage_off = (int)base;
+    return c;
+}
+
 template <bool kF32, bool kStage, bool kG4>
-void launch_valu_variant(const DecodeParams& P, dim3 grid, size_t smem, int off, hipStream_t s,
+const void* valu_kernel() {
+    return reinterpret_cast<const void*>(&decode_valu_kernel<kF32, kStage, kG4>);
+}
+
+const void* valu_kernel_of(const ValuChoice& c) {
+    if (c.f32) {
+        if (c.stage) return c.g4 ? valu_kernel<true, true, true>() : valu_kernel<true, true, false>();
+        return c.g4 ? valu_kernel<true, false, true>() : valu_kernel<true, false, false>();
+    }
+    if (c.stage) return c.g4 ? valu_kernel<false, true, true>() : valu_kernel<false, true, false>();
+    return c.g4 ? valu_kernel<false, false, true>() : valu_kernel<false, false, false>();
+}
+
+template <bool kF32, bool kStage, bool kG4>
+void launch_valu_variant(const DecodeParams& P, dim3 grid, const ValuChoice& c, hipStream_t s,
                          const KernelEvents& ev) {
-    hipExtLaunchKernelGGL((decode_valu_kernel<kF32, kStage, kG4>), grid, dim3(kThreads), smem, s, ev.start, ev.stop, 0,
-                          P, off);
+    hipExtLaunchKernelGGL((decode_valu_kernel<kF32, kStage, kG4>), grid, dim3(kThreads), c.smem, s, ev.start, ev.stop,
+                          0, P, c.stage_off);
 }
 
 template <bool kF32>
-void launch_valu_dtype(const DecodeParams& P, dim3 grid, size_t smem, int off, bool stage, bool g4, hipStream_t s,
-                       const KernelEvents& ev) {
-    if (stage) {
-        if (g4) launch_valu_variant<kF32, true, true>(P, grid, smem, off, s, ev);
-        else launch_valu_variant<kF32, true, false>(P, grid, smem, off, s, ev);
+void launch_valu_dtype(const DecodeParams& P, dim3 grid, const ValuChoice& c, hipStream_t s, const KernelEvents& ev) {
+    if (c.stage) {
+        if (c.g4) launch_valu_variant<kF32, true, true>(P, grid, c, s, ev);
+        else launch_valu_variant<kF32, true, false>(P, grid, c, s, ev);
     } else {
-        if (g4) launch_valu_variant<kF32, false, true>(P, grid, smem, off, s, ev);
-        else launch_valu_variant<kF32, false, false>(P, grid, smem, off, s, ev);
+        if (c.g4) launch_valu_variant<kF32, false, true>(P, grid, c, s, ev);
+        else launch_valu_variant<kF32, false, false>(P, grid, c, s, ev);
     }
+}
+
+}  // namespace
+
+// Workgroups of the vector-ALU kernel one CU holds at once for this shape
+// (registers of the chosen variant, its LDS), as the runtime reports it;
+// looked up once per (variant, LDS size).
+int decode_valu_blocks_per_cu(const kpa_dims& d) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, size_t>, int> cache;
+    const ValuChoice c = valu_choice(d);
+    const void* k = valu_kernel_of(c);
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({k, c.smem});
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kThreads, c.smem) != hipSuccess || n <= 0) n = 1;
+    cache[{k, c.smem}] = n;
+    return n;
 }
 
 hipError_t launch_decode_valu(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
     dim3 grid(P.n_split, P.n_q, P.batch);
-    const size_t base = (decode_valu_smem(P.d) + kChunkBytes - 1) / kChunkBytes * kChunkBytes;
-    const size_t staged = base + (size_t)P.L.tile_bytes;
-    const bool stage = staged <= 65536 && P.L.tile_bytes % kChunkBytes == 0;
-    const bool g4 = P.d.q2 % 4 == 0;
-    const size_t smem = stage ? staged : decode_valu_smem(P.d);
-    const int off = (int)base;
-    if (P.d.dtype == KPA_F32)
-        launch_valu_dtype<true>(P, grid, smem, off, stage, g4, s, ev);
+    const ValuChoice c = valu_choice(P.d);
+    if (c.f32)
+        launch_valu_dtype<true>(P, grid, c, s, ev);
     else
-        launch_valu_dtype<false>(P, grid, smem, off, stage, g4, s, ev);
+        launch_valu_dtype<false>(P, grid, c, s, ev);
     return hipGetLastError();
 }
 

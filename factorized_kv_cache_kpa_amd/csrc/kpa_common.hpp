@@ -212,6 +212,7 @@ hipError_t launch_stream_xor(const void* buf, int64_t bytes, uint32_t* partial, 
 hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);
 bool decode_mfma_supported(const kpa_dims& d, int n_q);
 int decode_mfma_blocks_per_cu(const kpa_dims& d, int n_q);
+int decode_valu_blocks_per_cu(const kpa_dims& d);
 int decode_mfma_query_groups(const kpa_dims& d, int n_q);
 
 }  // namespace kpa

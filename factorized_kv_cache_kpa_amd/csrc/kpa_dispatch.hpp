@@ -61,10 +61,10 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
         s = num_splits;
     } else {
         // one full round of workgroups: as many as the CUs hold at once (the
-        // matrix-core kernel's occupancy from its registers and LDS; the VALU
-        // kernel, a fallback, four per CU)
+        // kernel's occupancy from its registers and LDS, as the runtime
+        // reports it; a partial second round would leave most CUs idle)
         const bool mfma = p.path == Path::kMfmaSq;
-        const int64_t per_cu = mfma ? decode_mfma_blocks_per_cu(d, n_q) : 4;
+        const int64_t per_cu = mfma ? decode_mfma_blocks_per_cu(d, n_q) : decode_valu_blocks_per_cu(d);
         const int64_t target = per_cu * cus;
         // workgroups per chunk: one per query group (matrix cores), one per query (VALU)
         const int64_t wg_rows = mfma ? (int64_t)batch * decode_mfma_query_groups(d, n_q) : rows;
