@@ -33,6 +33,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -918,6 +919,18 @@ def summarize_util(args):
     print(path)
 
 
+def cpu_model():
+    """The host CPU's model name (the first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(inp, cfg, target_s, tokens_total):
     """Time the float64 C oracle on a bounded sample of the same decode.
 
@@ -960,7 +973,8 @@ def cpu_baseline(inp, cfg, target_s, tokens_total):
     b_idx = idx // (n_q * h)
     tok = float(ctx[b_idx].sum()) / h
     log(f"cpu oracle: {k} rows in {dt:.2f}s on {threads} threads")
-    return {"value": round(tok / dt, 1), "unit": "cached tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(tok / dt, 1), "unit": "cached tokens/s", "cores": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"{k} of {rows_total} (sequence, query, head) rows of the same workload "
                       f"(float64 C oracle, {n_q_eff} quer{'y' if n_q_eff == 1 else 'ies'} per sequence), "
                       f"{dt:.2f} s"}

@@ -33,7 +33,7 @@
 //
 // Precision: bf16 factors exactly; the rotated, scaled query is split into
 // bf16 hi + lo parts (two MFMAs) so it carries ~16 bits; the value operand
-// p * G^V is formed in fp32 and rounded once to bf16 (relative 2^-9 per
+// p * G^V is formed in fp32 and rounded once to bf16 (relative 2^-8 per
 // term, unbiased); the normaliser sums the fp32 weights; all accumulation is
 // fp32.  Because each KV chunk rounds against its own running max, results
 // for different chunk counts agree to that bf16 rounding, not bit for bit.

@@ -161,9 +161,6 @@ int kpa_cache_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t c
                      const int32_t* positions, const int32_t* slot0, int32_t n_new,
                      uint32_t* dev_status, void* stream);
 
-/* Workspace bytes kpa_decode / kpa_decode_multiq need for these arguments
- * (partial results of the split-KV decode).  num_splits as in kpa_decode.
- * Uses the current device's CU count. */
 /*
  * kpa_project_append -- project n_new tokens' hidden states to their factors
  * and write them into the cache, in one kernel ([KPA] Eq. (5) and the merged
@@ -191,6 +188,9 @@ int kpa_project_append(const kpa_dims* dims, void* cache, int32_t batch, int32_t
                        int32_t d_model, const void* w, const int32_t* positions, const int32_t* slot0,
                        int32_t n_new, uint32_t* dev_status, void* stream);
 
+/* Workspace bytes kpa_decode / kpa_decode_multiq need for these arguments
+ * (partial results of the split-KV decode).  num_splits as in kpa_decode.
+ * Uses the current device's CU count. */
 size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t max_ctx,
                                   int32_t n_q, int32_t num_splits);
 
@@ -210,7 +210,7 @@ size_t kpa_decode_workspace_bytes(const kpa_dims* dims, int32_t batch, int32_t m
  *       the CU count; > 0 forces it (clamped to [1, ceil(max_ctx / 32)]).
  *       Results agree across split counts up to rounding: float32 rounding on
  *       the vector-ALU path, the bf16 rounding of the softmax-weighted value
- *       operand (relative 2^-9 per term) on the matrix-core path.
+ *       operand (relative 2^-8 per term) on the matrix-core path.
  *   dev_status: as for kpa_cache_append (KPA_DEV_CTX_OUT_OF_RANGE), or NULL.
  * ctx_len[b] = 0 gives out = 0 and lse = -inf.
  */

@@ -43,7 +43,6 @@ __all__ = [
     "decode",
     "factored_score",
     "project_factors",
-    "round_bf16",
     "projected_cache_values",
 ]
 
@@ -287,14 +286,6 @@ def project_factors(x, w, r_k: int, r_v: int, p1: int, q1: int, p2: int, q2: int
     a_v = parts[2].reshape(*lead, r_v, p1, q1)
     b_v = parts[3].reshape(*lead, r_v, p2, q2)
     return a_k, b_k, a_v, b_v
-
-
-def round_bf16(x) -> np.ndarray:
-    """Round float64 values to the nearest bfloat16 (8 significant bits, ties
-    to even), returned as float64.  Finite normal range only."""
-    x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)  # x = m 2^e, 0.5 <= |m| < 1
-    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
 
 
 def projected_cache_values(x, w, positions, r_k: int, r_v: int, p1: int, q1: int, p2: int, q2: int,

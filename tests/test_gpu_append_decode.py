@@ -18,7 +18,7 @@ import torch
 
 import factorized_kv_cache_kpa_amd as kpa
 from oracle import kpa_oracle
-from tests.kpa_testutil import assert_close, dims_of, fill_cache
+from tests.kpa_testutil import assert_close, dims_of, fill_cache, scale_of
 from workloads import CONFIGS, flashtpa_config, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -106,7 +106,8 @@ def test_fused_step_equals_append_then_decode(gpu_lib, name, batch, ctx, n_q, ra
     assert np.array_equal(so, fo) and np.array_equal(sl, fl, equal_nan=True), "outputs differ"
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
                                inp.q, inp.q_pos, causal=True)
-    assert_close(fo.astype(np.float64), fl.astype(np.float64), ro, rl, cfg.dtype, f"{name} fused step")
+    assert_close(fo.astype(np.float64), fl.astype(np.float64), ro, rl, cfg.dtype, f"{name} fused step",
+                 scale=scale_of(inp))
 
 
 def test_fused_step_without_new_tokens_is_the_decode(gpu_lib):
@@ -193,7 +194,8 @@ def test_fused_step_with_more_new_tokens_than_queries(gpu_lib, name, batch, ctx,
     assert np.array_equal(so, fo) and np.array_equal(sl, fl, equal_nan=True), "outputs differ"
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
                                inp.q, inp.q_pos, causal=True)
-    assert_close(fo.astype(np.float64), fl.astype(np.float64), ro, rl, cfg.dtype, f"{name} fused step")
+    assert_close(fo.astype(np.float64), fl.astype(np.float64), ro, rl, cfg.dtype, f"{name} fused step",
+                 scale=scale_of(inp))
 
 
 PAST_CASES = [
@@ -233,7 +235,7 @@ def test_fused_step_writes_tokens_past_the_context(gpu_lib, name, batch, ctx, n_
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
                                inp.q, inp.q_pos, causal=True)
     assert_close(res[1][0].astype(np.float64), res[1][1].astype(np.float64), ro, rl, cfg.dtype,
-                 f"{name} step with tokens past the context")
+                 f"{name} step with tokens past the context", scale=scale_of(inp))
 
 
 def test_fused_step_flags_a_slot_near_the_int32_limit_like_the_append(gpu_lib):

@@ -3,8 +3,8 @@
 Small cases compare every output element with the oracle; they span several
 32-slot tiles, a ragged tail, ragged per-sequence contexts and several KV
 chunks.  Full-size cases (every config at its real shape, in the launch
-configuration the benchmark times) compare a seeded sample of (sequence,
-query, head) rows, which the streaming oracle computes one by one.
+configuration the benchmark times) compare every (sequence, query, head)
+row with the streaming oracle.
 """
 import numpy as np
 import pytest
@@ -12,7 +12,7 @@ import torch
 
 import factorized_kv_cache_kpa_amd as kpa
 from oracle import kpa_oracle
-from tests.kpa_testutil import assert_close, dims_of, fill_cache, rel_err, run_decode
+from tests.kpa_testutil import assert_close, dims_of, fill_cache, rel_err, run_decode, scale_of
 from workloads import CONFIGS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -45,7 +45,7 @@ def test_decode_rank_one_kpa(gpu_lib):
     cache, cap = fill_cache(inp, dims)
     go, gl = run_decode(inp, dims, cache, cap)
     ro, rl = _oracle(inp)
-    assert_close(go, gl, ro, rl, cfg.dtype, "rank one")
+    assert_close(go, gl, ro, rl, cfg.dtype, "rank one", scale=scale_of(inp))
 
 
 def test_garbage_past_the_context_is_ignored(gpu_lib):
@@ -61,7 +61,7 @@ def test_garbage_past_the_context_is_ignored(gpu_lib):
     torch.cuda.synchronize()
     go, gl = run_decode(inp, dims, nan_cache, cap, max_ctx=cap)
     ro, rl = _oracle(inp)
-    assert_close(go, gl, ro, rl, cfg.dtype, "NaN past the context")
+    assert_close(go, gl, ro, rl, cfg.dtype, "NaN past the context", scale=scale_of(inp))
 
 
 @pytest.mark.parametrize("name,batch,ctx,n_q,ragged,q_scale", SMALL)
@@ -72,7 +72,7 @@ def test_decode_matches_oracle_small(gpu_lib, name, batch, ctx, n_q, ragged, q_s
     cache, cap = fill_cache(inp, dims)
     go, gl = run_decode(inp, dims, cache, cap)
     ro, rl = _oracle(inp)
-    assert_close(go, gl, ro, rl, cfg.dtype, f"{name} b{batch} ctx{ctx}")
+    assert_close(go, gl, ro, rl, cfg.dtype, f"{name} b{batch} ctx{ctx}", scale=scale_of(inp))
 
 
 @pytest.mark.parametrize("name", ["tiny_f32", "kpa_32k", "multiq_16"])
@@ -82,7 +82,8 @@ def test_split_count_invariance(gpu_lib, name):
     dims = dims_of(cfg)
     cache, cap = fill_cache(inp, dims)
     # the matrix-core path rounds the weighted value operand to bf16 against each
-    # chunk's own running max, so chunkings agree to that rounding (2^-9 per term)
+    # chunk's own running max, so chunkings agree to that rounding (at most 2^-8
+    # relative per term in each of the two results)
     path = kpa.kpa_decode_path(dims, inp.q.shape[1])
     tol = 1e-5 if path == "valu" else 1e-2
     ro, rl = _oracle(inp)
@@ -91,7 +92,7 @@ def test_split_count_invariance(gpu_lib, name):
         o, l = run_decode(inp, dims, cache, cap, num_splits=s)
         assert rel_err(o, base_o).max() <= tol, s
         assert np.allclose(l, base_l, atol=1e-5), s
-        assert_close(o, l, ro, rl, cfg.dtype, f"splits={s}")
+        assert_close(o, l, ro, rl, cfg.dtype, f"splits={s}", scale=scale_of(inp))
 
 
 def test_non_causal_multi_query(gpu_lib):
@@ -101,7 +102,7 @@ def test_non_causal_multi_query(gpu_lib):
     cache, cap = fill_cache(inp, dims)
     go, gl = run_decode(inp, dims, cache, cap, causal=False)
     ro, rl = _oracle(inp, causal=False)
-    assert_close(go, gl, ro, rl, cfg.dtype, "non-causal")
+    assert_close(go, gl, ro, rl, cfg.dtype, "non-causal", scale=scale_of(inp))
 
 
 def test_multi_query_row_equals_truncated_single_query(gpu_lib):
@@ -117,7 +118,7 @@ def test_multi_query_row_equals_truncated_single_query(gpu_lib):
         sub.ctx_len = inp.ctx_len - 4 + n + 1
         o1, l1 = run_decode(sub, dims, cache, cap)
         # the two calls may take different kernel paths; the matrix-core path
-        # rounds the weighted value operand to bf16 (2^-9 per term)
+        # rounds the weighted value operand to bf16 (2^-8 relative per term)
         paths = {kpa.kpa_decode_path(dims, 4), kpa.kpa_decode_path(dims, 1)}
         tol = 1e-5 if paths == {"valu"} else 1e-2
         assert rel_err(go[:, n], o1[:, 0]).max() <= tol
@@ -132,7 +133,7 @@ def test_empty_context_and_zero_batch(gpu_lib):
     go, gl = run_decode(inp, dims, cache, cap, num_splits=3)
     assert np.all(go[1] == 0) and np.all(np.isneginf(gl[1]))
     ro, rl = _oracle(inp)
-    assert_close(go, gl, ro, rl, cfg.dtype, "ragged with empty")
+    assert_close(go, gl, ro, rl, cfg.dtype, "ragged with empty", scale=scale_of(inp))
     # every sequence empty, max_ctx = 0
     inp.ctx_len[:] = 0
     go, gl = run_decode(inp, dims, cache, cap, max_ctx=0)
@@ -154,23 +155,19 @@ def test_ctx_len_above_max_ctx_is_flagged(gpu_lib):
     assert int(status.item()) == kpa.KPA_DEV_CTX_OUT_OF_RANGE
 
 
-def _sample_items(rng, batch, n_q, h, k):
-    idx = rng.choice(batch * n_q * h, size=min(k, batch * n_q * h), replace=False)
-    return np.stack([idx // (n_q * h), (idx // h) % n_q, idx % h], axis=1).astype(np.int32)
-
-
-@pytest.mark.parametrize("name,k", [("tpa_degenerate", 48), ("kpa_32k", 32), ("long_512k", 8), ("multiq_16", 32)])
-def test_decode_full_size_sampled(gpu_lib, name, k):
+@pytest.mark.parametrize("name", ["tpa_degenerate", "kpa_32k", "long_512k", "multiq_16"])
+def test_decode_full_size_every_row(gpu_lib, name):
+    """Every config at its real shape, with the automatic chunk count the
+    benchmark uses: every (sequence, query, head) row against the streaming
+    float64 oracle."""
     cfg = CONFIGS[name]
     inp = make_inputs(cfg, seed=0)
     dims = dims_of(cfg)
     cache, cap = fill_cache(inp, dims)
     go, gl = run_decode(inp, dims, cache, cap)
-    items = _sample_items(np.random.default_rng(0), inp.batch, inp.q.shape[1], cfg.h, k)
-    ro, rl = _oracle(inp, items=items)
-    got_o = np.stack([go[b, n, hd] for b, n, hd in items])
-    got_l = np.array([gl[b, n, hd] for b, n, hd in items])
-    assert_close(got_o, got_l, ro, rl, cfg.dtype, f"{name} full size")
+    del cache
+    ro, rl = _oracle(inp)
+    assert_close(go, gl, ro, rl, cfg.dtype, f"{name} full size", scale=scale_of(inp))
 
 
 def test_kernel_timing_hook_brackets_the_decode_kernel(gpu_lib):
@@ -208,7 +205,7 @@ def test_odd_shape_and_two_level_merge(gpu_lib, dtype):
     ro, rl = _oracle(inp)
     for s in (1, 9, 75):
         go, gl = run_decode(inp, dims, cache, cap, num_splits=s)
-        assert_close(go, gl, ro, rl, dtype, f"odd shape, splits={s}")
+        assert_close(go, gl, ro, rl, dtype, f"odd shape, splits={s}", scale=scale_of(inp))
 
 
 @pytest.mark.parametrize("name,batch,ctx", [("kpa_32k", 32, 8192), ("long_512k", 1, 40000)])
@@ -239,7 +236,7 @@ def test_garbage_workspace_and_repeated_calls(gpu_lib, name, batch, ctx):
         torch.cuda.synchronize()
         go = out.cpu().numpy().astype(np.float64)[:, None]
         gl = lse.cpu().numpy().astype(np.float64)[:, None]
-        assert_close(go, gl, ro, rl, cfg.dtype, f"{name} call {call}")
+        assert_close(go, gl, ro, rl, cfg.dtype, f"{name} call {call}", scale=scale_of(inp))
 
 
 @pytest.mark.parametrize("p1,p2", [(8, 2), (4, 4), (2, 8), (10, 2), (4, 5), (2, 10), (5, 5),
@@ -256,7 +253,7 @@ def test_head_split_shapes_match_oracle(gpu_lib, p1, p2):
     ro, rl = _oracle(inp)
     for s in (0, 3):
         go, gl = run_decode(inp, dims, cache, cap, num_splits=s)
-        assert_close(go, gl, ro, rl, cfg.dtype, f"split {p1}x{p2} splits={s}")
+        assert_close(go, gl, ro, rl, cfg.dtype, f"split {p1}x{p2} splits={s}", scale=scale_of(inp))
 
 
 @pytest.mark.parametrize("h", [16, 32, 48])
@@ -272,4 +269,4 @@ def test_flashtpa_shapes_match_oracle(gpu_lib, h):
     ro, rl = _oracle(inp)
     for s in (0, 5):
         go, gl = run_decode(inp, dims, cache, cap, num_splits=s)
-        assert_close(go, gl, ro, rl, cfg.dtype, f"flashtpa h={h} splits={s}")
+        assert_close(go, gl, ro, rl, cfg.dtype, f"flashtpa h={h} splits={s}", scale=scale_of(inp))

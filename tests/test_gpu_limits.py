@@ -11,7 +11,7 @@ import pytest
 
 import factorized_kv_cache_kpa_amd as kpa
 from oracle import kpa_oracle
-from tests.kpa_testutil import assert_close, dims_of, fill_cache, run_decode
+from tests.kpa_testutil import assert_close, dims_of, fill_cache, run_decode, scale_of, score_scale
 from workloads import Config, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -46,7 +46,7 @@ def test_limits_and_degenerate_shapes(gpu_lib, cfg, batch, ctx, n_q, ragged):
     go, gl = run_decode(inp, dims, cache, cap)
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
                                inp.q, inp.q_pos, causal=True)
-    assert_close(go, gl, ro, rl, cfg.dtype, f"{cfg.name} ({kpa.kpa_decode_path(dims, n_q)})")
+    assert_close(go, gl, ro, rl, cfg.dtype, f"{cfg.name} ({kpa.kpa_decode_path(dims, n_q)})", scale=scale_of(inp))
 
 
 def test_many_short_sequences(gpu_lib):
@@ -62,4 +62,5 @@ def test_many_short_sequences(gpu_lib):
     sub = lambda t: t[rows]
     ro, rl = kpa_oracle.decode(sub(inp.a_k), sub(inp.b_k), sub(inp.a_v), sub(inp.b_v), sub(inp.positions),
                                sub(inp.ctx_len), sub(inp.q), sub(inp.q_pos), causal=True)
-    assert_close(go[rows], gl[rows], ro, rl, cfg.dtype, "many short sequences")
+    assert_close(go[rows], gl[rows], ro, rl, cfg.dtype, "many short sequences",
+                 scale=score_scale(sub(inp.a_k), sub(inp.b_k), sub(inp.ctx_len), sub(inp.q)))

@@ -17,7 +17,7 @@ import torch
 
 import factorized_kv_cache_kpa_amd as kpa
 from oracle import kpa_oracle, kpa_ref
-from tests.kpa_testutil import assert_close, dims_of
+from tests.kpa_testutil import assert_close, dims_of, score_scale
 from tests.test_gpu_append import unpack
 from workloads import CONFIGS, flashtpa_config
 
@@ -161,7 +161,7 @@ def test_slot_near_the_int32_limit_is_flagged_not_wrapped(gpu_lib):
 def test_decode_over_a_projected_cache_matches_oracle(gpu_lib, ctx):
     """End to end: every context token projected from its hidden state into
     the cache, then the decode; the oracle decodes the float64 projected
-    factors (the cache rounds them once to bf16, 2^-9 relative)."""
+    factors (the cache rounds them once to bf16, 2^-8 relative)."""
     cfg = CONFIGS["kpa_32k"]
     dims = dims_of(cfg)
     batch, d_model = 2, 512
@@ -187,4 +187,8 @@ def test_decode_over_a_projected_cache_matches_oracle(gpu_lib, ctx):
                                causal=True)
     go = out.cpu().numpy().astype(np.float64).reshape(batch, 1, cfg.h, cfg.d_h)
     gl = lse.cpu().numpy().astype(np.float64).reshape(batch, 1, cfg.h)
-    assert_close(go, gl, ro, rl, cfg.dtype, "decode over projected cache")
+    # both key factors are rounded from their float64 projections here (the
+    # seeded-input tests round only B~^K), so the score error is up to twice
+    # the one the lse bound assumes
+    assert_close(go, gl, ro, rl, cfg.dtype, "decode over projected cache",
+                 scale=2.0 * score_scale(a_k, b_k, ctx_len, q))

@@ -4,7 +4,8 @@ Each case swaps one oracle function for a plausible wrong variant -- a
 transposed Kronecker order, a dropped 1/R, a flipped rotation sign, the
 other Kronecker order of the rotary operator, the wrong softmax scale, a
 causal off-by-one, a factored query expanded with its factors' roles
-transposed -- and checks that at least one pin fails.
+transposed, a projected key rotated by its token index instead of its
+position -- and checks that at least one pin fails.
 """
 import numpy as np
 import pytest
@@ -86,6 +87,15 @@ def _project_sets_swapped(x, w, r_k, r_v, p1, q1, p2, q2):
     return _orig_project_factors(x, w2, r_k, r_v, p1, q1, p2, q2)
 
 
+_orig_projected_cache_values = ref.projected_cache_values
+
+
+def _projected_rotated_by_index(x, w, positions, r_k, r_v, p1, q1, p2, q2, base=10000.0):
+    # token t rotated by its index t instead of its position
+    idx = np.arange(np.asarray(positions).shape[0])
+    return _orig_projected_cache_values(x, w, idx, r_k, r_v, p1, q1, p2, q2, base)
+
+
 MUTATIONS = [
     ("kron_reconstruct", _kron_swapped, [pins.test_kron_entry_index_convention]),
     ("kron_reconstruct", _kron_no_norm, [pins.test_kron_sum_is_normalised_by_rank,
@@ -100,6 +110,8 @@ MUTATIONS = [
                                                     pins.test_factored_query_decode_equals_attention_from_factored_scores]),
     ("project_factors", _project_sets_swapped,
      [pins.test_projection_of_unit_vectors_reads_weight_columns_in_the_stated_order]),
+    ("projected_cache_values", _projected_rotated_by_index,
+     [pins.test_projected_cache_values_equal_the_rotated_full_key]),
 ]
 
 

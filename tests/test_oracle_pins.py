@@ -416,17 +416,6 @@ def test_projection_is_linear_and_keys_are_quadratic_in_the_hidden_state():
     assert np.allclose(ref.kron_reconstruct(a_k3, b_k3), 9.0 * ref.kron_reconstruct(a_k, b_k), atol=1e-10)
 
 
-def test_round_bf16_matches_torch_and_ties_to_even():
-    rng = np.random.default_rng(33)
-    v = rng.normal(size=4000).astype(np.float32) * np.float32(3.0)  # float32-exact inputs
-    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
-    assert np.array_equal(ref.round_bf16(v.astype(np.float64)), want)
-    # halfway cases: 1 + 2^-8 -> 1 (even), 1 + 3 * 2^-8 -> 1 + 2^-6 (even)
-    assert ref.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
-    assert ref.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
-    assert ref.round_bf16(np.array([-(1.0 + 3 * 2.0 ** -8)]))[0] == -(1.0 + 2.0 ** -6)
-
-
 def test_projected_cache_values_rotate_only_the_key_b_factor():
     rng = np.random.default_rng(34)
     sizes = _proj_sizes(**PROJ)
@@ -443,3 +432,27 @@ def test_projected_cache_values_rotate_only_the_key_b_factor():
         n0 = (b_k[t].reshape(-1, 2) ** 2).sum(-1)
         n1 = (cb_k[t].reshape(-1, 2) ** 2).sum(-1)
         assert np.allclose(n0, n1, atol=1e-12)
+
+
+def test_projected_cache_values_equal_the_rotated_full_key():
+    """The cached key factors of a projected token t, rebuilt into K, equal the
+    full projected key rotated by R_KPA at that token's own position
+    ([KPA] Thm. 2.4, Eqs. (7)-(8): (I (x) R(x)) (A (x) B) = A (x) (R(x) B)),
+    at positions that are not the token indices and are not in order."""
+    rng = np.random.default_rng(35)
+    sizes = _proj_sizes(**PROJ)
+    n_rows = sum(r * p * q for _, r, p, q in sizes)
+    w = rng.normal(size=(n_rows, 9))
+    x = rng.normal(size=(4, 9))
+    pos = np.array([7, 123457, 3, 524287])
+    a_k, b_k, _, _ = ref.project_factors(x, w, **PROJ)
+    ca_k, cb_k, _, _ = ref.projected_cache_values(x, w, pos, **PROJ)
+    q1, q2 = PROJ["q1"], PROJ["q2"]
+    for t in range(4):
+        # full-K route: rebuild K from the unrotated factors, then rotate every head row
+        k_full = ref.kron_block(a_k[t, 0], b_k[t, 0]) + ref.kron_block(a_k[t, 1], b_k[t, 1])
+        k_full /= 2.0
+        rot = np.kron(np.eye(q1), ref.rope_block(float(pos[t]), q2))
+        want = k_full @ rot.T
+        got = sum(ref.kron_block(ca_k[t, r], cb_k[t, r]) for r in range(2)) / 2.0
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
