@@ -7,7 +7,8 @@
 //   K_s = (1/R_K) sum_r A^K_r (x) B~^K_r, V_s likewise      ([KPA] Eqs. (3)-(4))
 //   z_{i,s} = q'_i . k_{s,i} / sqrt(d_h), q' = R_KPA(q_pos) q  ([KPA] §2.3, Def. 2.3)
 // Written with the two factors of a head: call F the factor whose feature
-// dimension is 16 (it is contracted on the matrix cores) and G the other one.
+// dimension is contracted on the matrix cores (8, 16, 32 or 64 wide) and G
+// the other one.
 // Head i = (iG, iF), feature j = (jG, jF) in the block order of the Kronecker
 // product ([KPA] Def. 2.1).  Then, per query n, rank r and cached slot s,
 //   W_r[(n,iG,jG), s] = sum_jF q'[n,iG,iF,jG,jF] F_r[s,iF,jF]   (MFMA 32x32x16:
@@ -69,7 +70,11 @@ struct Cfg {
     static constexpr int M = PG * QG;                // rows (iG, jG) per query
     static constexpr int MB32 = (M + 31) / 32;       // score MFMA row blocks (rows past M are zero)
     static constexpr int MB16 = (M + 15) / 16;       // value MFMA row blocks
-    static constexpr int KC = QF / 16;               // score MFMA K steps = value MFMA column blocks
+    // An 8-wide F feature dimension takes one 16-wide K step: the bf16 hi part
+    // of the query in the lower K half, its lo part in the upper half, and the
+    // F factor in both (so one MFMA forms (hi + lo) . F).
+    static constexpr bool K8 = QF == 8;
+    static constexpr int KC = K8 ? 1 : QF / 16;      // score MFMA K steps = value MFMA column blocks
     static constexpr int H = PG * PF;
     static constexpr int DH = QG * QF;
     // G factors of one tile: key set R_K*M elements in 16-byte chunks of 8
@@ -96,8 +101,9 @@ struct Cfg {
     static constexpr int SET_FK = F_IS_B ? 1 : 0;
     static constexpr int SET_GV = F_IS_B ? 2 : 3;
     static constexpr int SET_FV = F_IS_B ? 3 : 2;
-    static_assert(QF == 16 || QF == 32 || QF == 64, "the MFMA-side feature dimension must be 16, 32 or 64");
-    static_assert(QG == 1 || QG == 4 || QG == 8 || QG == 16, "G-side feature dimension 1, 4, 8 or 16");
+    static_assert(QF == 8 || QF == 16 || QF == 32 || QF == 64, "the MFMA-side feature dimension must be 8, 16, 32 or 64");
+    static_assert(QG == 1 || QG == 2 || QG == 4 || QG == 8 || QG == 16 || QG == 32,
+                  "G-side feature dimension 1, 2, 4, 8, 16 or 32");
     static_assert(M % 4 == 0, "rows (iG, jG) come in groups of four");
     static_assert(ROWS_P <= 64 && ROWS_P >= 2, "query-head rows of a wave must fit 64 lanes");
     static_assert(QROT <= 64, "rotary table holds 32 pairs");
@@ -146,7 +152,9 @@ __device__ __forceinline__ bf16x8 ld_f(const uint8_t* p) {
 }
 
 // One wave's F factors of one tile in registers: key set (R_K ranks) and
-// value set (R_V ranks), KC 16-byte groups each.
+// value set (R_V ranks), KC 16-byte groups each.  With an 8-wide F feature
+// dimension both halves of the wave hold the same key chunk, and the value
+// lanes of columns 8 .. 15 hold zeros.
 template <class S>
 struct FRegs {
     bf16x8 fk[S::RK_][S::KC];
@@ -154,8 +162,8 @@ struct FRegs {
 };
 
 // The F slice of wave iF: key-set lane (slot s, half) takes 8 features of
-// each 16-feature group; value-set lane (row l16, slot group g16) takes 8
-// slots of one feature row.
+// each 16-feature group (both halves the same 8 when F is 8 wide);
+// value-set lane (row l16, slot group g16) takes 8 slots of one feature row.
 template <class S>
 __device__ __forceinline__ void load_f_regs(const uint8_t* tile, int64_t offFK, int64_t offFV, int iF, int half, int s,
                                             int l16, int g16, FRegs<S>& f) {
@@ -164,12 +172,17 @@ __device__ __forceinline__ void load_f_regs(const uint8_t* tile, int64_t offFK, 
     for (int r = 0; r < S::RK_; ++r)
 #pragma unroll
         for (int kc = 0; kc < S::KC; ++kc)
-            f.fk[r][kc] = ld_f<S>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + 2 * kc + half) * 512 + s * 16);
+            f.fk[r][kc] = ld_f<S>(tile + offFK + (int64_t)((r * PF + iF) * (QF / 8) + (S::K8 ? 0 : 2 * kc + half)) * 512 +
+                                  s * 16);
 #pragma unroll
     for (int r = 0; r < S::RV_; ++r)
 #pragma unroll
-        for (int nb = 0; nb < S::KC; ++nb)
-            f.fv[r][nb] = ld_f<S>(tile + offFV + ((int64_t)((r * PF + iF) * QF + 16 * nb + l16) * 32 + 8 * g16) * 2);
+        for (int nb = 0; nb < S::KC; ++nb) {
+            if (S::K8 && l16 >= 8)
+                f.fv[r][nb] = bf16x8{};
+            else
+                f.fv[r][nb] = ld_f<S>(tile + offFV + ((int64_t)((r * PF + iF) * QF + 16 * nb + l16) * 32 + 8 * g16) * 2);
+        }
 }
 
 // Query elements (iG, iF, jG, jF0 .. jF0 + 7) of row `row`, unrotated.  Dense:
@@ -288,7 +301,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                 const int R = mb * 32 + s;
                 const bool row_ok = kFull32 || R < M;
                 const int iG = row_ok ? R / QG : 0, jG = row_ok ? R % QG : 0;
-                const float* src = P.q + (qrow * S::H + S::head(iG, iF)) * S::DH + S::feat(jG, 8 * half);
+                const float* src = P.q + (qrow * S::H + S::head(iG, iF)) * S::DH + S::feat(jG, S::K8 ? 0 : 8 * half);
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     q_pre[mb][kc][0] = *reinterpret_cast<const f32x4*>(src + 16 * kc);
@@ -341,7 +354,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                 // the 8 query elements (jG, jF0 .. jF0 + 7) of this lane and
                 // their rotary partners: (jG, jF ^ 1) when F = B (inside the
                 // same 8), (jG ^ 1, jF) when F = A
-                const int jF0 = 16 * kc + 8 * half;
+                const int jF0 = S::K8 ? 0 : 16 * kc + 8 * half;
                 float xs[8], ys[8];
                 if (kQPre && P.a_q == nullptr) {
 #pragma unroll
@@ -375,7 +388,14 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                     const float rot = first ? (x * c - y * sn) : (y * sn + x * c);
                     v[k] = row_ok ? rot * P.q_scale : 0.f;
                 }
-                split_bf16x8(v, q_hi[u][mb][kc], q_lo[u][mb][kc]);
+                if constexpr (S::K8) {
+                    // lower K half: hi; upper K half: lo (the F operand repeats)
+                    bf16x8 hi, lo;
+                    split_bf16x8(v, hi, lo);
+                    q_hi[u][mb][kc] = half ? lo : hi;
+                } else {
+                    split_bf16x8(v, q_hi[u][mb][kc], q_lo[u][mb][kc]);
+                }
             }
         }
     }
@@ -433,8 +453,9 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 #pragma unroll
         for (int mb = 0; mb < MB32; ++mb) {
             // [query][a][b]: sums over the rank, per row b (G feature dimension 1:
-            // every row is a head) or already summed over the in-lane jG
-            constexpr int ZB = QG == 1 ? 4 : 1;
+            // every row is a head), per pair of rows (dimension 2) or already
+            // summed over the in-lane jG
+            constexpr int ZB = QG == 1 ? 4 : QG == 2 ? 2 : 1;
             float zp[NQW][4][ZB];
 #pragma unroll
             for (int u = 0; u < NQW; ++u)
@@ -463,13 +484,20 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
 #pragma unroll
                     for (int kc = 0; kc < KC; ++kc) {
                         w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_hi[u][mb][kc], f.fk[r][kc], w, 0, 0, 0);
-                        w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_lo[u][mb][kc], f.fk[r][kc], w, 0, 0, 0);
+                        if constexpr (!S::K8)
+                            w = __builtin_amdgcn_mfma_f32_32x32x16_bf16(q_lo[u][mb][kc], f.fk[r][kc], w, 0, 0, 0);
                     }
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
+                        // row groups past M (the last block of a partial M): nothing to add
+                        if (!kFull32 && mb * 32 + 8 * a >= M) continue;
                         if constexpr (ZB == 4) {
 #pragma unroll
                             for (int bb = 0; bb < 4; ++bb) zp[u][a][bb] += w[a * 4 + bb] * g[a][bb];
+                        } else if constexpr (ZB == 2) {
+#pragma unroll
+                            for (int bb = 0; bb < 4; ++bb)
+                                zp[u][a][bb >> 1] = fmaf(w[a * 4 + bb], g[a][bb], zp[u][a][bb >> 1]);
                         } else {
                             // a chain of fused multiply-adds into the running sum
 #pragma unroll
@@ -491,6 +519,15 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                             const int R = mb * 32 + 8 * a + 4 * half + bb;
                             if (kFull32 || R < M) zrow[R * S::ZS + s] = ok ? zp[u][a][bb] : -INFINITY;
                         }
+                } else if constexpr (ZB == 2) {
+                    // rows 8a + 4half + 2c + {0, 1} form head mb*16 + 4a + 2half + c
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+#pragma unroll
+                        for (int c = 0; c < 2; ++c) {
+                            const int R = mb * 32 + 8 * a + 4 * half + 2 * c;
+                            if (kFull32 || R < M) zrow[(R >> 1) * S::ZS + s] = ok ? zp[u][a][c] : -INFINITY;
+                        }
                 } else {
                     float z4[4];
 #pragma unroll
@@ -509,12 +546,16 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                         const float zb = half ? z4[3] : z4[1];
                         if (kFull32 || mb * 32 + 16 * half < M) zrow[(mb * 4 + 2 * half + 0) * S::ZS + s] = ok ? za : -INFINITY;
                         if (kFull32 || mb * 32 + 16 * half + 8 < M) zrow[(mb * 4 + 2 * half + 1) * S::ZS + s] = ok ? zb : -INFINITY;
-                    } else {
-                        // QG == 16: iG = mb*2 + a/2, jG = 8(a%2) + 4half + b
+                    } else if constexpr (QG == 16) {
+                        // iG = mb*2 + a/2, jG = 8(a%2) + 4half + b
                         float z0 = z4[0] + z4[1], z1 = z4[2] + z4[3];
                         z0 = sum_halves(z0);
                         z1 = sum_halves(z1);
                         if (kFull32 || mb * 32 + 16 * half < M) zrow[(mb * 2 + half) * S::ZS + s] = ok ? (half ? z1 : z0) : -INFINITY;
+                    } else {
+                        // QG == 32: the whole row block is head mb
+                        const float z = sum_halves((z4[0] + z4[1]) + (z4[2] + z4[3]));
+                        if (half == 0 && (kFull32 || mb * 32 < M)) zrow[mb * S::ZS + s] = ok ? z : -INFINITY;
                     }
                 }
             }
@@ -702,6 +743,7 @@ __global__ void __launch_bounds__(S::WAVES * 64, S::MIN_WAVES) decode_mfma_kerne
                 const float l = ws.l_fin[u * PG + iG];
 #pragma unroll
                 for (int nb = 0; nb < KC; ++nb) {
+                    if (S::K8 && l16 >= 8) continue;  // the zero columns of an 8-wide F
                     const int j = S::feat(jG, 16 * nb + l16);
                     const float v = o_acc[u][mb][nb][c] * P.v_scale;
                     if (P.n_split == 1)
@@ -777,6 +819,21 @@ const MfmaKernel kKernels[] = {
     KPA_MFMA_ENTRY(16, 1, 1, 64, 1, 1, false, 16, 1, 1, 64, 1, 1, true, 1, 1, 2),
     KPA_MFMA_ENTRY(32, 1, 1, 64, 1, 1, false, 32, 1, 1, 64, 1, 1, true, 1, 1, 2),
     KPA_MFMA_ENTRY(48, 1, 1, 64, 1, 1, false, 48, 1, 1, 64, 1, 1, true, 1, 1, 1),
+    // The KPA page's head splits (d1 = d2 = 8, R_K = R_V = 2).  F is the
+    // factor with fewer heads (fewer waves, more rows per wave), except for
+    // 4 x 5, where four waves per workgroup (F = A) spread evenly over a
+    // CU's four SIMDs (five waves: 46% -> 62% of 8 TB/s measured)
+    KPA_MFMA_ENTRY(8, 2, 8, 8, 2, 2, false, 8, 8, 2, 8, 2, 2, true, 1, 1, 2),
+    KPA_MFMA_ENTRY(4, 4, 8, 8, 2, 2, false, 4, 8, 4, 8, 2, 2, true, 1, 1, 3),
+    KPA_MFMA_ENTRY(2, 8, 8, 8, 2, 2, false, 8, 8, 2, 8, 2, 2, false, 1, 1, 2),
+    KPA_MFMA_ENTRY(10, 2, 8, 8, 2, 2, false, 10, 8, 2, 8, 2, 2, true, 1, 1, 2),
+    KPA_MFMA_ENTRY(4, 5, 8, 8, 2, 2, false, 5, 8, 4, 8, 2, 2, false, 1, 1, 2),
+    KPA_MFMA_ENTRY(2, 10, 8, 8, 2, 2, false, 10, 8, 2, 8, 2, 2, false, 1, 1, 2),
+    KPA_MFMA_ENTRY(5, 5, 8, 8, 2, 2, false, 5, 8, 5, 8, 2, 2, true, 1, 1, 3),
+    KPA_MFMA_ENTRY(6, 2, 8, 8, 2, 2, false, 6, 8, 2, 8, 2, 2, true, 1, 1, 2),
+    KPA_MFMA_ENTRY(4, 3, 8, 8, 2, 2, false, 4, 8, 3, 8, 2, 2, true, 1, 1, 3),
+    KPA_MFMA_ENTRY(3, 4, 8, 8, 2, 2, false, 4, 8, 3, 8, 2, 2, false, 1, 1, 3),
+    KPA_MFMA_ENTRY(2, 6, 8, 8, 2, 2, false, 6, 8, 2, 8, 2, 2, false, 1, 1, 2),
 };
 #undef KPA_MFMA_ENTRY
 

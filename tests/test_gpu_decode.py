@@ -242,13 +242,15 @@ def test_garbage_workspace_and_repeated_calls(gpu_lib, name, batch, ctx):
 @pytest.mark.parametrize("p1,p2", [(8, 2), (4, 4), (2, 8), (10, 2), (4, 5), (2, 10), (5, 5),
                                    (6, 2), (4, 3), (3, 4), (2, 6)])
 def test_head_split_shapes_match_oracle(gpu_lib, p1, p2):
-    """The head splits the KPA page ablates (d1 = d2 = 8, R_K = R_V = 2):
-    ragged contexts over several chunks, automatic and forced chunk counts."""
+    """The head splits the KPA page ablates (d1 = d2 = 8, R_K = R_V = 2), on
+    the matrix cores (8-wide contraction): ragged contexts over several
+    chunks, automatic and forced chunk counts."""
     from workloads import SWEEP_SHAPES, headsplit_config
     assert (p1, p2) in SWEEP_SHAPES
     cfg = headsplit_config(p1, p2, 3, 330)
     inp = make_inputs(cfg, seed=20, ragged=True)  # lengths 274, 94, 127
     dims = dims_of(cfg)
+    assert kpa.kpa_decode_path(dims, 1) == "mfma_bf16"
     cache, cap = fill_cache(inp, dims)
     ro, rl = _oracle(inp)
     for s in (0, 3):
