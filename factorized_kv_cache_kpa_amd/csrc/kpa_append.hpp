@@ -52,7 +52,7 @@ __device__ __forceinline__ int append_slot(const AppendInputs& in, int b, int n)
 // thread).  An out-of-range slot or a negative position skips the token and
 // sets the dev_status bits.
 template <bool kF32>
-__device__ void append_token(const kpa_dims& d, const Layout& L, uint8_t* cache, int capacity,
+__device__ __forceinline__ void append_token(const kpa_dims& d, const Layout& L, uint8_t* cache, int capacity,
                              const AppendInputs& in, uint32_t* dev_status, int b, int n, int tid, int nthr) {
     const int slot = append_slot(in, b, n);
     const int pos = in.positions[(int64_t)b * in.n_new + n];

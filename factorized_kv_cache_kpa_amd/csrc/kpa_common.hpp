@@ -156,6 +156,9 @@ struct DecodeParams {
     // the new tokens of their own chunk into cache_w before reading them
     AppendInputs app;
     uint8_t* cache_w;
+    // matrix-core kernels of a generic family: 1 = B is the factor contracted
+    // on the matrix cores, 0 = A (set by the launcher)
+    int32_t f_is_b;
 };
 
 // Element (i, j) of the unrotated query of row (b, n): the dense query's, or,

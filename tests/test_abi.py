@@ -226,3 +226,52 @@ def test_capacity_limit():
         assert lib.kpa_project_append(dp, FAKE, 1, cap, FAKE, 256, FAKE, FAKE, FAKE, 1, None, None) == -7
         assert lib.kpa_decode(dp, FAKE, 1, cap, FAKE, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, 0, None,
                               None) == -7
+
+
+# Which shapes the matrix-core kernels take (host-side path choice; no GPU).
+# bf16 caches with a feature dimension of 8, 16, 32 or 64 contracted on the
+# matrix cores, the other a power of two up to 32, ranks up to 4, within the
+# row, wave and LDS caps include/kpa.h states; everything else on the
+# vector ALUs.
+MATRIX_CORE_SHAPES = [
+    # the workload configurations and the KPA page's head splits (d1 = d2 = 8, R = 2)
+    (12, 1, 1, 64, 2, 2), (4, 4, 8, 16, 2, 2), (8, 4, 8, 16, 2, 4), (4, 8, 16, 8, 4, 4),
+    (8, 2, 8, 8, 2, 2), (4, 4, 8, 8, 2, 2), (2, 8, 8, 8, 2, 2), (10, 2, 8, 8, 2, 2), (4, 5, 8, 8, 2, 2),
+    (2, 10, 8, 8, 2, 2), (5, 5, 8, 8, 2, 2), (6, 2, 8, 8, 2, 2), (4, 3, 8, 8, 2, 2), (3, 4, 8, 8, 2, 2),
+    (2, 6, 8, 8, 2, 2),
+    # FlashTPA's shapes
+    (16, 1, 1, 64, 1, 1), (32, 1, 1, 64, 1, 1), (48, 1, 1, 64, 1, 1),
+    # generic families
+    (3, 2, 8, 8, 1, 1), (6, 3, 8, 8, 3, 2), (16, 2, 8, 8, 2, 2), (2, 16, 8, 8, 1, 1), (4, 2, 4, 16, 1, 3),
+    (3, 3, 8, 16, 2, 2), (8, 2, 16, 16, 2, 2), (4, 2, 2, 32, 2, 2), (4, 4, 4, 32, 4, 1), (2, 2, 8, 32, 3, 3),
+    (20, 1, 1, 64, 2, 2), (7, 1, 1, 64, 1, 1), (8, 2, 2, 64, 1, 2), (6, 1, 4, 64, 3, 3), (2, 2, 32, 8, 2, 2),
+    (3, 4, 16, 2, 2, 2), (4, 4, 8, 16, 4, 4), (4, 4, 8, 16, 3, 1), (2, 4, 16, 8, 1, 4),
+]
+VECTOR_ALU_SHAPES = [
+    (3, 5, 3, 6, 2, 2),     # no feature dimension of 8, 16, 32 or 64
+    (3, 3, 6, 8, 2, 2),     # the other feature dimension (6) not a power of two
+    (4, 4, 8, 16, 5, 2),    # rank above 4
+    (7, 1, 1, 64, 2, 2),    # 7 rows with two key ranks
+    (2, 2, 4, 4, 2, 2),     # feature dimensions 4 and 4
+]
+
+
+@pytest.mark.parametrize("shape", MATRIX_CORE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_matrix_core_path_for_shapes_in_the_family(shape):
+    dims = kpa.make_dims(*shape)
+    assert kpa.kpa_decode_path(dims, 1) == "mfma_bf16"
+
+
+@pytest.mark.parametrize("shape", VECTOR_ALU_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_vector_alu_path_outside_the_family(shape):
+    dims = kpa.make_dims(*shape)
+    assert kpa.kpa_decode_path(dims, 1) == "valu"
+    # float32 caches always take the vector ALUs
+    assert kpa.kpa_decode_path(kpa.make_dims(4, 4, 8, 16, 2, 2, dtype="f32"), 1) == "valu"
+
+
+@pytest.mark.parametrize("shape", [(4, 8, 16, 8, 4, 4), (6, 3, 8, 8, 3, 2), (20, 1, 1, 64, 2, 2),
+                                   (8, 2, 16, 16, 2, 2), (3, 4, 16, 2, 2, 2)], ids=lambda s: "x".join(map(str, s)))
+def test_matrix_core_path_for_several_queries(shape):
+    dims = kpa.make_dims(*shape)
+    assert kpa.kpa_decode_path(dims, 16) == "mfma_bf16"
