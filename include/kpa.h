@@ -323,8 +323,31 @@ int kpa_stream_xor(const void* buf, size_t bytes, uint32_t* partial, int32_t n_b
 /* Static description of a kpa_status code. */
 const char* kpa_status_string(int status);
 
-/* Name of the kernel path kpa_decode / kpa_decode_multiq would run for these
- * dims and n_q ("mfma_bf16", "valu", ...), or "" if unsupported.  Host only. */
+/*
+ * kpa_decode_path -- name of the kernel path the decode entry points run for
+ * these dims and n_q, or "" for invalid arguments.  Host only.
+ *   "mfma_bf16": the bf16 matrix cores.  Taken by every bf16 cache for which
+ *       one factor -- call it F -- has a feature dimension of 8, 16, 32 or 64
+ *       (contracted on the matrix cores) and
+ *         - the other factor's feature dimension q_G is 1, 2, 4, 8, 16 or 32;
+ *         - R_K <= 4 and R_V <= 4;
+ *         - its rows M = p_G q_G (p_G = the other factor's head count) are
+ *           at most 128 when F's feature dimension is 8 or 16, at most 64
+ *           when it is 32 or 64 (32 for n_q > 1), and a multiple of 4
+ *           unless R_K = 1;
+ *         - F's head count p_F is at most 8 for one query (4 when the
+ *           shape's rows exceed 64 or a rank exceeds 2, or F is 32 or 64
+ *           wide) and at most 4 for n_q > 1, and 2 p_G <= 64 for n_q > 1;
+ *       plus the exact shapes the library is tuned for (the workload
+ *       configurations, the KPA page's head splits and FlashTPA's shapes).
+ *       When both factors qualify, the one giving an even spread of waves
+ *       over a CU's four SIMDs, then fewer padded rows, is chosen.
+ *   "valu": the vector ALUs: float32 caches, and bf16 shapes outside the
+ *       family above (e.g. no feature dimension of 8/16/32/64, a rank above
+ *       4, a non-power-of-two q_G).  Every shape within the kpa_dims limits
+ *       runs on one of the two paths; results agree within the stated
+ *       tolerances.
+ */
 const char* kpa_decode_path(const kpa_dims* dims, int32_t n_q);
 
 #ifdef __cplusplus
