@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "kpa_common.hpp"
 #include "kpa_dispatch.hpp"
@@ -296,6 +297,71 @@ int kpa_append_decode(const kpa_dims* dims, void* cache, int32_t batch, int32_t 
     const AppendInputs app{a_k, b_k, a_v, b_v, positions, slot0, n_new};
     return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causal, false, q, nullptr, nullptr, 0,
                          q_pos, out, lse, workspace, workspace_bytes, num_splits, dev_status, stream, &app);
+}
+
+}  // extern "C"
+
+// Scratch of kpa_append_decode_noalloc (the split-KV partials): one array of
+// KPA_NOALLOC_SCRATCH_BYTES per device, for the life of the process.  In host
+// code `scratch` names a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[KPA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (its address set up on first use).
+int scratch_of_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KPA_ERR_HIP;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KPA_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return KPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kpa_append_decode_noalloc(const kpa_dims* dims, void* cache, int32_t batch, int32_t capacity,
+                              const void* a_k, const void* b_k, const void* a_v, const void* b_v,
+                              const int32_t* positions, const int32_t* slot0, int32_t n_new,
+                              const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
+                              const float* q, const int32_t* q_pos, float* out, float* lse,
+                              int32_t num_splits, uint32_t* dev_status, void* stream) {
+    int st = check_decode_args(dims, batch, capacity, max_ctx, n_q);
+    if (st != KPA_OK) {
+        t_kernel_events = KernelEvents{};  // a pending measurement request applies to this call only
+        return st;
+    }
+    const Plan plan = plan_decode(*dims, batch, max_ctx, n_q, num_splits, num_cus());
+    void* ws = nullptr;
+    if (plan.workspace_bytes > 0) {
+        if (plan.workspace_bytes > KPA_NOALLOC_SCRATCH_BYTES) {
+            t_kernel_events = KernelEvents{};
+            return KPA_ERR_WORKSPACE;
+        }
+        st = scratch_of_current_device(&ws);
+        if (st != KPA_OK) {
+            t_kernel_events = KernelEvents{};
+            return st;
+        }
+    }
+    const AppendInputs app{a_k, b_k, a_v, b_v, positions, slot0, n_new};
+    return decode_common(dims, cache, batch, capacity, ctx_len, max_ctx, n_q, causal, false, q, nullptr, nullptr, 0,
+                         q_pos, out, lse, ws, ws ? (size_t)KPA_NOALLOC_SCRATCH_BYTES : 0, num_splits, dev_status,
+                         stream, &app);
 }
 
 const char* kpa_status_string(int status) {

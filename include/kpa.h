@@ -283,6 +283,32 @@ int kpa_append_decode(const kpa_dims* dims, void* cache, int32_t batch, int32_t 
                       void* workspace, size_t workspace_bytes, int32_t num_splits,
                       uint32_t* dev_status, void* stream);
 
+/* Device scratch of kpa_append_decode_noalloc, per GPU (32 MiB). */
+#define KPA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * kpa_append_decode_noalloc -- kpa_append_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without
+ * workspace / workspace_bytes; the split-KV partials live in a static
+ * device array of KPA_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends (its address is looked up once per
+ * device, on that device's first call).  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  Results and cache
+ * bytes equal kpa_append_decode's with the same num_splits.  Returns as
+ * kpa_append_decode, and KPA_ERR_WORKSPACE (nothing launched) when the
+ * partials of this call would exceed KPA_NOALLOC_SCRATCH_BYTES
+ * (kpa_decode_workspace_bytes() tells the size).  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ */
+int kpa_append_decode_noalloc(const kpa_dims* dims, void* cache, int32_t batch, int32_t capacity,
+                              const void* a_k, const void* b_k, const void* a_v, const void* b_v,
+                              const int32_t* positions, const int32_t* slot0, int32_t n_new,
+                              const int32_t* ctx_len, int32_t max_ctx, int32_t n_q, int32_t causal,
+                              const float* q, const int32_t* q_pos, float* out, float* lse,
+                              int32_t num_splits, uint32_t* dev_status, void* stream);
+
 /*
  * kpa_time_next_decode_kernel -- measurement hook.  start_event and
  * stop_event are hipEvent_t handles created by the caller with timing

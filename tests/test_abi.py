@@ -275,3 +275,21 @@ def test_vector_alu_path_outside_the_family(shape):
 def test_matrix_core_path_for_several_queries(shape):
     dims = kpa.make_dims(*shape)
     assert kpa.kpa_decode_path(dims, 16) == "mfma_bf16"
+
+
+def test_noalloc_scratch_limit_matches_binding_and_is_enforced_before_launch():
+    text = open(os.path.join(ROOT, "include", "kpa.h")).read()
+    m = re.search(r"#define KPA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == kpa.KPA_NOALLOC_SCRATCH_BYTES
+    lib = kpa.load()
+    d = ctypes.byref(kpa.make_dims(4, 4, 8, 16, 2, 2))
+    # 256 sequences x 64 chunks of partials (136 MB) exceed the scratch: refused before anything runs
+    need = lib.kpa_decode_workspace_bytes(d, 256, 65536, 1, 64)
+    assert need > kpa.KPA_NOALLOC_SCRATCH_BYTES
+    st = lib.kpa_append_decode_noalloc(d, FAKE, 256, 65536, None, None, None, None, None, None, 0, FAKE, 65536, 1,
+                                       1, FAKE, FAKE, FAKE, None, 64, None, None)
+    assert st == -4  # KPA_ERR_WORKSPACE
+    # argument errors come first, as for kpa_append_decode
+    st = lib.kpa_append_decode_noalloc(d, FAKE, 1, 64, None, None, None, None, None, None, 0, FAKE, 65, 1,
+                                       1, FAKE, FAKE, FAKE, None, 0, None, None)
+    assert st == -7  # KPA_ERR_INVALID_ARG (max_ctx > capacity)
