@@ -739,11 +739,15 @@ def cpu_baseline_project(cfg, x, w, positions, max_tokens=256):
     return ms / (time.perf_counter() - t0)
 
 
-def _time_decode_shape(kpa, cfg, g, dev):
+def _time_decode_shape(kpa, cfg, g, dev, r_q=0):
     """Fill a cache of cfg's shape (factors drawn on the GPU with cfg's
-    deviations, written by kpa_cache_append in chunks), then time kpa_decode
+    deviations, written by kpa_cache_append in chunks), then time the decode
     of one query per sequence at the last position: medians of 10 calls after
-    at least 30 ms of untimed ones.  Returns (kernel us, call us, kernel GB/s)."""
+    at least 30 ms of untimed ones.  The query is dense (kpa_decode); with
+    r_q > 0 the same cache is also decoded with a factored query of rank r_q
+    (kpa_decode_factored; factors scaled so the expanded query has
+    unit-variance elements).  Returns (kernel us, call us, kernel GB/s), or a
+    pair of them (dense, factored) when r_q > 0."""
     import numpy as np
     import torch
 
@@ -770,35 +774,48 @@ def _time_decode_shape(kpa, cfg, g, dev):
     lse = torch.empty((nb, h), device=dev)
     ws = kpa.alloc_workspace(dims, nb, ctx, device=dev)
 
-    def decode():
+    def dense():
         kpa.kpa_decode(dims, cache, nb, ctx, ctx_len, ctx, q, q_pos, out, lse, ws)
 
-    # at least 30 ms of calls before timing (clocks settle; no idle gap after)
-    t_w, n_w = time.perf_counter(), 0
-    while n_w < 3 or time.perf_counter() - t_w < 0.03:
-        decode()
-        n_w += 1
-        if n_w % 20 == 0:
-            torch.cuda.synchronize()
-    reps = 10
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for a, b in kev + cev:
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    for k in range(reps):
-        kpa.kpa_time_next_decode_kernel(*kev[k])
-        cev[k][0].record()
-        decode()
-        cev[k][1].record()
-    torch.cuda.synchronize()
-    kern = float(np.median([a.elapsed_time(b) for a, b in kev])) * 1e3
-    call = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
-    gbs = (nb * ctx * cfg.bytes_per_token) / (kern * 1e-6) / 1e9
+    def timed(decode):
+        # at least 30 ms of calls before timing (clocks settle; no idle gap after)
+        t_w, n_w = time.perf_counter(), 0
+        while n_w < 3 or time.perf_counter() - t_w < 0.03:
+            decode()
+            n_w += 1
+            if n_w % 20 == 0:
+                torch.cuda.synchronize()
+        reps = 10
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in kev + cev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        for k in range(reps):
+            kpa.kpa_time_next_decode_kernel(*kev[k])
+            cev[k][0].record()
+            decode()
+            cev[k][1].record()
+        torch.cuda.synchronize()
+        kern = float(np.median([a.elapsed_time(b) for a, b in kev])) * 1e3
+        call = float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e3
+        return kern, call, (nb * ctx * cfg.bytes_per_token) / (kern * 1e-6) / 1e9
+
+    res = timed(dense)
+    if r_q > 0:
+        s_f = (r_q ** 0.5) ** 0.5
+        a_q = (torch.randn((nb, 1, r_q, cfg.p1, cfg.q1), generator=g, device=dev) * s_f).contiguous()
+        b_q = (torch.randn((nb, 1, r_q, cfg.p2, cfg.q2), generator=g, device=dev) * s_f).contiguous()
+        qp1, out1, lse1 = q_pos.view(nb, 1), out.view(nb, 1, h, dh), lse.view(nb, 1, h)
+
+        def factored():
+            kpa.kpa_decode_factored(dims, r_q, cache, nb, ctx, ctx_len, ctx, 1, 1, a_q, b_q, qp1, out1, lse1, ws)
+
+        res = (res, timed(factored))
     del cache, ws
     torch.cuda.empty_cache()
-    return kern, call, gbs
+    return res
 
 
 def _write_table(args, lines):
@@ -810,16 +827,19 @@ def _write_table(args, lines):
 
 
 def sweep_flashtpa(args):
-    """Decode kernel time over FlashTPA's benchmark grid (TPA split, d_h = 64,
-    R_K = R_V = 1; heads x batch x sequence length).  Factors and queries are
-    drawn on the GPU from a seeded generator (no oracle here: the same shapes
-    are parity-tested at small sizes); the cache is filled by kpa_cache_append
-    before timing.  One line per shape: kernel and whole-call time (decode +
-    merge), cached tokens/s and the kernel's HBM roofline fraction."""
+    """Decode over FlashTPA's benchmark grid as the TPA summary page states it
+    (TPA split, d_h = 64, R_K = R_V = 1, a factored query of rank R_Q = 16;
+    h = 16 / 32 / 48, i.e. d_model 1024 / 2048 / 3072; batch 1, 2, 4, 8, 16;
+    2^12 .. 2^19 cached tokens per sequence), with the dense query beside it.
+    Factors and queries are drawn on the GPU from a seeded generator (no
+    oracle here: the same shapes are parity-tested at small sizes); the cache
+    is filled by kpa_cache_append before timing.  One line per shape: kernel
+    times of both query forms, the factored call's time (decode + merge),
+    cached tokens/s and the factored kernel's HBM roofline fraction."""
     import torch
 
     import factorized_kv_cache_kpa_amd as kpa
-    from workloads import FLASHTPA_BATCHES, FLASHTPA_HEADS, FLASHTPA_SEQS, flashtpa_config
+    from workloads import FLASHTPA_BATCHES, FLASHTPA_HEADS, FLASHTPA_RQ, FLASHTPA_SEQS, flashtpa_config
 
     kpa.load()
     dev = "cuda"
@@ -828,13 +848,16 @@ def sweep_flashtpa(args):
     for h in FLASHTPA_HEADS:
         for nb in FLASHTPA_BATCHES:
             for ctx in FLASHTPA_SEQS:
-                kern, call, gbs = _time_decode_shape(kpa, flashtpa_config(h, nb, ctx), g, dev)
-                rows.append((h, nb, ctx, kern, call, nb * ctx / (call * 1e-6), gbs))
-                log(f"h={h} batch={nb} seq={ctx}: kernel {kern:.1f} us, call {call:.1f} us, {gbs:.0f} GB/s")
-    lines = ["| h | batch | seq | decode kernel us | call (kernel + merge) us | cached tokens/s | kernel GB/s | of 8 TB/s |",
-             "|---|---|---|---|---|---|---|---|"]
-    for h, nb, ctx, kern, call, tps, gbs in rows:
-        lines.append(f"| {h} | {nb} | {ctx} | {kern:.1f} | {call:.1f} | {tps:.3e} | {gbs:.0f} | "
+                (kd, _, _), (kf, cf, gbs) = _time_decode_shape(kpa, flashtpa_config(h, nb, ctx), g, dev,
+                                                              r_q=FLASHTPA_RQ)
+                rows.append((h, nb, ctx, kd, kf, cf, nb * ctx / (cf * 1e-6), gbs))
+                log(f"h={h} batch={nb} seq={ctx}: dense {kd:.1f} us, factored {kf:.1f} us (call {cf:.1f}), "
+                    f"{gbs:.0f} GB/s")
+    lines = [f"| h | batch | seq | dense-query kernel us | factored-query (R_Q = {FLASHTPA_RQ}) kernel us | "
+             "factored call (kernel + merge) us | cached tokens/s (factored call) | factored kernel GB/s | "
+             "of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for h, nb, ctx, kd, kf, cf, tps, gbs in rows:
+        lines.append(f"| {h} | {nb} | {ctx} | {kd:.1f} | {kf:.1f} | {cf:.1f} | {tps:.3e} | {gbs:.0f} | "
                      f"{100 * gbs / HBM_PEAK_GBPS:.1f}% |")
     _write_table(args, lines)
 

@@ -353,14 +353,27 @@ __device__ __forceinline__ void query_group8(const Geo& g, const DecodeParams& P
     const float* f = fs + row * P.r_q * F_SET + iF * QF + jF0;
     const float* gp = gs + row * P.r_q * G_SET + iG * g.qg + jG;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < P.r_q; ++r) {
-        const float gv = gp[(int64_t)r * G_SET];
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(f + (int64_t)r * F_SET);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(f + (int64_t)r * F_SET + 4);
+    // four ranks per round: their loads are all issued before the first
+    // multiply-add, so a rank-16 query costs four memory round trips, not 16
+    constexpr int RB = 4;
+    for (int r0 = 0; r0 < P.r_q; r0 += RB) {
+        float gv[RB];
+        f32x4 lo[RB], hi[RB];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            acc[k] = fmaf(gv, lo[k], acc[k]);
-            acc[4 + k] = fmaf(gv, hi[k], acc[4 + k]);
+        for (int t = 0; t < RB; ++t) {
+            const int r = min(r0 + t, P.r_q - 1);  // past the last rank: reloads it, weight 0 below
+            gv[t] = gp[(int64_t)r * G_SET];
+            lo[t] = *reinterpret_cast<const f32x4*>(f + (int64_t)r * F_SET);
+            hi[t] = *reinterpret_cast<const f32x4*>(f + (int64_t)r * F_SET + 4);
+        }
+#pragma unroll
+        for (int t = 0; t < RB; ++t) {
+            const float w = r0 + t < P.r_q ? gv[t] : 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc[k] = fmaf(w, lo[t][k], acc[k]);
+                acc[4 + k] = fmaf(w, hi[t][k], acc[4 + k]);
+            }
         }
     }
     const float inv = 1.f / (float)P.r_q;

@@ -88,3 +88,22 @@ def test_factored_query_full_size_every_row(gpu_lib):
     q = kpa_ref.query_from_factors(a_q.numpy(), b_q.numpy())
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len, q, inp.q_pos)
     assert_close(go, gl, ro, rl, cfg.dtype, "kpa_32k factored full size", scale=scale_of(inp, q=q))
+
+
+@pytest.mark.parametrize("h", [16, 32, 48])
+def test_flashtpa_shapes_with_a_rank_16_factored_query(gpu_lib, h):
+    """FlashTPA's decoding benchmark as the TPA summary page states it: TPA
+    split, d_h = 64, R_K = R_V = 1 and a factored query of rank R_Q = 16
+    (batches of ragged contexts over several chunks)."""
+    from workloads import FLASHTPA_RQ, flashtpa_config
+    cfg = flashtpa_config(h, 3, 2500)
+    inp = make_inputs(cfg, seed=33, ragged=True)
+    a_q, b_q = make_query_factors(cfg, FLASHTPA_RQ, seed=33, n_q=1)
+    dims = dims_of(cfg)
+    assert kpa.kpa_decode_path(dims, 1) == "mfma_bf16"
+    cache, cap = fill_cache(inp, dims)
+    q = kpa_ref.query_from_factors(a_q.numpy(), b_q.numpy())
+    ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len, q, inp.q_pos)
+    for s in (0, 6):
+        go, gl = _run(inp, dims, cache, cap, a_q, b_q, num_splits=s)
+        assert_close(go, gl, ro, rl, cfg.dtype, f"flashtpa h={h} R_Q={FLASHTPA_RQ} splits={s}", scale=scale_of(inp, q=q))

@@ -97,8 +97,9 @@ SWEEP_SHAPES = [
 # KPA: A_r is h x 1, B_r is 1 x 64.  The pages give no factor distribution;
 # the TPA config's sd 1/8 is used.
 FLASHTPA_HEADS = (16, 32, 48)
-FLASHTPA_SEQS = (1 << 12, 1 << 14, 1 << 16, 1 << 19)
-FLASHTPA_BATCHES = (1, 4, 16)
+FLASHTPA_SEQS = tuple(1 << k for k in range(12, 20))
+FLASHTPA_BATCHES = (1, 2, 4, 8, 16)
+FLASHTPA_RQ = 16  # the benchmark's factored-query rank
 
 
 def headsplit_config(p1: int, p2: int, batch: int, ctx: int) -> Config:
