@@ -119,7 +119,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     kpa.load()
-    cfg = CONFIGS[args.workload]
+    cfg = workload_config(args.workload)
     dev = "cuda"
     dims = kpa.make_dims(cfg.p1, cfg.p2, cfg.q1, cfg.q2, cfg.r_k, cfg.r_v, dtype=cfg.dtype,
                          rope_base=cfg.rope_base)
@@ -388,6 +388,21 @@ def decode_roofline(cfg, tokens, io_bytes, kern_ms, call_ms, path):
     return r
 
 
+def workload_config(name):
+    """A named workload: one of the configurations, or split_<h1>x<h2>, a head
+    split the KPA page ablates (d1 = d2 = 8, R_K = R_V = 2) on 16 sequences of
+    32768 cached tokens."""
+    import re
+
+    from workloads import CONFIGS, headsplit_config
+    if name in CONFIGS:
+        return CONFIGS[name]
+    m = re.fullmatch(r"split_(\d+)x(\d+)", name)
+    if m:
+        return headsplit_config(int(m.group(1)), int(m.group(2)), 16, 32768).scaled(name=name)
+    raise SystemExit(f"unknown workload {name!r}")
+
+
 def kernel_sources_hash():
     import hashlib
     h = hashlib.sha256()
@@ -445,7 +460,7 @@ def _find(dirname, suffix):
 
 
 def _short_kernel(name):
-    name = name.replace("kpa::(anonymous namespace)::", "").replace("(kpa::DecodeParams)", "")
+    name = name.replace("kpa::(anonymous namespace)::", "").replace("kpa::mfma::", "").replace("(kpa::DecodeParams)", "")
     name = name.replace("kpa::(anonymous namespace)::", "")
     return name if len(name) < 110 else name[:107] + "..."
 
@@ -546,8 +561,7 @@ def summarize_pmc(args):
         if "--workload" in c:
             wl = c.split("--workload", 1)[1].split()[0]
     wl = wl or "kpa_32k"
-    from workloads import CONFIGS
-    cfg = CONFIGS[wl]
+    cfg = workload_config(wl)
     n_q = cfg.n_q
     alg = cfg.batch * cfg.ctx * cfg.bytes_per_token + cfg.batch * n_q * cfg.h * (2 * cfg.d_h + 1) * 4
     lines = [f"# HBM traffic of the split-KV decode kernel: {wl}", "",
