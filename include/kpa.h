@@ -364,6 +364,9 @@ const char* kpa_status_string(int status);
  *         - F's head count p_F is at most 8 for one query (4 when the
  *           shape's rows exceed 64 or a rank exceeds 2, or F is 32 or 64
  *           wide) and at most 4 for n_q > 1, and 2 p_G <= 64 for n_q > 1;
+ *         - the kernel's LDS for the shape (two staged tiles of the G
+ *           factors plus per-wave score rows, growing with the rows and
+ *           ranks) fits the 160 KB of a compute unit;
  *       plus the exact shapes the library is tuned for (the workload
  *       configurations, the KPA page's head splits and FlashTPA's shapes).
  *       When both factors qualify, the one giving an even spread of waves
