@@ -9,7 +9,7 @@ namespace mfma {
 // Shapes with an exact instantiation.  Cfg arguments: PG, QG, PF, QF (F = the
 // factor whose feature dimension is contracted on the matrix cores: B for
 // most, A for the multi-query shape and some head splits), R_K, R_V, F is B,
-// queries per wave, query subgroups, waves/SIMD.
+// queries per wave, query subgroups, waves/SIMD[, waves per F head].
 const MfmaKernel* exact_kernels(int* count) {
     static const MfmaKernel tab[] = {
         KPA_MFMA_ENTRY(4, 4, 8, 16, 2, 2, false, 4, 8, 4, 16, 2, 2, true, 1, 1, 3),
@@ -26,15 +26,20 @@ const MfmaKernel* exact_kernels(int* count) {
         // The KPA page's head splits (d1 = d2 = 8, R_K = R_V = 2).  F is the
         // factor with fewer heads (fewer waves, more rows per wave), except for
         // 4 x 5, where four waves per workgroup (F = A) spread evenly over a
-        // CU's four SIMDs (five waves: 46% -> 62% of 8 TB/s measured)
+        // CU's four SIMDs (five waves: 46% -> 62% of 8 TB/s measured), with
+        // registers for three waves per SIMD (61.6 -> 59.6 us).  10 x 2, 2 x 10
+        // and 6 x 2 split each F head's G heads over two waves, so a CU runs 8
+        // (10 x 2: LDS held it to three 2-wave workgroups) and 12 waves instead
+        // of 6 and 8 (75.2 -> 69.4, 75.9 -> 72.2, 48.1 -> 47.0 us at 16 x 32768
+        // tokens, A/B).
         KPA_MFMA_ENTRY(8, 2, 8, 8, 2, 2, false, 8, 8, 2, 8, 2, 2, true, 1, 1, 2),
         KPA_MFMA_ENTRY(4, 4, 8, 8, 2, 2, false, 4, 8, 4, 8, 2, 2, true, 1, 1, 3),
         KPA_MFMA_ENTRY(2, 8, 8, 8, 2, 2, false, 8, 8, 2, 8, 2, 2, false, 1, 1, 2),
-        KPA_MFMA_ENTRY(10, 2, 8, 8, 2, 2, false, 10, 8, 2, 8, 2, 2, true, 1, 1, 2),
-        KPA_MFMA_ENTRY(4, 5, 8, 8, 2, 2, false, 5, 8, 4, 8, 2, 2, false, 1, 1, 2),
-        KPA_MFMA_ENTRY(2, 10, 8, 8, 2, 2, false, 10, 8, 2, 8, 2, 2, false, 1, 1, 2),
+        KPA_MFMA_ENTRY(10, 2, 8, 8, 2, 2, false, 10, 8, 2, 8, 2, 2, true, 1, 1, 2, 2),
+        KPA_MFMA_ENTRY(4, 5, 8, 8, 2, 2, false, 5, 8, 4, 8, 2, 2, false, 1, 1, 3),
+        KPA_MFMA_ENTRY(2, 10, 8, 8, 2, 2, false, 10, 8, 2, 8, 2, 2, false, 1, 1, 2, 2),
         KPA_MFMA_ENTRY(5, 5, 8, 8, 2, 2, false, 5, 8, 5, 8, 2, 2, true, 1, 1, 3),
-        KPA_MFMA_ENTRY(6, 2, 8, 8, 2, 2, false, 6, 8, 2, 8, 2, 2, true, 1, 1, 2),
+        KPA_MFMA_ENTRY(6, 2, 8, 8, 2, 2, false, 6, 8, 2, 8, 2, 2, true, 1, 1, 3, 2),
         KPA_MFMA_ENTRY(4, 3, 8, 8, 2, 2, false, 4, 8, 3, 8, 2, 2, true, 1, 1, 3),
         KPA_MFMA_ENTRY(3, 4, 8, 8, 2, 2, false, 4, 8, 3, 8, 2, 2, false, 1, 1, 3),
         KPA_MFMA_ENTRY(2, 6, 8, 8, 2, 2, false, 6, 8, 2, 8, 2, 2, false, 1, 1, 2),

@@ -79,11 +79,13 @@ __host__ __device__ __forceinline__ int ilog2(int x) {
 
 // Exact shape: G factor PG x QG, F factor PF x QF, ranks RK, RV; F_IS_B: F
 // is B (else A); NQW queries per wave, NQG query subgroups per workgroup; MW
-// waves per SIMD the registers must allow.
-template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int NQW, int NQG, int MW>
+// waves per SIMD the registers must allow; RS waves share one F head, each
+// taking PG / RS of the G heads (the tile's G factors in LDS serve them all).
+template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int NQW, int NQG, int MW, int RS = 1>
 struct Cfg {
     static constexpr bool GEN = false;
     static constexpr int PG_ = PG, QG_ = QG, PF_ = PF, QF_ = QF, RK_ = RK, RV_ = RV;
+    static constexpr int RS_ = RS, PGW_ = PG / RS;    // G heads per wave
     static constexpr bool F_IS_B_ = F_IS_B;
     static constexpr int RKC = RK, RVC = RV;          // register arrays per rank
     // Kernels with one query per workgroup serve single-query decode, where a
@@ -95,12 +97,13 @@ struct Cfg {
     static constexpr int NQW_ = NQW;                 // queries per wave
     static constexpr int NQG_ = NQG;                 // query subgroups per workgroup
     static constexpr int QPW = NQW * NQG;            // queries per workgroup
-    static constexpr int WAVES = PF * NQG;
+    static constexpr int WAVES = PF * RS * NQG;
     static constexpr int WAVES_MAX = WAVES;
     static constexpr int MIN_WAVES = MW;
-    static constexpr int M = PG * QG;                // rows (iG, jG) per query
-    static constexpr int MB32 = (M + 31) / 32;       // score MFMA row blocks (rows past M are zero)
-    static constexpr int MB16 = (M + 15) / 16;       // value MFMA row blocks
+    static constexpr int M = PG * QG;                // rows (iG, jG) per query in a tile's G factors
+    static constexpr int MR = PGW_ * QG;             // rows of one wave
+    static constexpr int MB32 = (MR + 31) / 32;      // score MFMA row blocks (rows past MR are zero)
+    static constexpr int MB16 = (MR + 15) / 16;      // value MFMA row blocks
     // An 8-wide F feature dimension takes one 16-wide K step: the bf16 hi part
     // of the query in the lower K half, its lo part in the upper half, and the
     // F factor in both (so one MFMA forms (hi + lo) . F).
@@ -118,7 +121,7 @@ struct Cfg {
     static constexpr int G_BLOCKS = GK_BLOCKS + GV_BLOCKS;
     // softmax: NQW*PG (query, head) rows per wave, padded to a power of two,
     // spread over 64 lanes
-    static constexpr int ROWS = NQW * PG;
+    static constexpr int ROWS = NQW * PGW_;
     static constexpr int ROWS_P = pow2_at_least(ROWS);
     static constexpr int GROUPS = 64 / ROWS_P;       // lanes per row
     static constexpr int TPG = 32 / GROUPS;          // slots per lane
@@ -129,7 +132,8 @@ struct Cfg {
     static_assert(QF == 8 || QF == 16 || QF == 32 || QF == 64, "the MFMA-side feature dimension must be 8, 16, 32 or 64");
     static_assert(QG == 1 || QG == 2 || QG == 4 || QG == 8 || QG == 16 || QG == 32,
                   "G-side feature dimension 1, 2, 4, 8, 16 or 32");
-    static_assert(M % 4 == 0, "rows (iG, jG) come in groups of four");
+    static_assert(PG % RS == 0, "the G heads split evenly over a head's waves");
+    static_assert(MR % 4 == 0, "rows (iG, jG) come in groups of four");
     static_assert(ROWS_P <= 64 && ROWS_P >= 2, "query-head rows of a wave must fit 64 lanes");
     static_assert((F_IS_B ? QF : QG) <= 64, "rotary table holds 32 pairs");
     static_assert(RK <= 4 && RV <= 4, "ranks up to 4");
@@ -158,6 +162,7 @@ struct GenCfg {
     static constexpr int ZS = 36;  // score scratch row stride (floats)
     // placeholders of the exact-only names (never read on the generic path)
     static constexpr int PG_ = 0, QG_ = 0, PF_ = 0, RK_ = 0, RV_ = 0, TPG = 1, ROWS_P = 2, WAVES = 0;
+    static constexpr int RS_ = 1, PGW_ = 0;
     static constexpr int GK_BYTES = 0, GV_BYTES = 0, GK_BLOCKS = 0, G_BLOCKS = 0;
     static constexpr bool F_IS_B_ = true;
     static_assert(QF == 8 || QF == 16 || QF == 32 || QF == 64, "the MFMA-side feature dimension must be 8, 16, 32 or 64");
@@ -168,6 +173,7 @@ struct GenCfg {
 // values read from the launch parameters for a generic one.
 struct Geo {
     int pg, pf, qg, lqg, m, h, rk, rv;
+    int rs, pgw, mr;  // waves per F head, G heads and rows per wave
     bool fb;      // F is B
     int qrot;     // feature dimension of B (the rotary pairs)
     int gk_bytes, gv_bytes, gkb, gb;  // G key/value sets per tile; 1 KB blocks (key, total)
@@ -188,6 +194,8 @@ __host__ __device__ __forceinline__ Geo make_geo(const kpa_dims& d, int f_is_b) 
         g.fb = S::F_IS_B_;
         g.lqg = ilog2(S::QG_);
         g.rows_p = S::ROWS_P;
+        g.rs = S::RS_;
+        g.pgw = S::PGW_;
     } else {
         g.fb = f_is_b != 0;
         g.pg = g.fb ? d.p1 : d.p2;
@@ -198,8 +206,11 @@ __host__ __device__ __forceinline__ Geo make_geo(const kpa_dims& d, int f_is_b) 
         g.lqg = ilog2(g.qg);
         g.rows_p = pow2_ceil(S::NQW_ * g.pg);
         if (g.rows_p < 2) g.rows_p = 2;
+        g.rs = 1;
+        g.pgw = g.pg;
     }
     g.m = g.pg * g.qg;
+    g.mr = g.pgw * g.qg;
     g.h = g.pg * g.pf;
     g.qrot = g.fb ? S::QF_ : g.qg;
     g.gk_bytes = (g.rk * g.m + 7) / 8 * 512;
@@ -210,8 +221,8 @@ __host__ __device__ __forceinline__ Geo make_geo(const kpa_dims& d, int f_is_b) 
     g.set_fk = g.fb ? 1 : 0;
     g.set_gv = g.fb ? 2 : 3;
     g.set_fv = g.fb ? 3 : 2;
-    g.waves = g.pf * S::NQG_;
-    g.rows = S::NQW_ * g.pg;
+    g.waves = g.pf * g.rs * S::NQG_;
+    g.rows = S::NQW_ * g.pgw;
     g.groups = 64 / g.rows_p;
     g.tpg = 32 / g.groups;
     return g;
@@ -387,8 +398,9 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
     constexpr int RKC = S::RKC, RVC = S::RVC;
     const Geo G = make_geo<S>(P.d, P.f_is_b);
     // whole row blocks: the bounds checks on rows vanish at compile time
-    constexpr bool kFull32 = !S::GEN && S::PG_ * S::QG_ % 32 == 0, kFull16 = !S::GEN && S::PG_ * S::QG_ % 16 == 0;
-    const int M = G.m, PG = G.pg, QG = G.qg;
+    constexpr bool kFull32 = !S::GEN && S::PGW_ * S::QG_ % 32 == 0, kFull16 = !S::GEN && S::PGW_ * S::QG_ % 16 == 0;
+    // M, PG: this wave's rows and G heads; MT: rows of the tile's G factors
+    const int M = G.mr, PG = G.pgw, QG = G.qg, MT = G.m;
 
     // LDS: static arrays for the exact kernels, one dynamic region for the
     // generic ones
@@ -426,7 +438,9 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
     auto cs_at = [&](int nq, int m, int k) -> float& { return cs_base[(nq * 32 + m) * 2 + k]; };
 
     const int iF = wave % G.pf;
-    const int qsub = wave / G.pf;
+    const int rsub = (wave / G.pf) % G.rs;  // which G heads of F head iF
+    const int qsub = wave / (G.pf * G.rs);
+    const int iG0 = rsub * PG, m0 = rsub * M;  // first G head, first tile row of this wave
     const int half = lane >> 5;
     const int s = lane & 31;       // slot within the tile for the score side
     const int l16 = lane & 15;
@@ -477,7 +491,7 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
             for (int mb = 0; mb < MB32; ++mb) {
                 const int R = mb * 32 + s;
                 const bool row_ok = kFull32 || R < M;
-                const int iG = row_ok ? R / QG : 0, jG = row_ok ? R % QG : 0;
+                const int iG = iG0 + (row_ok ? R / QG : 0), jG = row_ok ? R % QG : 0;
                 const float* src = P.q + (qrow * G.h + G.head(iG, iF)) * (QG * QF) + feat<S>(G, jG, S::K8 ? 0 : 8 * half);
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
@@ -527,7 +541,7 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
         for (int mb = 0; mb < MB32; ++mb) {
             const int R = mb * 32 + s;
             const bool row_ok = kFull32 || R < M;  // padding rows of the last block are zero
-            const int iG = row_ok ? R >> G.lqg : 0, jG = row_ok ? R & (QG - 1) : 0;
+            const int iG = iG0 + (row_ok ? R >> G.lqg : 0), jG = row_ok ? R & (QG - 1) : 0;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
                 // the 8 query elements (jG, jF0 .. jF0 + 7) of this lane and
@@ -645,10 +659,11 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
             for (int r = 0; r < RKC; ++r) {
                 if (r >= G.rk) continue;
                 // this lane's G values for its rows, shared by every query:
-                // element e0 = r*M + mb*32 + 8a + 4half, four consecutive
-                // ones in one 16-byte chunk; the lane's part of the address
-                // is per rank, the (mb, a) part a constant offset
-                const int e_lane = r * M + 4 * half;
+                // element e0 = r*MT + m0 + mb*32 + 8a + 4half, four
+                // consecutive ones in one 16-byte chunk (m0 is a multiple of
+                // 4); the lane's part of the address is per rank, the (mb, a)
+                // part a constant offset
+                const int e_lane = r * MT + m0 + 4 * half;
                 const uint8_t* gk_lane = gcur + (e_lane >> 3) * 512 + s * 16 + (e_lane & 7) * 2;
                 float gx[4][4];
 #pragma unroll
@@ -887,10 +902,10 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
                     if (r >= G.rv) continue;
                     float gvf[8];
                     if (row_ok) {
-                        // element row e = r*M + mb*16 + l16 of the value set; its
-                        // chunk swizzle depends on bits 1-2 of e, which mb*16
-                        // leaves alone: a per-rank lane address plus mb KB
-                        const int e_lane = r * M + l16;
+                        // element row e = r*MT + m0 + mb*16 + l16 of the value
+                        // set; its chunk swizzle depends on bits 1-2 of e, which
+                        // mb*16 leaves alone: a per-rank lane address plus mb KB
+                        const int e_lane = r * MT + m0 + l16;
                         const uint8_t* gv_lane = gvbase + e_lane * 64 + ((g16 ^ ((e_lane >> 1) & 3)) * 16);
                         unpack_bf16x8(*reinterpret_cast<const bf16x8*>(gv_lane + mb * 1024), gvf);
                     } else {
@@ -992,7 +1007,7 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
                 const int R = mb * 16 + 4 * g16 + c;
                 if (R >= M) continue;
                 const int iG = R >> G.lqg, jG = R & (QG - 1);
-                const int i = G.head(iG, iF);
+                const int i = G.head(iG0 + iG, iF);
                 const float l = l_fin[u * PG + iG];
 #pragma unroll
                 for (int nb = 0; nb < KC; ++nb) {
@@ -1007,7 +1022,7 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
             }
         }
         if (lane < PG) {
-            const int i = G.head(lane, iF);
+            const int i = G.head(iG0 + lane, iF);
             const float m = m_fin[u * PG + lane], l = l_fin[u * PG + lane];
             if (P.n_split == 1) {
                 if (P.lse) P.lse[row * H + i] = l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
