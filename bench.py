@@ -293,6 +293,9 @@ def main():
     roofline = decode_roofline(cfg, tokens, q.numel() * 4 + out.numel() * 4 + lse.numel() * 4 + app_bytes,
                                float(kern_ms.mean()), float(call_ms.mean()) if call_ev else None,
                                kpa.kpa_decode_path(dims, n_q))
+    # the roofline takes the average launch (what rocprofv3's average reports);
+    # the median of the same samples, for comparison
+    roofline["launch_us_median"] = round(float(np.median(kern_ms)) * 1e3, 2)
     if stream_gbps:
         roofline["stream_read_gbps"] = round(stream_gbps, 1)
         roofline["hbm_frac_of_stream_read"] = round(roofline["hbm_gbps"] / stream_gbps, 4)
@@ -756,8 +759,8 @@ def cpu_baseline_project(cfg, x, w, positions, max_tokens=256):
 def _time_decode_shape(kpa, cfg, g, dev, r_q=0):
     """Fill a cache of cfg's shape (factors drawn on the GPU with cfg's
     deviations, written by kpa_cache_append in chunks), then time the decode
-    of one query per sequence at the last position: medians of 10 calls after
-    at least 30 ms of untimed ones.  The query is dense (kpa_decode); with
+    of one query per sequence at the last position: medians of 30 calls after
+    at least 50 ms of untimed ones.  The query is dense (kpa_decode); with
     r_q > 0 the same cache is also decoded with a factored query of rank r_q
     (kpa_decode_factored; factors scaled so the expanded query has
     unit-variance elements).  Returns (kernel us, call us, kernel GB/s), or a
@@ -792,14 +795,14 @@ def _time_decode_shape(kpa, cfg, g, dev, r_q=0):
         kpa.kpa_decode(dims, cache, nb, ctx, ctx_len, ctx, q, q_pos, out, lse, ws)
 
     def timed(decode):
-        # at least 30 ms of calls before timing (clocks settle; no idle gap after)
+        # at least 50 ms of calls before timing (clocks settle; no idle gap after)
         t_w, n_w = time.perf_counter(), 0
-        while n_w < 3 or time.perf_counter() - t_w < 0.03:
+        while n_w < 3 or time.perf_counter() - t_w < 0.05:
             decode()
             n_w += 1
             if n_w % 20 == 0:
                 torch.cuda.synchronize()
-        reps = 10
+        reps = 30
         kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in kev + cev:

@@ -6,7 +6,7 @@ bit for bit, as kpa_cache_append followed by kpa_decode_multiq on the same
 inputs; and, with the step's tokens in place, the decode must match the
 float64 oracle.  Before the step the new tokens' slots hold other tokens'
 factors, so a step that skipped or misplaced its append would read them.
-Cases cover every kernel shape, new tokens in the first tile of a KV chunk
+Cases cover every kernel shape (head splits included), new tokens in the first tile of a KV chunk
 (one-tile chunks), tokens straddling two chunks, ragged contexts, the
 vector-ALU path (append kernel launched first), an out-of-range slot,
 n_new = 0, more new tokens than queries, and new tokens written past the
@@ -19,7 +19,7 @@ import torch
 import factorized_kv_cache_kpa_amd as kpa
 from oracle import kpa_oracle
 from tests.kpa_testutil import assert_close, dims_of, fill_cache, scale_of
-from workloads import CONFIGS, flashtpa_config, make_inputs
+from workloads import CONFIGS, flashtpa_config, headsplit_config, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -86,11 +86,20 @@ CASES = [
     ("tpa_degenerate", 4, 1000, 1, True, 0),
     ("tiny_f32", 2, 301, 1, True, 0),      # vector-ALU path: append kernel, then decode
     ("flashtpa_h32", 2, 4100, 1, True, 0),
+    ("split_8x2", 3, 1000, 1, True, 0),    # the KPA page's head splits: 8-wide contraction
+    ("split_10x2", 3, 900, 1, True, 0),    # two waves per F head
+    ("split_6x2", 2, 777, 1, False, 25),   # two waves per F head, one-tile chunks
+    ("split_4x5", 2, 1100, 1, True, 0),    # F = A, rows not a multiple of 32
 ]
 
 
 def _cfg(name):
-    return flashtpa_config(32, 2, 4100) if name == "flashtpa_h32" else CONFIGS[name]
+    if name == "flashtpa_h32":
+        return flashtpa_config(32, 2, 4100)
+    if name.startswith("split_"):
+        p1, p2 = (int(x) for x in name[len("split_"):].split("x"))
+        return headsplit_config(p1, p2, 2, 1024)
+    return CONFIGS[name]
 
 
 @pytest.mark.parametrize("name,batch,ctx,n_q,ragged,num_splits", CASES)
