@@ -319,6 +319,12 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu,
         "event_every": max(1, args.event_every), "prewarm_s": args.prewarm_s,
     }
+    if n_q > 1:
+        # (query, cached token) pairs the causal decode scores per second:
+        # query n of a sequence with c cached tokens sees c - n_q + n + 1
+        cl = inp.ctx_len.to(torch.int64)
+        pairs = sum(int((cl - n_q + n + 1).clamp(min=0).minimum(cl).sum().item()) for n in range(n_q))
+        res["query_token_pairs_per_s"] = round(pairs / (ms_per_step / 1e3), 1)
     line = json.dumps(res)
     print(line, flush=True)
     if args.json_out:
