@@ -363,7 +363,8 @@ const char* kpa_status_string(int status);
  *           unless R_K = 1;
  *         - F's head count p_F is at most 8 for one query (4 when the
  *           shape's rows exceed 64 or a rank exceeds 2, or F is 32 or 64
- *           wide) and at most 4 for n_q > 1, and 2 p_G <= 64 for n_q > 1;
+ *           wide) and at most 4 for n_q > 1; the other factor's head count
+ *           p_G is at most 64 for one query and 32 for n_q > 1;
  *         - the kernel's LDS for the shape (two staged tiles of the G
  *           factors plus per-wave score rows, growing with the rows and
  *           ranks) fits the 160 KB of a compute unit;
