@@ -25,7 +25,8 @@
 // grows) is the blocked online log-sum-exp of FlashTPA decoding ([TPA]).
 //
 // Work split: a workgroup owns one KV chunk of one sequence for a group of
-// queries; its waves are (iF, query subgroup).  The G factors of a tile are
+// queries; its waves are (iF, part of the G heads, query subgroup) -- a tuned
+// shape may split an F head's G heads over two waves.  The G factors of a tile are
 // shared by every wave of the workgroup: they go HBM -> LDS by direct DMA,
 // one tile ahead, double-buffered.  Each wave's F slice goes HBM ->
 // registers, one tile ahead.  No cross-wave reduction: the (query, head)
@@ -119,8 +120,8 @@ struct Cfg {
     static constexpr int GK_BLOCKS = (GK_BYTES + 1023) / 1024;
     static constexpr int GV_BLOCKS = (GV_BYTES + 1023) / 1024;
     static constexpr int G_BLOCKS = GK_BLOCKS + GV_BLOCKS;
-    // softmax: NQW*PG (query, head) rows per wave, padded to a power of two,
-    // spread over 64 lanes
+    // softmax: NQW*PGW_ (query, head) rows per wave, padded to a power of
+    // two, spread over 64 lanes
     static constexpr int ROWS = NQW * PGW_;
     static constexpr int ROWS_P = pow2_at_least(ROWS);
     static constexpr int GROUPS = 64 / ROWS_P;       // lanes per row

@@ -1,7 +1,6 @@
 // General-shape split-KV decode on the vector ALUs (any split/rank within the
 // kpa.h limits, float32 or bfloat16 factors, one or many queries).  Used for
-// float32 caches, for the TPA-degenerate split and for shapes the matrix-core
-// kernels do not cover.
+// float32 caches and for bf16 shapes outside the matrix-core kernels' families.
 //
 // Per (chunk of the cache, query, sequence) one workgroup:
 //   1. rotates the query (dense, or expanded from its Kronecker factors) with
