@@ -217,5 +217,12 @@ bool decode_mfma_supported(const kpa_dims& d, int n_q);
 int decode_mfma_blocks_per_cu(const kpa_dims& d, int n_q);
 int decode_valu_blocks_per_cu(const kpa_dims& d);
 int decode_mfma_query_groups(const kpa_dims& d, int n_q);
+// Multi-query decode with K and V rebuilt per tile on the matrix cores
+// (decode_rebuild.hip): taken from kRebuildMinQ queries per sequence.
+constexpr int kRebuildMinQ = 8;
+hipError_t launch_decode_rebuild(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);
+bool decode_rebuild_supported(const kpa_dims& d, int n_q);
+int decode_rebuild_blocks_per_cu(const kpa_dims& d);
+int decode_rebuild_query_groups(int n_q);
 
 }  // namespace kpa

@@ -7,7 +7,7 @@
 
 namespace kpa {
 
-enum class Path { kUnsupported, kValu, kMfmaSq };
+enum class Path { kUnsupported, kValu, kMfmaSq, kMfmaRebuild };
 
 struct Plan {
     Path path;
@@ -39,11 +39,13 @@ inline const char* path_name(Path p) {
     switch (p) {
         case Path::kValu: return "valu";
         case Path::kMfmaSq: return "mfma_bf16";
+        case Path::kMfmaRebuild: return "mfma_rebuild";
         default: return "";
     }
 }
 
 inline Path select_path(const kpa_dims& d, int32_t n_q) {
+    if (decode_rebuild_supported(d, n_q)) return Path::kMfmaRebuild;
     if (decode_mfma_supported(d, n_q)) return Path::kMfmaSq;
     return Path::kValu;
 }
@@ -63,11 +65,16 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
         // one full round of workgroups: as many as the CUs hold at once (the
         // kernel's occupancy from its registers and LDS, as the runtime
         // reports it; a partial second round would leave most CUs idle)
-        const bool mfma = p.path == Path::kMfmaSq;
-        const int64_t per_cu = mfma ? decode_mfma_blocks_per_cu(d, n_q) : decode_valu_blocks_per_cu(d);
+        const bool mfma = p.path == Path::kMfmaSq, rebuild = p.path == Path::kMfmaRebuild;
+        const int64_t per_cu = rebuild ? decode_rebuild_blocks_per_cu(d)
+                               : mfma  ? decode_mfma_blocks_per_cu(d, n_q)
+                                       : decode_valu_blocks_per_cu(d);
         const int64_t target = per_cu * cus;
-        // workgroups per chunk: one per query group (matrix cores), one per query (VALU)
-        const int64_t wg_rows = mfma ? (int64_t)batch * decode_mfma_query_groups(d, n_q) : rows;
+        // workgroups per chunk: one per query group (matrix cores; the
+        // rebuild kernel also one per A head), one per query (VALU)
+        const int64_t wg_rows = rebuild ? (int64_t)batch * d.p1 * decode_rebuild_query_groups(n_q)
+                                : mfma  ? (int64_t)batch * decode_mfma_query_groups(d, n_q)
+                                        : rows;
         s = wg_rows > 0 ? (target + wg_rows - 1) / wg_rows : 1;
         const int64_t min_tiles_per_chunk = 2;
         const int64_t cap = (tiles + min_tiles_per_chunk - 1) / min_tiles_per_chunk;
@@ -106,6 +113,7 @@ inline hipError_t launch_plan(const Plan& plan, const DecodeParams& P, hipStream
     switch (plan.path) {
         case Path::kValu: return launch_decode_valu(P, s, ev);
         case Path::kMfmaSq: return launch_decode_mfma(P, s, ev);
+        case Path::kMfmaRebuild: return launch_decode_rebuild(P, s, ev);
         default: return hipErrorInvalidValue;
     }
 }

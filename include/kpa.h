@@ -352,7 +352,13 @@ const char* kpa_status_string(int status);
 /*
  * kpa_decode_path -- name of the kernel path the decode entry points run for
  * these dims and n_q, or "" for invalid arguments.  Host only.
- *   "mfma_bf16": the bf16 matrix cores.  Taken by every bf16 cache for which
+ *   "mfma_rebuild": several queries per sequence on the bf16 matrix cores with
+ *       K and V rebuilt per tile from their factors (Eqs. (3)-(4): per token
+ *       and head a sum of R outer products, formed by matrix instructions)
+ *       and plain attention over the rebuilt rows.  Taken for bf16 caches
+ *       with n_q >= 8, q1 = 16, q2 = 8, p2 = 2, 4, 6 or 8, any p1, R_K <= 4
+ *       and R_V <= 4; every rebuilt row then serves 8-16 queries.
+ *   "mfma_bf16": the bf16 matrix cores.  Taken by every other bf16 cache where
  *       one factor -- call it F -- has a feature dimension of 8, 16, 32 or 64
  *       (contracted on the matrix cores) and
  *         - the other factor's feature dimension q_G is 1, 2, 4, 8, 16 or 32;
@@ -373,9 +379,9 @@ const char* kpa_status_string(int status);
  *       When both factors qualify, the one giving an even spread of waves
  *       over a CU's four SIMDs, then fewer padded rows, is chosen.
  *   "valu": the vector ALUs: float32 caches, and bf16 shapes outside the
- *       family above (e.g. no feature dimension of 8/16/32/64, a rank above
+ *       families above (e.g. no feature dimension of 8/16/32/64, a rank above
  *       4, a non-power-of-two q_G).  Every shape within the kpa_dims limits
- *       runs on one of the two paths; results agree within the stated
+ *       runs on one of these paths; results agree within the stated
  *       tolerances.
  */
 const char* kpa_decode_path(const kpa_dims* dims, int32_t n_q);

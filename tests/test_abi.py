@@ -274,7 +274,10 @@ def test_vector_alu_path_outside_the_family(shape):
                                    (8, 2, 16, 16, 2, 2), (3, 4, 16, 2, 2, 2)], ids=lambda s: "x".join(map(str, s)))
 def test_matrix_core_path_for_several_queries(shape):
     dims = kpa.make_dims(*shape)
-    assert kpa.kpa_decode_path(dims, 16) == "mfma_bf16"
+    # q1 = 16, q2 = 8 with an even p2 <= 8 rebuilds K and V per tile
+    rebuild = shape[2] == 16 and shape[3] == 8 and shape[1] in (2, 4, 6, 8)
+    assert kpa.kpa_decode_path(dims, 16) == ("mfma_rebuild" if rebuild else "mfma_bf16")
+    assert kpa.kpa_decode_path(dims, 7) == "mfma_bf16"
 
 
 def test_noalloc_scratch_limit_matches_binding_and_is_enforced_before_launch():

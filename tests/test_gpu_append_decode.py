@@ -116,7 +116,7 @@ def test_fused_step_equals_append_then_decode(gpu_lib, name, batch, ctx, n_q, ra
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
                                inp.q, inp.q_pos, causal=True)
     assert_close(fo.astype(np.float64), fl.astype(np.float64), ro, rl, cfg.dtype, f"{name} fused step",
-                 scale=scale_of(inp))
+                 scale=scale_of(inp), path=kpa.kpa_decode_path(dims, inp.q.shape[1]))
 
 
 def test_fused_step_without_new_tokens_is_the_decode(gpu_lib):
@@ -204,7 +204,7 @@ def test_fused_step_with_more_new_tokens_than_queries(gpu_lib, name, batch, ctx,
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
                                inp.q, inp.q_pos, causal=True)
     assert_close(fo.astype(np.float64), fl.astype(np.float64), ro, rl, cfg.dtype, f"{name} fused step",
-                 scale=scale_of(inp))
+                 scale=scale_of(inp), path=kpa.kpa_decode_path(dims, inp.q.shape[1]))
 
 
 PAST_CASES = [
@@ -244,7 +244,8 @@ def test_fused_step_writes_tokens_past_the_context(gpu_lib, name, batch, ctx, n_
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
                                inp.q, inp.q_pos, causal=True)
     assert_close(res[1][0].astype(np.float64), res[1][1].astype(np.float64), ro, rl, cfg.dtype,
-                 f"{name} step with tokens past the context", scale=scale_of(inp))
+                 f"{name} step with tokens past the context", scale=scale_of(inp),
+                 path=kpa.kpa_decode_path(dims, inp.q.shape[1]))
 
 
 def test_fused_step_flags_a_slot_near_the_int32_limit_like_the_append(gpu_lib):

@@ -54,7 +54,8 @@ def test_factored_query_matches_oracle(gpu_lib, name, batch, ctx, n_q, r_q, ragg
     go, gl = _run(inp, dims, cache, cap, a_q, b_q)
     q = kpa_ref.query_from_factors(a_q.numpy(), b_q.numpy())
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len, q, inp.q_pos)
-    assert_close(go, gl, ro, rl, cfg.dtype, f"{name} factored R_Q={r_q}", scale=scale_of(inp, q=q))
+    assert_close(go, gl, ro, rl, cfg.dtype, f"{name} factored R_Q={r_q}", scale=scale_of(inp, q=q),
+                 path=kpa.kpa_decode_path(dims, n_q))
 
 
 def test_factored_query_equals_dense_decode_of_its_expansion(gpu_lib):

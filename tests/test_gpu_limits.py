@@ -46,7 +46,8 @@ def test_limits_and_degenerate_shapes(gpu_lib, cfg, batch, ctx, n_q, ragged):
     go, gl = run_decode(inp, dims, cache, cap)
     ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len,
                                inp.q, inp.q_pos, causal=True)
-    assert_close(go, gl, ro, rl, cfg.dtype, f"{cfg.name} ({kpa.kpa_decode_path(dims, n_q)})", scale=scale_of(inp))
+    assert_close(go, gl, ro, rl, cfg.dtype, f"{cfg.name} ({kpa.kpa_decode_path(dims, n_q)})", scale=scale_of(inp),
+                 path=kpa.kpa_decode_path(dims, n_q))
 
 
 def test_many_short_sequences(gpu_lib):

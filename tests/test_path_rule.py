@@ -7,7 +7,9 @@ kernel tables: a bf16 shape runs on the matrix cores when it is one of the
 tuned shapes, or when one factor F has a contracted feature dimension of 8,
 16, 32 or 64 and the other factor G meets the row, rank, head-count and LDS
 conditions of a generic family; everything else (and every float32 cache)
-runs on the vector ALUs.
+runs on the vector ALUs.  Several queries per sequence (8 or more) on
+shapes with q1 = 16, q2 = 8, an even p2 up to 8 and ranks up to 4 rebuild K
+and V per tile on the matrix cores instead.
 """
 import random
 
@@ -79,6 +81,8 @@ def _generic_ok(pf, qf, pg, qg, r_k, r_v, multi):
 def documented_path(p1, p2, q1, q2, r_k, r_v, n_q):
     multi = n_q > 1
     shape = (p1, p2, q1, q2, r_k, r_v)
+    if n_q >= 8 and q1 == 16 and q2 == 8 and p2 in (2, 4, 6, 8) and r_k <= 4 and r_v <= 4:
+        return "mfma_rebuild"
     if shape in TUNED and (not multi or shape in TUNED_MULTI):
         return "mfma_bf16"
     if _generic_ok(p2, q2, p1, q1, r_k, r_v, multi) or _generic_ok(p1, q1, p2, q2, r_k, r_v, multi):
@@ -107,7 +111,7 @@ def _random_shapes(n, seed):
 SHAPES = _random_shapes(400, seed=2024)
 
 
-@pytest.mark.parametrize("n_q", [1, 4])
+@pytest.mark.parametrize("n_q", [1, 4, 16])
 def test_library_path_matches_the_documented_rule(n_q):
     mismatches = []
     for shape in SHAPES:
@@ -118,8 +122,19 @@ def test_library_path_matches_the_documented_rule(n_q):
             mismatches.append((shape, got, want))
     assert not mismatches, f"{len(mismatches)} of {len(SHAPES)} differ, e.g. {mismatches[:5]}"
     # the sample covers both paths
-    paths = {kpa.kpa_decode_path(kpa.make_dims(*s), n_q) for s in SHAPES}
-    assert paths == {"mfma_bf16", "valu"}
+    paths = {kpa.kpa_decode_path(kpa.make_dims(*s), n_q) for s in SHAPES + REBUILD_SHAPES}
+    assert paths == ({"mfma_bf16", "valu", "mfma_rebuild"} if n_q >= 8 else {"mfma_bf16", "valu"})
+
+
+# shapes of the rebuild family and its edges (q1 = 16, q2 = 8)
+REBUILD_SHAPES = [(p1, p2, 16, 8, rk, rv) for p1 in (1, 3, 4) for p2 in (1, 2, 3, 4, 6, 8, 10)
+                  for rk, rv in ((1, 1), (4, 4), (2, 3), (5, 2))]
+
+
+@pytest.mark.parametrize("n_q", [1, 7, 8, 16, 64])
+def test_rebuild_family_matches_the_documented_rule(n_q):
+    for shape in REBUILD_SHAPES:
+        assert kpa.kpa_decode_path(kpa.make_dims(*shape), n_q) == documented_path(*shape, n_q), shape
 
 
 def test_float32_caches_take_the_vector_alus():

@@ -59,7 +59,7 @@ def test_noalloc_step_equals_workspace_step(gpu_lib, name, cases):
         assert np.array_equal(ref[1], got[1]) and np.array_equal(ref[2], got[2]), f"{name} call {k}: outputs differ"
         ro, rl = kpa_oracle.decode(inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions, inp.ctx_len, inp.q, inp.q_pos)
         assert_close(got[1].astype(np.float64), got[2].astype(np.float64), ro, rl, cfg.dtype, f"{name} call {k}",
-                     scale=scale_of(inp))
+                     scale=scale_of(inp), path=kpa.kpa_decode_path(dims, nq))
 
 
 def test_noalloc_refuses_a_call_beyond_the_scratch(gpu_lib):
