@@ -86,10 +86,9 @@ struct Lds {
     static constexpr int BV = BK + kTileSlots * B_ROW;
     static constexpr int TILE = BV + kTileSlots * B_ROW;
     // per wave: rebuilt keys [32 slots][16 chunks of 8 features][16 B]
-    static constexpr int KS = 2 * TILE;
     static constexpr int KS_WAVE = kTileSlots * 256;
-    static constexpr int CS = KS + P2 * KS_WAVE;        // rotary cos/sin [16 queries][4 pairs][2]
-    static constexpr int TOTAL = CS + kNQ * 4 * 2 * 4;
+    // two tile buffers, the rebuilt keys and the rotary cos/sin [16 queries][4 pairs][2]
+    static constexpr int TOTAL = 2 * TILE + P2 * KS_WAVE + kNQ * 4 * 2 * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS of one CU");
 };
 
@@ -145,6 +144,7 @@ struct Stage {
     u32x4 v[C::UPT][4];
     uint32_t src[C::UPT];  // byte offset of rank 0 in the tile
     uint32_t dst[C::UPT];  // LDS byte offset
+    int slot[C::UPT];      // the unit's slot (keys) or first of its 8 slots (values)
     int kind[C::UPT];      // wave-uniform
 
     __device__ __forceinline__ void init(const Layout& L, int i1, int p1) {
@@ -156,28 +156,33 @@ struct Stage {
             if (u < C::U_BK) {  // B~^K chunk (r P2 + i2) of slot s
                 const int s = u % kTileSlots, i2 = u / kTileSlots;
                 kd = kBK;
+                slot[k] = s;
                 src[k] = (uint32_t)(L.off[1] + i2 * (kTileSlots * 16) + s * 16);
                 dst[k] = LY::BK + s * LY::B_ROW + i2 * 64;
             } else if (u < C::U_BK + C::U_BV) {  // B^V element (r P2 + i2) q2 + j2, 8 slots
                 const int x = u - C::U_BK;
                 const int sg = x & 3, e = x >> 2;
                 kd = kBV;
+                slot[k] = 8 * sg;
                 src[k] = (uint32_t)(L.off[3] + e * 64 + sg * 16);
                 dst[k] = LY::BV + (8 * sg) * LY::B_ROW + e * 8;
             } else if (u < C::U_BK + C::U_BV + C::U_AK) {  // A^K chunk (r p1 + i1) 2 + hf of slot s
                 const int x = u - C::U_BK - C::U_BV;
                 const int s = x % kTileSlots, hf = x / kTileSlots;
                 kd = kAK;
+                slot[k] = s;
                 src[k] = (uint32_t)(L.off[0] + (i1 * 2 + hf) * (kTileSlots * 16) + s * 16);
                 dst[k] = LY::AK + s * LY::A_ROW + hf * 64;
             } else if (u < C::UNITS) {  // A^V element (r p1 + i1) q1 + j1, 8 slots
                 const int x = u - C::U_BK - C::U_BV - C::U_AK;
                 const int sg = x & 3, j1 = x >> 2;
                 kd = kAV;
+                slot[k] = 8 * sg;
                 src[k] = (uint32_t)(L.off[2] + (i1 * kQ1 + j1) * 64 + sg * 16);
                 dst[k] = LY::AV + (8 * sg) * LY::A_ROW + j1 * 8;
             } else {
                 kd = kNone;
+                slot[k] = 0;
                 src[k] = 0;
                 dst[k] = 0;
             }
@@ -187,7 +192,9 @@ struct Stage {
 
     // Issue the loads of one tile for this thread's units.  Rank r of a unit
     // is r * stride bytes after rank 0: P2 chunks (B~^K), P2 q2 elements
-    // (B^V), 2 p1 chunks (A^K), p1 q1 elements (A^V).
+    // (B^V), 2 p1 chunks (A^K), p1 q1 elements (A^V).  Ranks past the key or
+    // value rank count re-read rank 0 (branch-free, so the loads issue back
+    // to back); store() writes zeros for them.
     __device__ __forceinline__ void load(const uint8_t* tile, int p1, int rk, int rv) {
 #pragma unroll
         for (int k = 0; k < C::UPT; ++k) {
@@ -201,17 +208,38 @@ struct Stage {
                                                 : p1 * kQ1 * 64;
             const uint8_t* p = tile + src[k];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[k][r] = r < nr ? ld16<u32x4>(p + r * stride) : u32x4{0u, 0u, 0u, 0u};
+            for (int r = 0; r < 4; ++r) v[k][r] = ld16<u32x4>(p + (r < nr ? r : 0) * stride);
         }
     }
 
     // Write the loaded units into LDS with the ranks interleaved.
-    __device__ __forceinline__ void store(uint8_t* lds) const {
+    // Slots at or past `valid` (slot index inside the tile; tail tiles only)
+    // are written as zeros: they lie past every query's context and may
+    // hold arbitrary bytes, and a zero softmax weight times a NaN value
+    // would still poison the value sums.
+    __device__ __forceinline__ void store(uint8_t* lds, int rk, int rv, bool tail, int valid) {
         using LY = Lds<P2>;
 #pragma unroll
         for (int k = 0; k < C::UPT; ++k) {
             const int kd = kind[k];
             if (kd == kNone) continue;
+            const bool key = kd == kBK || kd == kAK;
+            const int nr = key ? rk : rv;
+#pragma unroll
+            for (int r = 1; r < 4; ++r)
+                if (r >= nr) v[k][r] = u32x4{0u, 0u, 0u, 0u};
+            if (tail) {
+                u32x4 keep;
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    keep[d] = key ? (slot[k] < valid ? 0xffffffffu : 0u)
+                                  : ((slot[k] + 2 * d < valid ? 0x0000ffffu : 0u) |
+                                     (slot[k] + 2 * d + 1 < valid ? 0xffff0000u : 0u));
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) v[k][r][d] &= keep[d];
+            }
             // o[d]: items 2d and 2d + 1 (j = element or slot 0..7 of the
             // chunks), each as ranks (0, 1) then (2, 3)
             u32x4 o[4];
@@ -245,7 +273,11 @@ __device__ __forceinline__ s16x4 lds8(const uint8_t* p) {
 template <int P2>
 __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams P) {
     using LY = Lds<P2>;
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    // separate LDS objects, so that the compiler can tell the rebuilt keys
+    // (written per tile) from the tile factors (read around those writes)
+    __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * LY::TILE];
+    __shared__ __attribute__((aligned(16))) uint8_t kscr[P2 * LY::KS_WAVE];
+    __shared__ float cs[kNQ * 4 * 2];
     const int lane = threadIdx.x & 63;
     const int i2 = (int)(threadIdx.x >> 6);  // this wave's B head
     const int p1 = P.d.p1;
@@ -277,7 +309,6 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
     if (first < last) stage.load(seq + (int64_t)(first / kTileSlots) * L.tile_bytes, p1, P.d.r_k, P.d.r_v);
 
     // ---- rotated, scaled query as the score MFMA's B operand (hi + lo) -----
-    float* cs = reinterpret_cast<float*>(lds + LY::CS);
     if (threadIdx.x < kNQ * 4) {
         const int nq = threadIdx.x >> 2, m = threadIdx.x & 3;
         const int nn = min(qg * kNQ + nq, P.n_q - 1);
@@ -332,13 +363,13 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
     const int bk = lane >> 2;         // 4x4 block (keys: slot within 16)
     const int g4 = (lane >> 2) & 3;   // values: j1 group
     const int t8 = lane >> 4;         // values: 8-slot group; scores: 4-slot group
-    uint8_t* ks_w = lds + LY::KS + i2 * LY::KS_WAVE;
+    uint8_t* ks_w = kscr + i2 * LY::KS_WAVE;
 
     // tiles: the first one staged before the loop, then one barrier per tile;
     // after it each wave writes the next tile (loaded one tile earlier) into
     // the other buffer and issues the loads of the tile after that
     if (first < last) {
-        stage.store(lds);
+        stage.store(tiles, P.d.r_k, P.d.r_v, first + kTileSlots > vis_max, vis_max - first);
         if (first + kTileSlots < last) stage.load(seq + (int64_t)(first / kTileSlots + 1) * L.tile_bytes, p1, P.d.r_k, P.d.r_v);
     }
     // masking is needed only where some query of the group stops seeing slots
@@ -353,10 +384,11 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
     for (int s0 = first; s0 < last; s0 += kTileSlots, buf ^= LY::TILE) {
         __syncthreads();  // tile s0 is in LDS (buffer buf); every wave is done with the other buffer
         if (s0 + kTileSlots < last) {
-            stage.store(lds + (buf ^ LY::TILE));
+            stage.store(tiles + (buf ^ LY::TILE), P.d.r_k, P.d.r_v, s0 + 2 * kTileSlots > vis_max,
+                        vis_max - (s0 + kTileSlots));
             if (s0 + 2 * kTileSlots < last) stage.load(seq + (int64_t)(s0 / kTileSlots + 2) * L.tile_bytes, p1, P.d.r_k, P.d.r_v);
         }
-        const uint8_t* tl = lds + buf;
+        const uint8_t* tl = tiles + buf;
 
         // ---- keys: K[slot][j1][j2] of head (i1, i2), bf16, into ks_w ----------
 #pragma unroll
@@ -378,36 +410,32 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
 
         // ---- values: V^T rebuilt straight into the value MFMA's A layout --------
         // (independent of the scores: issued before them, so that the two
-        // overlap).  Slots no query of the group sees (past the context) hold
-        // arbitrary bytes: their rebuilt values are zeroed, since a zero
-        // weight times a NaN would still poison the sum.
-        const bool tail = s0 + kTileSlots > vis_max;
+        // overlap; slots past the context were zeroed when staged)
         uint32_t vop[kQ2][4];  // block j2: element e = slot 8 t8 + e of feature j1 = lane & 15
 #pragma unroll
-        for (int u2 = 0; u2 < 4; ++u2) {
-            f32x4 dv[2][2];
+        for (int h2 = 0; h2 < 2; ++h2) {  // slots 8 t8 + 4 h2 + uu
+            s16x4 vy[4], vx0[4], vx1[4];
 #pragma unroll
-            for (int uu = 0; uu < 2; ++uu) {
-                const int s = 8 * t8 + 2 * u2 + uu;
-                const s16x4 y = lds8(tl + LY::AV + s * LY::A_ROW + (4 * g4 + l4) * 8);      // A^V, j1 = 4 g4 + l4
-                const s16x4 x0 = lds8(tl + LY::BV + s * LY::B_ROW + i2 * 64 + l4 * 8);        // B^V, j2 = l4
-                const s16x4 x1 = lds8(tl + LY::BV + s * LY::B_ROW + i2 * 64 + (4 + l4) * 8);  // j2 = 4 + l4
-                const f32x4 zz = {0.f, 0.f, 0.f, 0.f};
-                dv[uu][0] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(x0, y, zz, 0, 0, 0);
-                dv[uu][1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(x1, y, zz, 0, 0, 0);
-                if (tail) {
-                    const bool ok = s0 + s < vis_max;
+            for (int uu = 0; uu < 4; ++uu) {
+                const int s = 8 * t8 + 4 * h2 + uu;
+                vy[uu] = lds8(tl + LY::AV + s * LY::A_ROW + (4 * g4 + l4) * 8);        // A^V, j1 = 4 g4 + l4
+                vx0[uu] = lds8(tl + LY::BV + s * LY::B_ROW + i2 * 64 + l4 * 8);        // B^V, j2 = l4
+                vx1[uu] = lds8(tl + LY::BV + s * LY::B_ROW + i2 * 64 + (4 + l4) * 8);  // j2 = 4 + l4
+            }
+            f32x4 dv[4][2];
+            const f32x4 zz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        dv[uu][0][c] = ok ? dv[uu][0][c] : 0.f;
-                        dv[uu][1][c] = ok ? dv[uu][1][c] : 0.f;
-                    }
-                }
+            for (int uu = 0; uu < 4; ++uu) {
+                dv[uu][0] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(vx0[uu], vy[uu], zz, 0, 0, 0);
+                dv[uu][1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(vx1[uu], vy[uu], zz, 0, 0, 0);
             }
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+            for (int u2 = 0; u2 < 2; ++u2)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) vop[4 * hf + c][u2] = pack2(dv[0][hf][c], dv[1][hf][c]);
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        vop[4 * hf + c][2 * h2 + u2] = pack2(dv[2 * u2][hf][c], dv[2 * u2 + 1][hf][c]);
         }
         wave_lds_sync();  // this wave's keys are in ks_w
 
@@ -541,16 +569,10 @@ struct Kernel {
 template <int P2>
 struct Entry {
     static hipError_t launch(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
-        static std::atomic<bool> attr{false};
-        if (!attr.load(std::memory_order_acquire)) {
-            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(decode_rebuild_kernel<P2>),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, Lds<P2>::TOTAL);
-            attr.store(true, std::memory_order_release);
-        }
         const int split_pad = (P.n_split + kXcds - 1) / kXcds * kXcds;
         const int qgroups = (P.n_q + kNQ - 1) / kNQ;
         dim3 grid(split_pad * P.d.p1, P.batch, qgroups);
-        hipExtLaunchKernelGGL(decode_rebuild_kernel<P2>, grid, dim3(P2 * 64), Lds<P2>::TOTAL, s, ev.start,
+        hipExtLaunchKernelGGL(decode_rebuild_kernel<P2>, grid, dim3(P2 * 64), 0, s, ev.start,
                               ev.stop, 0, P);
         return hipGetLastError();
     }
@@ -558,11 +580,8 @@ struct Entry {
         static std::atomic<int> cached{0};
         int v = cached.load(std::memory_order_relaxed);
         if (v > 0) return v;
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(decode_rebuild_kernel<P2>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, Lds<P2>::TOTAL);
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_rebuild_kernel<P2>, P2 * 64,
-                                                         Lds<P2>::TOTAL) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_rebuild_kernel<P2>, P2 * 64, 0) != hipSuccess ||
             nb <= 0)
             nb = 1;
         cached.store(nb, std::memory_order_relaxed);
