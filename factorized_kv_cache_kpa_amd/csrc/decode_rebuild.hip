@@ -19,28 +19,33 @@
 // which leaves the vector ALUs only conversions and the softmax.
 //
 // Per workgroup: one KV chunk of one sequence, one head group (one A head i1,
-// every B head i2: one wave per i2) and up to 16 queries.  Per 32-slot tile:
+// every B head i2) and up to 16 queries; two waves per B head, each taking
+// 16 of every tile's 32 slots (so a CU runs 16 waves, 4 per SIMD).  Per
+// 32-slot tile:
 //   1. The tile's factors go HBM -> registers (one tile ahead) -> LDS with
 //      their ranks interleaved: element (slot, row, feature) -> 4 ranks in
 //      8 bytes, so each operand of a rebuild MFMA is one 8-byte LDS read.
-//   2. Keys: 16 rebuild MFMAs per wave give K[32 slots][128 features] of its
-//      head in float32; rounded to bf16 and written to the wave's own LDS
-//      rows (16-byte chunks, XOR-swizzled so that the writes and the reads
-//      below spread over the banks).
+//      Double-buffered: one barrier per tile.
+//   2. Keys: 8 rebuild MFMAs per wave give K[16 slots][128 features] of its
+//      head in float32, rounded to bf16.  A rebuild lane holds its slot's
+//      features in registers as the score MFMA needs them, but at a lane
+//      index rotated by two bits; one ds_bpermute per register moves them.
 //   3. Scores: MFMA 16x16x32 with M = 16 slots, N = 16 queries, K = 32
-//      features; the query (rotated, scaled) is carried as bf16 hi + lo, two
-//      MFMAs per K step.  The result holds a query per lane (lane % 16) and
-//      slots in registers and lane bits 4-5.
-//   4. Online softmax per (query, head): the running max is shared by a
-//      query's four lanes (two lane swaps); the weights p = 2^(z - m), in
-//      bf16, are moved into the value MFMA's operand layout by two
-//      permlane swaps (slots into registers and lane bits 4-5).
-//   5. Values: 16 rebuild MFMAs per wave whose outputs already sit in the
+//      features; the query (rotated, scaled) rounded to bf16.  The result
+//      holds a query per lane (lane % 16) and its slots in registers and
+//      lane bits 4-5 -- exactly the B operand layout of the 16x16x16 value
+//      MFMA, so the softmax weights need no data movement.
+//   4. Online softmax per (query, head, wave): the running max is shared by
+//      a query's four lanes (two lane swaps); it moves only when a score
+//      exceeds it by more than 2^8, so the output is rarely rescaled.
+//   5. Values: 8 rebuild MFMAs per wave whose outputs already sit in the
 //      operand layout of the value MFMA (slots on the inner dimension: rebuild
-//      u of 8 covers slot 8 (lane >> 4) + u), then O^T[feature][query] +=
-//      V^T P^T, MFMA 16x16x32, eight per tile (one per j2).
+//      u of 4 covers slot 4 (lane >> 4) + u), then O^T[feature][query] +=
+//      V^T P^T, MFMA 16x16x16, eight per tile (one per j2).
 //   The running output O^T keeps a query per lane (lane % 16), so the rescale
-//   by the softmax correction is a plain multiply.
+//   by the softmax correction is a plain multiply.  At the end of the chunk
+//   the second wave of each head hands its (m, l, O) to the first through
+//   LDS, which combines them as the split-KV merge does.
 // The online softmax and the chunk partials (m, l, o) are those of the other
 // decode kernels (the blocked online log-sum-exp of FlashTPA decoding,
 // "Tensor Product Attention Is All You Need", summary page), merged by the
@@ -49,13 +54,13 @@
 // Shapes: bf16 caches with A's feature dimension q1 = 16 (j1: a lane's 16
 // columns) and B's q2 = 8 (j2: 8 consecutive features, the rotary pairs),
 // ranks up to 4 (missing ranks are zero rows of the inner dimension), B head
-// count p2 = 2, 4, 6 or 8 (one wave each), any A head count p1 (one
+// count p2 = 2, 4, 6 or 8 (two waves each), any A head count p1 (one
 // workgroup each), up to 16 queries per workgroup (more queries: more
 // workgroups per chunk).
 //
-// Precision: bf16 factors exactly; the rebuilt K and V rows and the softmax
-// weights are rounded once to bf16 (relative 2^-8 per element at most,
-// unbiased); the query carries ~16 bits (hi + lo); all sums in float32.
+// Precision: bf16 factors exactly; the rebuilt K and V rows, the rotated
+// query and the softmax weights are each rounded once to bf16 (relative 2^-8
+// per element at most, unbiased); all sums in float32.
 #include <atomic>
 
 #include "kpa_common.hpp"
@@ -85,10 +90,8 @@ struct Lds {
     static constexpr int BK = AV + kTileSlots * A_ROW;
     static constexpr int BV = BK + kTileSlots * B_ROW;
     static constexpr int TILE = BV + kTileSlots * B_ROW;
-    // per wave: rebuilt keys [32 slots][16 chunks of 8 features][16 B]
-    static constexpr int KS_WAVE = kTileSlots * 256;
-    // two tile buffers, the rebuilt keys and the rotary cos/sin [16 queries][4 pairs][2]
-    static constexpr int TOTAL = 2 * TILE + P2 * KS_WAVE + kNQ * 4 * 2 * 4;
+    // two tile buffers and the rotary cos/sin [16 queries][4 pairs][2]
+    static constexpr int TOTAL = 2 * TILE + kNQ * 4 * 2 * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS of one CU");
 };
 
@@ -112,15 +115,9 @@ __device__ __forceinline__ float other32(float x) {
     return (threadIdx.x & 32) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);
 }
 
-// Chunk swizzle of the rebuilt-key rows: chunk c of slot t sits at
-// c ^ swz(t).  swz is a bijection on 0..7 (conflict-free reads of 8 slots
-// at one chunk) with swz(2k) ^ swz(2k+1) = 4 (conflict-free writes of the
-// 4 chunks of 2 slots).
-__device__ __forceinline__ int swz(int t) { return ((t & 1) << 2) | ((t >> 1) & 3); }
-
 template <int P2>
 struct Cfg {
-    static constexpr int WAVES = P2;
+    static constexpr int WAVES = 2 * P2;  // two per B head: slots 0-15 and 16-31 of each tile
     static constexpr int THREADS = WAVES * 64;
     // staging units of one tile (64 B of LDS each, from 4 x 16 B of cache):
     // B~^K (slot, i2), B^V (i2, j2, 8-slot group), A^K (slot, 8-feature
@@ -130,7 +127,7 @@ struct Cfg {
     static constexpr int UPT = (UNITS + THREADS - 1) / THREADS;  // units per thread
     // kinds of unit start at multiples of 64 (one kind per wave): P2 even
     static_assert(P2 >= 2 && P2 <= 8 && P2 % 2 == 0, "one wave per B head: 2, 4, 6 or 8");
-    static_assert(UPT <= 2, "at most two staging units per thread");
+    static_assert(UPT == 1, "one staging unit per thread");
 };
 
 // This thread's staging units of a tile: for each, the four 16-byte source
@@ -271,15 +268,16 @@ __device__ __forceinline__ s16x4 lds8(const uint8_t* p) {
 }
 
 template <int P2>
-__global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams P) {
+__global__ void __launch_bounds__(2 * P2 * 64, 1) decode_rebuild_kernel(DecodeParams P) {
     using LY = Lds<P2>;
     // separate LDS objects, so that the compiler can tell the rebuilt keys
     // (written per tile) from the tile factors (read around those writes)
     __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * LY::TILE];
-    __shared__ __attribute__((aligned(16))) uint8_t kscr[P2 * LY::KS_WAVE];
     __shared__ float cs[kNQ * 4 * 2];
     const int lane = threadIdx.x & 63;
-    const int i2 = (int)(threadIdx.x >> 6);  // this wave's B head
+    const int wave = (int)(threadIdx.x >> 6);
+    const int i2 = wave % P2;   // this wave's B head
+    const int hh = wave / P2;   // and its half of every tile: slots 16 hh .. 16 hh + 15
     const int p1 = P.d.p1;
     const int H = p1 * P2;
     // workgroup -> (chunk, A head): the head groups of a chunk share an XCD,
@@ -308,7 +306,7 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
     stage.init(L, i1, p1);
     if (first < last) stage.load(seq + (int64_t)(first / kTileSlots) * L.tile_bytes, p1, P.d.r_k, P.d.r_v);
 
-    // ---- rotated, scaled query as the score MFMA's B operand (hi + lo) -----
+    // ---- rotated, scaled query as the score MFMA's B operand (bf16) --------
     if (threadIdx.x < kNQ * 4) {
         const int nq = threadIdx.x >> 2, m = threadIdx.x & 3;
         const int nn = min(qg * kNQ + nq, P.n_q - 1);
@@ -322,7 +320,7 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
         for (int k = 0; k < kNQ; ++k)
             if (qg * kNQ + k < P.n_q) clear_merge_counters(P, (int64_t)b * P.n_q + qg * kNQ + k, split);
     __syncthreads();
-    bf16x8 q_hi[4], q_lo[4];
+    bf16x8 q_hi[4];
     {
         const int64_t row = (int64_t)b * P.n_q + min(n, P.n_q - 1);
 #pragma unroll
@@ -350,7 +348,7 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
                 v[2 * m] = q_ok ? (x0 * c - x1 * sn) * P.q_scale : 0.f;
                 v[2 * m + 1] = q_ok ? (x1 * c + x0 * sn) * P.q_scale : 0.f;
             }
-            split_bf16x8(v, q_hi[ks], q_lo[ks]);
+            q_hi[ks] = pack_bf16x8(v);
         }
     }
 
@@ -363,7 +361,16 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
     const int bk = lane >> 2;         // 4x4 block (keys: slot within 16)
     const int g4 = (lane >> 2) & 3;   // values: j1 group
     const int t8 = lane >> 4;         // values: 8-slot group; scores: 4-slot group
-    uint8_t* ks_w = kscr + i2 * LY::KS_WAVE;
+    const int sb = 16 * hh;           // this wave's first slot of each tile
+    // per-lane LDS offsets of the tile reads (inside a tile buffer) and of
+    // the rebuilt keys; the loop adds constants only
+    const int a_bk = LY::BK + (sb + bk) * LY::B_ROW + i2 * 64 + l4 * 8;
+    const int a_ak = LY::AK + (sb + bk) * LY::A_ROW + l4 * 8;
+    const int a_av = LY::AV + (sb + 4 * t8) * LY::A_ROW + (4 * g4 + l4) * 8;
+    const int a_bv = LY::BV + (sb + 4 * t8) * LY::B_ROW + i2 * 64 + l4 * 8;
+    // source lane (byte address) of the key operand: lane (t + 16 kg) reads
+    // rebuild lane (4 t + kg)
+    const int k_src = ((ql << 2) | t8) << 2;
 
     // tiles: the first one staged before the loop, then one barrier per tile;
     // after it each wave writes the next tile (loaded one tile earlier) into
@@ -390,77 +397,48 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
         }
         const uint8_t* tl = tiles + buf;
 
-        // ---- keys: K[slot][j1][j2] of head (i1, i2), bf16, into ks_w ----------
+        // ---- keys: K[slot][j1][j2] of head (i1, i2) for slots sb .. sb + 15,
+        // bf16.  Rebuild lane (4 bk + l4) holds K[sb + bk][j1 = 4 jg + l4][0..7]
+        // for jg = 0..3; the score MFMA wants lane (t + 16 kg) to hold
+        // K[sb + t][j1 = 4 jg + kg][0..7]: the same registers, lanes rotated
+        // by two bits (one ds_bpermute per dword, no LDS memory traffic).
+        u32x4 kop[4];
+        {
+            const s16x4 x0 = lds8(tl + a_bk);       // B~^K, slot sb + bk, j2 = l4
+            const s16x4 x1 = lds8(tl + a_bk + 32);  // j2 = 4 + l4
+            s16x4 y[4];
 #pragma unroll
-        for (int th = 0; th < 2; ++th) {
-            const int s = 16 * th + bk;
-            const s16x4 x0 = lds8(tl + LY::BK + s * LY::B_ROW + i2 * 64 + l4 * 8);        // B~^K, j2 = l4
-            const s16x4 x1 = lds8(tl + LY::BK + s * LY::B_ROW + i2 * 64 + (4 + l4) * 8);  // j2 = 4 + l4
+            for (int jg = 0; jg < 4; ++jg) y[jg] = lds8(tl + a_ak + 32 * jg);  // A^K, j1 = 4 jg + l4
 #pragma unroll
             for (int jg = 0; jg < 4; ++jg) {
-                const s16x4 y = lds8(tl + LY::AK + s * LY::A_ROW + (4 * jg + l4) * 8);  // A^K, j1 = 4 jg + l4
                 const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(x0, y, z, 0, 0, 0);
-                const f32x4 d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(x1, y, z, 0, 0, 0);
-                // lane (4 bk + l4): K[s][j1 = 4 jg + l4][j2 = 0..7]
-                const u32x4 w = {pack2(d0[0], d0[1]), pack2(d0[2], d0[3]), pack2(d1[0], d1[1]), pack2(d1[2], d1[3])};
-                *reinterpret_cast<u32x4*>(ks_w + s * 256 + (((4 * jg + l4) ^ swz(s & 7)) << 4)) = w;
+                const f32x4 d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(x0, y[jg], z, 0, 0, 0);
+                const f32x4 d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(x1, y[jg], z, 0, 0, 0);
+                kop[jg] = u32x4{pack2(d0[0], d0[1]), pack2(d0[2], d0[3]), pack2(d1[0], d1[1]), pack2(d1[2], d1[3])};
             }
+#pragma unroll
+            for (int jg = 0; jg < 4; ++jg)
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    kop[jg][d] = (uint32_t)__builtin_amdgcn_ds_bpermute(k_src, (int)kop[jg][d]);
         }
 
-        // ---- values: V^T rebuilt straight into the value MFMA's A layout --------
-        // (independent of the scores: issued before them, so that the two
-        // overlap; slots past the context were zeroed when staged)
-        uint32_t vop[kQ2][4];  // block j2: element e = slot 8 t8 + e of feature j1 = lane & 15
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {  // slots 8 t8 + 4 h2 + uu
-            s16x4 vy[4], vx0[4], vx1[4];
-#pragma unroll
-            for (int uu = 0; uu < 4; ++uu) {
-                const int s = 8 * t8 + 4 * h2 + uu;
-                vy[uu] = lds8(tl + LY::AV + s * LY::A_ROW + (4 * g4 + l4) * 8);        // A^V, j1 = 4 g4 + l4
-                vx0[uu] = lds8(tl + LY::BV + s * LY::B_ROW + i2 * 64 + l4 * 8);        // B^V, j2 = l4
-                vx1[uu] = lds8(tl + LY::BV + s * LY::B_ROW + i2 * 64 + (4 + l4) * 8);  // j2 = 4 + l4
-            }
-            f32x4 dv[4][2];
-            const f32x4 zz = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int uu = 0; uu < 4; ++uu) {
-                dv[uu][0] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(vx0[uu], vy[uu], zz, 0, 0, 0);
-                dv[uu][1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(vx1[uu], vy[uu], zz, 0, 0, 0);
-            }
-#pragma unroll
-            for (int u2 = 0; u2 < 2; ++u2)
-#pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        vop[4 * hf + c][2 * h2 + u2] = pack2(dv[2 * u2][hf][c], dv[2 * u2 + 1][hf][c]);
-        }
-        wave_lds_sync();  // this wave's keys are in ks_w
-
-        // ---- scores: Z[slot][query] = K q'^T ----------------------------------
-        float z[2][4];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const int t = 16 * tb + ql;
+        // ---- scores: Z[slot][query] = K q'^T for the wave's 16 slots ---------
+        float z[4];
+        {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 kop = ld_lds16(reinterpret_cast<const uint16_t*>(
-                    ks_w + t * 256 + (((4 * ks + t8) ^ swz(t & 7)) << 4)));
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q_hi[ks], acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, q_lo[ks], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[ks]), q_hi[ks], acc, 0,
+                                                              0, 0);
             }
-            // lane: query ql, slots 16 tb + 4 t8 + c
+            // lane: query ql, slots sb + 4 t8 + c
 #pragma unroll
-            for (int c = 0; c < 4; ++c) z[tb][c] = acc[c];
+            for (int c = 0; c < 4; ++c) z[c] = acc[c];
         }
-        if (s0 + kTileSlots > vis_min) {  // some query of the group stops inside this tile
+        if (s0 + sb + 16 > vis_min) {  // some query of the group stops inside these slots
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) z[tb][c] = (s0 + 16 * tb + 4 * t8 + c < vis) ? z[tb][c] : -INFINITY;
+            for (int c = 0; c < 4; ++c) z[c] = (s0 + sb + 4 * t8 + c < vis) ? z[c] : -INFINITY;
         }
 
         // ---- online softmax ---------------------------------------------------
@@ -468,8 +446,7 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
         // it by more than kSlack (log2 units); otherwise the weights stay
         // below 2^kSlack and the rescale of the running sums is skipped.  The
         // result is the same for any reference point.
-        float mx = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
-                         fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+        float mx = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
         mx = fmaxf(mx, other16(mx));
         mx = fmaxf(mx, other32(mx));
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0) {
@@ -483,44 +460,76 @@ __global__ void __launch_bounds__(P2 * 64, 1) decode_rebuild_kernel(DecodeParams
             m_run = m_new;
         }
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float p[2][4];
+        float p[4];
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                p[tb][c] = fast_exp2(z[tb][c] - m_use);
-                l_run += p[tb][c];
-            }
-
-        // weights into the value MFMA's B layout: lane (query ql, 8-slot
-        // group lane >> 4), slot 8 (lane >> 4) + e in element e
-        bf16x8 pop;
-        {
-            uint32_t pk[2][2];
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int d = 0; d < 2; ++d) pk[tb][d] = pack2(p[tb][2 * d], p[tb][2 * d + 1]);
-            uint32_t x[2][2], y[2][2];
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-                const auto r = __builtin_amdgcn_permlane32_swap(pk[0][d], pk[1][d], false, false);
-                x[0][d] = r[0];
-                x[1][d] = r[1];
-            }
-#pragma unroll
-            for (int d = 0; d < 2; ++d) {
-                const auto r = __builtin_amdgcn_permlane16_swap(x[0][d], x[1][d], false, false);
-                y[0][d] = r[0];
-                y[1][d] = r[1];
-            }
-            pop = __builtin_bit_cast(bf16x8, u32x4{y[0][0], y[0][1], y[1][0], y[1][1]});
+        for (int c = 0; c < 4; ++c) {
+            p[c] = fast_exp2(z[c] - m_use);
+            l_run += p[c];
         }
+        // ---- values: V^T rebuilt straight into the value MFMA's A layout --------
+        // (slots past the context were zeroed when staged).  Rebuild
+        // u covers slot sb + 4 (lane >> 4) + u: the inner dimension of the
+        // 16x16x16 value MFMA.
+        uint32_t vop[kQ2][2];  // block j2: elements e = slot sb + 4 t8 + e of feature j1 = lane & 15
+#pragma unroll
+        for (int u2 = 0; u2 < 2; ++u2) {  // slots sb + 4 t8 + 2 u2 + uu
+            s16x4 vy[2], vx0[2], vx1[2];
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+                const int u = 2 * u2 + uu;  // slot sb + 4 t8 + u
+                vy[uu] = lds8(tl + a_av + u * LY::A_ROW);        // A^V, j1 = 4 g4 + l4
+                vx0[uu] = lds8(tl + a_bv + u * LY::B_ROW);       // B^V, j2 = l4
+                vx1[uu] = lds8(tl + a_bv + u * LY::B_ROW + 32);  // j2 = 4 + l4
+            }
+            f32x4 dv[2][2];
+            const f32x4 zz = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+                dv[uu][0] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(vx0[uu], vy[uu], zz, 0, 0, 0);
+                dv[uu][1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(vx1[uu], vy[uu], zz, 0, 0, 0);
+            }
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) vop[4 * hf + c][u2] = pack2(dv[0][hf][c], dv[1][hf][c]);
+        }
+
+        // the weights in the score layout are the value MFMA's B operand:
+        // lane (query ql), slot sb + 4 t8 + e in element e
+        const s16x4 pop = __builtin_bit_cast(s16x4, uint2{pack2(p[0], p[1]), pack2(p[2], p[3])});
 #pragma unroll
         for (int j = 0; j < kQ2; ++j)
-            o_acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, u32x4{vop[j][0], vop[j][1], vop[j][2], vop[j][3]}), pop, o_acc[j], 0, 0,
-                0);
+            o_acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s16x4, uint2{vop[j][0], vop[j][1]}), pop, o_acc[j], 0, 0, 0);
+    }
+
+    // ---- the two halves of each head: the second wave hands its (m, l, O)
+    // to the first through LDS (the tile buffers are free now), which
+    // combines them as the split-KV merge does ----------------------------------
+    __syncthreads();
+    float* xch = reinterpret_cast<float*>(tiles) + (size_t)i2 * 34 * 64 + lane;
+    static_assert(P2 * 34 * 64 * 4 <= 2 * LY::TILE, "exchange fits the tile buffers");
+    if (hh == 1) {
+        xch[0] = m_run;
+        xch[64] = l_run;
+#pragma unroll
+        for (int j = 0; j < kQ2; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xch[(2 + 4 * j + c) * 64] = o_acc[j][c];
+    }
+    __syncthreads();
+    if (hh == 1) return;
+    {
+        const float m1 = xch[0], l1 = xch[64];
+        const float mm = fmaxf(m_run, m1);
+        const float mref = mm == -INFINITY ? 0.f : mm;
+        const float a0 = fast_exp2(m_run - mref), a1 = fast_exp2(m1 - mref);
+        l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+        for (int j = 0; j < kQ2; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) o_acc[j][c] = o_acc[j][c] * a0 + xch[(2 + 4 * j + c) * 64] * a1;
+        m_run = mm;
     }
 
     // ---- finish: the query's sum over its four lanes, then write -------------
@@ -572,7 +581,7 @@ struct Entry {
         const int split_pad = (P.n_split + kXcds - 1) / kXcds * kXcds;
         const int qgroups = (P.n_q + kNQ - 1) / kNQ;
         dim3 grid(split_pad * P.d.p1, P.batch, qgroups);
-        hipExtLaunchKernelGGL(decode_rebuild_kernel<P2>, grid, dim3(P2 * 64), 0, s, ev.start,
+        hipExtLaunchKernelGGL(decode_rebuild_kernel<P2>, grid, dim3(2 * P2 * 64), 0, s, ev.start,
                               ev.stop, 0, P);
         return hipGetLastError();
     }
@@ -581,7 +590,7 @@ struct Entry {
         int v = cached.load(std::memory_order_relaxed);
         if (v > 0) return v;
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_rebuild_kernel<P2>, P2 * 64, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_rebuild_kernel<P2>, 2 * P2 * 64, 0) != hipSuccess ||
             nb <= 0)
             nb = 1;
         cached.store(nb, std::memory_order_relaxed);
