@@ -5,8 +5,9 @@
 //    is computed once (a B^K row of every rank and head row shares it), the
 //    feature-chunk sets are written as whole 16-byte chunks and the value
 //    sets slot-contiguous.
-//  * append_kernel: one workgroup per (new token, sequence); for q2 > 64,
-//    whose angle table would not fit the tile kernel's LDS.
+//  * append_kernel: one workgroup per (new token, sequence); for decode-step
+//    token counts, and for q2 > 64, whose angle table would not fit the tile
+//    kernel's LDS.
 // Both write the same bytes: the elements of the new tokens' slots and their
 // positions (never the padding of a chunk), with the same float64 rotation.
 #include "kpa_append.hpp"
@@ -15,6 +16,7 @@ namespace kpa {
 namespace {
 
 constexpr int kMaxTilePairs = 32;  // q2 / 2 the tile kernel's angle table holds
+constexpr int64_t kPerTokenMax = 4096;  // new tokens (all sequences) for the per-token kernel
 // input rows (bytes) the tile kernel stages in LDS: with the largest angle
 // table (32 pairs: 32 KB) the launch stays within 64 KB of dynamic LDS
 constexpr int kStageRowMax = 992;
@@ -194,7 +196,11 @@ __global__ void __launch_bounds__(256) append_tile_kernel(AppendParams P) {
 }  // namespace
 
 hipError_t launch_append(const AppendParams& P, hipStream_t s) {
-    if (P.d.q2 / 2 <= kMaxTilePairs) {
+    // The tile kernel's chain of staged phases costs ~12-20 us even for one
+    // token per sequence; up to kPerTokenMax new tokens in all, one block per
+    // token is faster (decode steps: 5.6-7.1 us; the two break even at
+    // 32 x 128 tokens) and writes the same bytes.
+    if (P.d.q2 / 2 <= kMaxTilePairs && (int64_t)P.in.n_new * P.batch > kPerTokenMax) {
         // the new tokens of a sequence touch at most ceil(n_new / 32) + 1 tiles
         const dim3 grid((P.in.n_new + kTileSlots - 1) / kTileSlots + 1, P.batch);
         int row = 0;  // the longest row the kernel may stage

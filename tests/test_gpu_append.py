@@ -185,3 +185,45 @@ def test_slot_near_the_int32_limit_is_flagged_not_wrapped(gpu_lib, n_new):
     assert np.array_equal(positions[1, 3:3 + n_new], inp.positions[1].numpy())
     assert np.array_equal(sets[0][1, 3:3 + n_new].reshape(n_new, -1),
                           _bits(inp.a_k[1]).reshape(n_new, -1))
+
+
+@pytest.mark.parametrize("name", ["kpa_32k", "multiq_16", "tiny_f32"])
+def test_tile_and_per_token_appends_write_the_same_bytes(gpu_lib, name):
+    """More than 4096 new tokens in one call run the tile-wise kernel; the same
+    tokens appended 100 per sequence per call run the per-token kernel.  Both
+    caches must hold the same bytes (copies bit-exact, B~^K from the same
+    float64 rotation), and a sample of slots is checked against the oracle's
+    rotation."""
+    cfg = CONFIGS[name]
+    dims = dims_of(cfg)
+    nb, n = 2, 2100
+    inp = make_inputs(cfg, seed=17, batch=nb, ctx=n, pos_offset=300000)
+    cap = n + 64
+    slot0 = torch.tensor([3, 40], dtype=torch.int32)
+    dev = [t.cuda().contiguous() for t in (inp.a_k, inp.b_k, inp.a_v, inp.b_v, inp.positions)]
+    one = kpa.alloc_cache(dims, nb, cap)
+    kpa.kpa_cache_append(dims, one, nb, cap, *dev, slot0.cuda(), n_new=n)
+    many = kpa.alloc_cache(dims, nb, cap)
+    for s in range(0, n, 100):
+        part = [t[:, s:s + 100].contiguous() for t in dev]
+        kpa.kpa_cache_append(dims, many, nb, cap, *part, (slot0 + s).cuda(), n_new=min(100, n - s))
+    torch.cuda.synchronize()
+    assert torch.equal(one, many), "tile-wise and per-token appends differ"
+    lay = kpa.kpa_cache_layout(dims, nb, cap)
+    cache_np = one.cpu().numpy()
+    T, tb = lay["tile_slots"], lay["tile_bytes"]
+    bk = inp.b_k.to(torch.float64).numpy()
+    ulp_bits = 23 if cfg.dtype == "f32" else 7
+    rng = np.random.default_rng(0)
+    for b, t in zip(rng.integers(0, nb, 40), rng.integers(0, n, 40)):
+        sl = int(slot0[b]) + int(t)
+        base = (b * lay["n_tiles"] + sl // T) * tb + lay["comp_offset"][1]
+        eb = lay["elem_bytes"]
+        per_chunk = 16 // eb
+        ne = lay["comp_elems"][1]
+        raw = np.array([cache_np[base + (e // per_chunk) * T * 16 + (sl % T) * 16 + (e % per_chunk) * eb:][:eb]
+                        .view(np.float32 if eb == 4 else np.uint16)[0] for e in range(ne)])
+        got = _to_f64(raw, cfg.dtype).reshape(bk.shape[2:])
+        want = kpa_ref.append_rotate(bk[b, t], int(inp.positions[b, t]))
+        half_ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 1 - ulp_bits) * 0.5
+        assert np.all(np.abs(got - want) <= half_ulp * (1 + 1e-6) + 1e-300), (b, t)
