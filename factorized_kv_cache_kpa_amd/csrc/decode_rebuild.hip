@@ -83,13 +83,19 @@ struct Lds {
     // rank-interleaved tile: 8 bytes (4 ranks) per (slot, row, feature);
     // rows of a slot padded so that slot stride = 8 banks mod 32; offsets
     // inside one of the two tile buffers
-    static constexpr int A_ROW = kQ1 * 8 + 32;         // A^K or A^V of the group's A head
-    static constexpr int B_ROW = P2 * kQ2 * 8 + 32;    // B~^K or B^V of every B head
+    // key sets: a row per slot holding its features (the key rebuild reads
+    // one slot's rows per lane group)
+    static constexpr int A_ROW = kQ1 * 8 + 32;         // A^K of the group's A head
+    static constexpr int B_ROW = P2 * kQ2 * 8 + 32;    // B~^K of every B head
+    // value sets: a row per element holding its 32 slots (the value rebuild
+    // reads two consecutive slots at once); 272 B rows put the 16 rows one
+    // read instruction touches on distinct banks
+    static constexpr int V_ROW = kTileSlots * 8 + 16;
     static constexpr int AK = 0;
-    static constexpr int AV = AK + kTileSlots * A_ROW;
-    static constexpr int BK = AV + kTileSlots * A_ROW;
-    static constexpr int BV = BK + kTileSlots * B_ROW;
-    static constexpr int TILE = BV + kTileSlots * B_ROW;
+    static constexpr int BK = AK + kTileSlots * A_ROW;
+    static constexpr int AV = BK + kTileSlots * B_ROW;   // [j1][slot]
+    static constexpr int BV = AV + kQ1 * V_ROW;          // [i2 q2 + j2][slot]
+    static constexpr int TILE = BV + P2 * kQ2 * V_ROW;
     // two tile buffers and the rotary cos/sin [16 queries][4 pairs][2]
     static constexpr int TOTAL = 2 * TILE + kNQ * 4 * 2 * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS of one CU");
@@ -162,7 +168,7 @@ struct Stage {
                 kd = kBV;
                 slot[k] = 8 * sg;
                 src[k] = (uint32_t)(L.off[3] + e * 64 + sg * 16);
-                dst[k] = LY::BV + (8 * sg) * LY::B_ROW + e * 8;
+                dst[k] = LY::BV + e * LY::V_ROW + 64 * sg;
             } else if (u < C::U_BK + C::U_BV + C::U_AK) {  // A^K chunk (r p1 + i1) 2 + hf of slot s
                 const int x = u - C::U_BK - C::U_BV;
                 const int s = x % kTileSlots, hf = x / kTileSlots;
@@ -176,7 +182,7 @@ struct Stage {
                 kd = kAV;
                 slot[k] = 8 * sg;
                 src[k] = (uint32_t)(L.off[2] + (i1 * kQ1 + j1) * 64 + sg * 16);
-                dst[k] = LY::AV + (8 * sg) * LY::A_ROW + j1 * 8;
+                dst[k] = LY::AV + j1 * LY::V_ROW + 64 * sg;
             } else {
                 kd = kNone;
                 slot[k] = 0;
@@ -215,7 +221,6 @@ struct Stage {
     // hold arbitrary bytes, and a zero softmax weight times a NaN value
     // would still poison the value sums.
     __device__ __forceinline__ void store(uint8_t* lds, int rk, int rv, bool tail, int valid) {
-        using LY = Lds<P2>;
 #pragma unroll
         for (int k = 0; k < C::UPT; ++k) {
             const int kd = kind[k];
@@ -248,17 +253,10 @@ struct Stage {
                 o[d][3] = pair_hi(v[k][2][d], v[k][3][d]);
             }
             uint8_t* out = lds + dst[k];
-            if (kd == kBK || kd == kAK) {  // items = 8 consecutive features: 64 contiguous bytes
+            // items = 8 consecutive features of a slot (key sets) or 8
+            // consecutive slots of an element (value sets): 64 contiguous bytes
 #pragma unroll
-                for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4*>(out + 16 * d) = o[d];
-            } else {  // items = 8 consecutive slots: one 8-byte entry per slot row
-                const int row = kd == kBV ? LY::B_ROW : LY::A_ROW;
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    *reinterpret_cast<uint2*>(out + (2 * d) * row) = uint2{o[d][0], o[d][1]};
-                    *reinterpret_cast<uint2*>(out + (2 * d + 1) * row) = uint2{o[d][2], o[d][3]};
-                }
-            }
+            for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4*>(out + 16 * d) = o[d];
         }
     }
 };
@@ -366,8 +364,8 @@ __global__ void __launch_bounds__(2 * P2 * 64, 1) decode_rebuild_kernel(DecodePa
     // the rebuilt keys; the loop adds constants only
     const int a_bk = LY::BK + (sb + bk) * LY::B_ROW + i2 * 64 + l4 * 8;
     const int a_ak = LY::AK + (sb + bk) * LY::A_ROW + l4 * 8;
-    const int a_av = LY::AV + (sb + 4 * t8) * LY::A_ROW + (4 * g4 + l4) * 8;
-    const int a_bv = LY::BV + (sb + 4 * t8) * LY::B_ROW + i2 * 64 + l4 * 8;
+    const int a_av = LY::AV + (4 * g4 + l4) * LY::V_ROW + (sb + 4 * t8) * 8;
+    const int a_bv = LY::BV + (i2 * kQ2 + l4) * LY::V_ROW + (sb + 4 * t8) * 8;
     // source lane (byte address) of the key operand: lane (t + 16 kg) reads
     // rebuild lane (4 t + kg)
     const int k_src = ((ql << 2) | t8) << 2;
@@ -472,28 +470,25 @@ __global__ void __launch_bounds__(2 * P2 * 64, 1) decode_rebuild_kernel(DecodePa
         // 16x16x16 value MFMA.
         uint32_t vop[kQ2][2];  // block j2: elements e = slot sb + 4 t8 + e of feature j1 = lane & 15
 #pragma unroll
-        for (int u2 = 0; u2 < 2; ++u2) {  // slots sb + 4 t8 + 2 u2 + uu
-            s16x4 vy[2], vx0[2], vx1[2];
-#pragma unroll
-            for (int uu = 0; uu < 2; ++uu) {
-                const int u = 2 * u2 + uu;  // slot sb + 4 t8 + u
-                vy[uu] = lds8(tl + a_av + u * LY::A_ROW);        // A^V, j1 = 4 g4 + l4
-                vx0[uu] = lds8(tl + a_bv + u * LY::B_ROW);       // B^V, j2 = l4
-                vx1[uu] = lds8(tl + a_bv + u * LY::B_ROW + 32);  // j2 = 4 + l4
-            }
+        for (int u2 = 0; u2 < 2; ++u2) {  // slots sb + 4 t8 + 2 u2 + (0, 1): one 16-byte read each
+            const u32x4 vy = *reinterpret_cast<const u32x4*>(tl + a_av + 16 * u2);                   // A^V, j1 = 4 g4 + l4
+            const u32x4 vx0 = *reinterpret_cast<const u32x4*>(tl + a_bv + 16 * u2);                  // B^V, j2 = l4
+            const u32x4 vx1 = *reinterpret_cast<const u32x4*>(tl + a_bv + 4 * LY::V_ROW + 16 * u2);  // j2 = 4 + l4
             f32x4 dv[2][2];
             const f32x4 zz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int uu = 0; uu < 2; ++uu) {
-                dv[uu][0] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(vx0[uu], vy[uu], zz, 0, 0, 0);
-                dv[uu][1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(vx1[uu], vy[uu], zz, 0, 0, 0);
+                const s16x4 y = __builtin_bit_cast(s16x4, uint2{vy[2 * uu], vy[2 * uu + 1]});
+                dv[uu][0] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                    __builtin_bit_cast(s16x4, uint2{vx0[2 * uu], vx0[2 * uu + 1]}), y, zz, 0, 0, 0);
+                dv[uu][1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                    __builtin_bit_cast(s16x4, uint2{vx1[2 * uu], vx1[2 * uu + 1]}), y, zz, 0, 0, 0);
             }
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) vop[4 * hf + c][u2] = pack2(dv[0][hf][c], dv[1][hf][c]);
         }
-
         // the weights in the score layout are the value MFMA's B operand:
         // lane (query ql), slot sb + 4 t8 + e in element e
         const s16x4 pop = __builtin_bit_cast(s16x4, uint2{pack2(p[0], p[1]), pack2(p[2], p[3])});
