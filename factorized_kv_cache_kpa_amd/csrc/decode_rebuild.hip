@@ -80,11 +80,10 @@ constexpr float kSlack = 8.f;          // log2 units the weights may exceed 1 by
 // LDS layout (bytes) for P2 B heads.
 template <int P2>
 struct Lds {
-    // rank-interleaved tile: 8 bytes (4 ranks) per (slot, row, feature);
-    // rows of a slot padded so that slot stride = 8 banks mod 32; offsets
-    // inside one of the two tile buffers
-    // key sets: a row per slot holding its features (the key rebuild reads
-    // one slot's rows per lane group)
+    // Rank-interleaved tile: 8 bytes (4 ranks) per (slot, row, feature);
+    // offsets inside one of the two tile buffers.
+    // Key sets: a row per slot holding its features (the key rebuild reads
+    // the rows of 16 slots per instruction), padded by 32 bytes.
     static constexpr int A_ROW = kQ1 * 8 + 32;         // A^K of the group's A head
     static constexpr int B_ROW = P2 * kQ2 * 8 + 32;    // B~^K of every B head
     // value sets: a row per element holding its 32 slots (the value rebuild
@@ -132,7 +131,7 @@ struct Cfg {
     static constexpr int UNITS = U_BK + U_BV + U_AK + U_AV;
     static constexpr int UPT = (UNITS + THREADS - 1) / THREADS;  // units per thread
     // kinds of unit start at multiples of 64 (one kind per wave): P2 even
-    static_assert(P2 >= 2 && P2 <= 8 && P2 % 2 == 0, "one wave per B head: 2, 4, 6 or 8");
+    static_assert(P2 >= 2 && P2 <= 8 && P2 % 2 == 0, "two waves per B head: P2 = 2, 4, 6 or 8");
     static_assert(UPT == 1, "one staging unit per thread");
 };
 
