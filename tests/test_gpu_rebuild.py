@@ -115,3 +115,37 @@ def test_rebuild_empty_and_short_sequences(gpu_lib):
     ro, rl = _oracle(inp, causal=False)
     assert np.all(go[0] == 0) and np.all(np.isneginf(gl[0]))
     assert_close(go[1:], gl[1:], ro[1:], rl[1:], cfg.dtype, "short", scale=scale_of(inp)[1:], path="mfma_rebuild")
+
+
+def test_rebuild_two_level_merge(gpu_lib):
+    """More than 1024 forced chunks: the partials go through the two-level
+    merge (arrival counters cleared by the decode kernel's first chunk)."""
+    cfg = BASE
+    dims = dims_of(cfg)
+    inp = make_inputs(cfg, seed=45, batch=1, ctx=35200, n_q=8)
+    cache, cap = fill_cache(inp, dims)
+    for ns in (1100, 70):
+        go, gl = run_decode(inp, dims, cache, cap, num_splits=ns)
+        ro, rl = _oracle(inp)
+        assert_close(go, gl, ro, rl, cfg.dtype, f"splits={ns}", scale=scale_of(inp), path="mfma_rebuild")
+
+
+def test_rebuild_ctx_len_above_max_ctx_is_flagged(gpu_lib):
+    cfg = BASE
+    dims = dims_of(cfg)
+    inp = make_inputs(cfg, seed=46, batch=2, ctx=64, n_q=16)
+    cache, cap = fill_cache(inp, dims)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nb, nq, h, dh = 2, 16, dims.h, dims.d_h
+    out = torch.empty((nb, nq, h, dh), device="cuda")
+    lse = torch.empty((nb, nq, h), device="cuda")
+    ctx = torch.tensor([64, 40], dtype=torch.int32, device="cuda")
+    ws = kpa.alloc_workspace(dims, nb, 40, nq)
+    kpa.kpa_decode_multiq(dims, cache, nb, cap, ctx, 40, nq, 1, inp.q.cuda(), inp.q_pos.cuda(), out, lse, ws,
+                          dev_status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kpa.KPA_DEV_CTX_OUT_OF_RANGE
+    # zero sequences: nothing to do, no error
+    kpa.kpa_decode_multiq(dims, cache, 0, cap, ctx, 40, nq, 1, inp.q.cuda(), inp.q_pos.cuda(), out, lse, ws,
+                          dev_status=status)
+    torch.cuda.synchronize()
