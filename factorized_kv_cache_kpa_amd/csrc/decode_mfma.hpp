@@ -20,7 +20,9 @@
 // factor, then the other; K is never rebuilt.  The value side, per iF,
 //   O[(n,iG,jG), jF] += sum_{r,s} (p[n,iG,iF,s] G^V_r[s,iG,jG]) F^V_r[s,iF,jF]
 // is a GEMM over slots (MFMA 16x16x32: M = (iG,jG), N = jF, K = 32 slots),
-// with the softmax weight folded into the G factor on the VALU.  The online
+// with the softmax weight folded into the G factor: by 4x4x4 matrix
+// instructions (A = diag of four weights, B = four slots of G^V) where four
+// consecutive rows (iG, jG) share a head, else on the VALU.  The online
 // softmax (running max and sum per (query, head), rescaling O when the max
 // grows) is the blocked online log-sum-exp of FlashTPA decoding ([TPA]).
 //
@@ -46,9 +48,10 @@
 // Precision: bf16 factors exactly; the rotated, scaled query is split into
 // bf16 hi + lo parts (two MFMAs, or one with the two parts in the two K
 // halves when F is 8 wide) so it carries ~16 bits; the value operand
-// p * G^V is formed in fp32 and rounded once to bf16 (relative 2^-8 per
-// term, unbiased); the normaliser sums the fp32 weights; all accumulation is
-// fp32.  Because each KV chunk rounds against its own running max, results
+// p * G^V is rounded to bf16 (relative 2^-8 per term, unbiased) -- formed in
+// fp32 on the VALU, or, on the matrix cores, from p rounded to bf16 first
+// (the product of two bf16 is exact in fp32: 2 * 2^-8 per term); the
+// normaliser sums the fp32 weights; all accumulation is fp32.  Because each KV chunk rounds against its own running max, results
 // for different chunk counts agree to that bf16 rounding, not bit for bit.
 #pragma once
 
@@ -638,6 +641,21 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
         load_f(tile, f);
     };
 
+    // Exact kernels whose G feature dimension is a multiple of 4 (so each
+    // group of four rows is one head) fold the softmax weights into the
+    // value factor on the matrix cores; the others on the vector ALU.
+    constexpr bool kMxFold = !S::GEN && S::QG_ % 4 == 0;
+    // v_perm_b32 selectors that place the low bf16 of a dword at element i4
+    // of a zeroed 4-element operand: dword 0, dword 1
+    const int i4 = lane & 3;
+    uint32_t psel[2];
+    {
+        constexpr uint32_t kZ = 0x0c0c0c0cu;  // every byte 0
+        constexpr uint32_t kLo = 0x0c0c0100u, kHi = 0x01000c0cu;  // the low bf16 to the low / high half
+        psel[0] = i4 == 0 ? kLo : i4 == 1 ? kHi : kZ;
+        psel[1] = i4 == 2 ? kLo : i4 == 3 ? kHi : kZ;
+    }
+
     auto process = [&](int s0, const uint8_t* gcur, FR& f) __attribute__((always_inline)) {
         const int valid = min(kTileSlots, last - s0);
         // ---- scores: W = q' F (MFMA), z = sum G W (VALU) --------------------
@@ -873,7 +891,7 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
                 const int R_row = mb * 16 + l16;               // row of this lane's A operand
                 const bool row_ok = kFull16 || R_row < M;
                 const int iG_row = row_ok ? R_row >> G.lqg : 0;
-                float p[NQW][8];
+                float p[NQW][kMxFold ? 2 : 8];
 #pragma unroll
                 for (int u = 0; u < NQW; ++u) {
                     // rows of this lane's accumulators: mb*16 + 4*g16 + c
@@ -893,10 +911,70 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
                             for (int nb = 0; nb < KC; ++nb) o_acc[u][mb][nb][c] *= a;
                         }
                     }
-                    ld_lds32(&zp0[(u * PG + iG_row) * ZS + 8 * g16], p[u]);
-                    if (!row_ok)
+                    if constexpr (kMxFold) {
+                        // two weights: slots 8 g16 + i4 and 8 g16 + 4 + i4
+                        const float* pz = &zp0[(u * PG + iG_row) * ZS + 8 * g16 + i4];
+                        p[u][0] = row_ok ? pz[0] : 0.f;
+                        p[u][1] = row_ok ? pz[4] : 0.f;
+                    } else {
+                        ld_lds32(&zp0[(u * PG + iG_row) * ZS + 8 * g16], p[u]);
+                        if (!row_ok)
 #pragma unroll
-                        for (int k = 0; k < 8; ++k) p[u][k] = 0.f;
+                            for (int k = 0; k < 8; ++k) p[u][k] = 0.f;
+                    }
+                }
+                if constexpr (kMxFold) {
+                    // p * G^V on the matrix cores.  One 4x4x4 block per (four
+                    // rows of one head, four slots): A = diag(p of the four
+                    // slots), B = G^V of the rows at those slots, so D holds
+                    // p * G^V with each lane's own row in its column -- the
+                    // four slots of the value MFMA's A operand, in order.
+                    // Lane (4 blk + i) gives A's row i: its weight at k = i.
+                    s16x4 pa[NQW][2];
+#pragma unroll
+                    for (int u = 0; u < NQW; ++u) {
+                        // the weight in the low half of a packed pair, the other
+                        // weight in the high half (not read)
+                        const uint32_t pk0 = pack2_bf16(p[u][0], p[u][1]), pk1 = pack2_bf16(p[u][1], p[u][0]);
+                        pa[u][0] = __builtin_bit_cast(s16x4, uint2{__builtin_amdgcn_perm(pk0, pk0, psel[0]),
+                                                                     __builtin_amdgcn_perm(pk0, pk0, psel[1])});
+                        pa[u][1] = __builtin_bit_cast(s16x4, uint2{__builtin_amdgcn_perm(pk1, pk1, psel[0]),
+                                                                     __builtin_amdgcn_perm(pk1, pk1, psel[1])});
+                    }
+#pragma unroll
+                    for (int r = 0; r < RVC; ++r) {
+                        uint4 graw = uint4{0u, 0u, 0u, 0u};
+                        if (row_ok) {
+                            const int e_lane = r * MT + m0 + l16;
+                            const uint8_t* gv_lane = gvbase + e_lane * 64 + ((g16 ^ ((e_lane >> 1) & 3)) * 16);
+                            graw = *reinterpret_cast<const uint4*>(gv_lane + mb * 1024);
+                        }
+                        if constexpr (kPartial) {
+                            // slots past the end hold arbitrary bytes: 0 * NaN
+                            // would reach every output of the block
+                            const int left = valid - 8 * g16;  // slots of this lane's 8 that are valid
+                            graw.x = left >= 2 ? graw.x : left >= 1 ? (graw.x & 0xffffu) : 0u;
+                            graw.y = left >= 4 ? graw.y : left >= 3 ? (graw.y & 0xffffu) : 0u;
+                            graw.z = left >= 6 ? graw.z : left >= 5 ? (graw.z & 0xffffu) : 0u;
+                            graw.w = left >= 8 ? graw.w : left >= 7 ? (graw.w & 0xffffu) : 0u;
+                        }
+                        const s16x4 gb0 = __builtin_bit_cast(s16x4, uint2{graw.x, graw.y});
+                        const s16x4 gb1 = __builtin_bit_cast(s16x4, uint2{graw.z, graw.w});
+#pragma unroll
+                        for (int u = 0; u < NQW; ++u) {
+                            const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+                            const f32x4 d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pa[u][0], gb0, zero4, 0, 0, 0);
+                            const f32x4 d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pa[u][1], gb1, zero4, 0, 0, 0);
+                            const bf16x8 ga = __builtin_bit_cast(
+                                bf16x8, u32x4{pack2_bf16(d0[0], d0[1]), pack2_bf16(d0[2], d0[3]),
+                                              pack2_bf16(d1[0], d1[1]), pack2_bf16(d1[2], d1[3])});
+#pragma unroll
+                            for (int nb = 0; nb < KC; ++nb)
+                                o_acc[u][mb][nb] =
+                                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(ga, f.fv[r][nb], o_acc[u][mb][nb], 0, 0, 0);
+                        }
+                    }
+                    continue;
                 }
 #pragma unroll
                 for (int r = 0; r < RVC; ++r) {

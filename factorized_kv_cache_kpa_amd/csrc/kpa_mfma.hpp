@@ -7,6 +7,9 @@
 //   v_mfma_f32_16x16x32_bf16: A[m][k] is element k%8 of lane m + 16*(k/8);
 //     B[k][n] is element k%8 of lane n + 16*(k/8); D[m][n] is register m%4
 //     of lane n + 16*(m/4).
+//   v_mfma_f32_4x4x4_16b_bf16: 16 independent 4x4x4 blocks, block b in lanes
+//     4b .. 4b+3: A_b[i][k] is element k of lane 4b + i; B_b[k][j] is element
+//     k of lane 4b + j; D_b[i][j] is register i of lane 4b + j.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,6 +22,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;  // 4 bf16: a 4x4x4 MFMA operand
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
@@ -80,6 +84,11 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
     for (int k = 0; k < 4; ++k)
         r[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2 * k], v[2 * k + 1]}, bf16x2));
     return __builtin_bit_cast(bf16x8, r);
+}
+
+// bf16 of two floats in one dword (low half = first), round to nearest even.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // 2^x on the hardware exp unit (x <= 0 here; results below 2^-126 flush to 0).
