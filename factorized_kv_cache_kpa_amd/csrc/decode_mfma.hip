@@ -9,20 +9,28 @@ namespace mfma {
 // Shapes with an exact instantiation.  Cfg arguments: PG, QG, PF, QF (F = the
 // factor whose feature dimension is contracted on the matrix cores: B for
 // most, A for the multi-query shape and some head splits), R_K, R_V, F is B,
-// queries per wave, query subgroups, waves/SIMD[, waves per F head].
+// queries per wave, query subgroups, waves/SIMD[, waves per F head[, percent
+// of the resident-workgroup slots the planner fills[, strided chunks]]].
 const MfmaKernel* exact_kernels(int* count) {
     static const MfmaKernel tab[] = {
         KPA_MFMA_ENTRY(4, 4, 8, 16, 2, 2, false, 4, 8, 4, 16, 2, 2, true, 1, 1, 3),
         KPA_MFMA_ENTRY(4, 4, 8, 16, 1, 1, false, 4, 8, 4, 16, 1, 1, true, 1, 1, 2),
-        KPA_MFMA_ENTRY(8, 4, 8, 16, 2, 4, false, 8, 8, 4, 16, 2, 4, true, 1, 1, 2),
+        // long_512k's shape: 48 KB tiles, two workgroups per CU.  One
+        // sequence of 2^19 tokens runs fastest with ~90% of the slots filled
+        // (456 chunks against 512: 136.1 -> 131.3 us per call) and strided
+        // chunks (-> 128.9 us; 136.9 -> 128.5-130.3 us for the two together,
+        // A/B on one box)
+        KPA_MFMA_ENTRY(8, 4, 8, 16, 2, 4, false, 8, 8, 4, 16, 2, 4, true, 1, 1, 2, 1, 90, true),
         KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, false, 8, 8, 4, 16, 4, 4, false, 1, 1, 1),
         KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, true, 8, 8, 4, 16, 4, 4, false, 2, 2, 2),
         // TPA split (A: h x 1, B: 1 x d_h): G = A with feature dimension 1, F = B
         KPA_MFMA_ENTRY(12, 1, 1, 64, 2, 2, false, 12, 1, 1, 64, 2, 2, true, 1, 1, 1),
         // FlashTPA's benchmark shapes: d_h = 64, R_K = R_V = 1, h = 16 / 32 / 48
+        // (strided chunks for h = 32 and 48: 0.9-2.1% faster at batch 1, 4
+        // and 16, A/B; h = 16 within 0.5%)
         KPA_MFMA_ENTRY(16, 1, 1, 64, 1, 1, false, 16, 1, 1, 64, 1, 1, true, 1, 1, 2),
-        KPA_MFMA_ENTRY(32, 1, 1, 64, 1, 1, false, 32, 1, 1, 64, 1, 1, true, 1, 1, 2),
-        KPA_MFMA_ENTRY(48, 1, 1, 64, 1, 1, false, 48, 1, 1, 64, 1, 1, true, 1, 1, 1),
+        KPA_MFMA_ENTRY(32, 1, 1, 64, 1, 1, false, 32, 1, 1, 64, 1, 1, true, 1, 1, 2, 1, 100, true),
+        KPA_MFMA_ENTRY(48, 1, 1, 64, 1, 1, false, 48, 1, 1, 64, 1, 1, true, 1, 1, 1, 1, 100, true),
         // The KPA page's head splits (d1 = d2 = 8, R_K = R_V = 2).  F is the
         // factor with fewer heads (fewer waves, more rows per wave), except for
         // 4 x 5, where four waves per workgroup (F = A) spread evenly over a
@@ -139,6 +147,11 @@ bool decode_mfma_supported(const kpa_dims& d, int n_q) { return find_kernel(d, n
 int decode_mfma_blocks_per_cu(const kpa_dims& d, int n_q) {
     const Choice c = find_kernel(d, n_q);
     return c.k ? c.k->blocks_per_cu(d, c.f_is_b) : 1;
+}
+
+int decode_mfma_fill_pct(const kpa_dims& d, int n_q) {
+    const Choice c = find_kernel(d, n_q);
+    return c.k ? c.k->fill_pct : 100;
 }
 
 // Workgroups one KV chunk needs (one per group of queries).

@@ -56,6 +56,7 @@
 #pragma once
 
 #include <atomic>
+#include <climits>
 #include <mutex>
 #include <type_traits>
 
@@ -84,12 +85,18 @@ __host__ __device__ __forceinline__ int ilog2(int x) {
 // Exact shape: G factor PG x QG, F factor PF x QF, ranks RK, RV; F_IS_B: F
 // is B (else A); NQW queries per wave, NQG query subgroups per workgroup; MW
 // waves per SIMD the registers must allow; RS waves share one F head, each
-// taking PG / RS of the G heads (the tile's G factors in LDS serve them all).
-template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int NQW, int NQG, int MW, int RS = 1>
+// taking PG / RS of the G heads (the tile's G factors in LDS serve them all);
+// FILL: percent of the resident-workgroup slots the split-KV planner fills;
+// STRIDED: a chunk is every n_split-th tile (one query per workgroup only)
+// rather than consecutive tiles.
+template <int PG, int QG, int PF, int QF, int RK, int RV, bool F_IS_B, int NQW, int NQG, int MW, int RS = 1,
+          int FILL = 100, bool STRIDED = false>
 struct Cfg {
     static constexpr bool GEN = false;
     static constexpr int PG_ = PG, QG_ = QG, PF_ = PF, QF_ = QF, RK_ = RK, RV_ = RV;
     static constexpr int RS_ = RS, PGW_ = PG / RS;    // G heads per wave
+    static constexpr int FILL_ = FILL;
+    static constexpr bool STRIDED_ = STRIDED;
     static constexpr bool F_IS_B_ = F_IS_B;
     static constexpr int RKC = RK, RVC = RV;          // register arrays per rank
     // Kernels with one query per workgroup serve single-query decode, where a
@@ -142,6 +149,7 @@ struct Cfg {
     static_assert((F_IS_B ? QF : QG) <= 64, "rotary table holds 32 pairs");
     static_assert(RK <= 4 && RV <= 4, "ranks up to 4");
     static_assert(WAVES * 64 <= 1024, "at most 16 waves per workgroup");
+    static_assert(!STRIDED || NQW * NQG == 1, "strided chunks for one query per workgroup");
 };
 
 // Generic family: F feature dimension QF, at most RKC key and RVC value
@@ -166,7 +174,8 @@ struct GenCfg {
     static constexpr int ZS = 36;  // score scratch row stride (floats)
     // placeholders of the exact-only names (never read on the generic path)
     static constexpr int PG_ = 0, QG_ = 0, PF_ = 0, RK_ = 0, RV_ = 0, TPG = 1, ROWS_P = 2, WAVES = 0;
-    static constexpr int RS_ = 1, PGW_ = 0;
+    static constexpr int RS_ = 1, PGW_ = 0, FILL_ = 100;
+    static constexpr bool STRIDED_ = false;
     static constexpr int GK_BYTES = 0, GV_BYTES = 0, GK_BLOCKS = 0, G_BLOCKS = 0;
     static constexpr bool F_IS_B_ = true;
     static_assert(QF == 8 || QF == 16 || QF == 32 || QF == 64, "the MFMA-side feature dimension must be 8, 16, 32 or 64");
@@ -507,12 +516,20 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
     }
     const int64_t offFK = L.off[G.set_fk], offGK = L.off[G.set_gk];
     const int64_t offFV = L.off[G.set_fv], offGV = L.off[G.set_gv];
+    // The tiles of a chunk: chunk_tiles consecutive tiles, or (STRIDED)
+    // tiles split, split + n_split, split + 2 n_split, ..., so that the
+    // chunks' workgroups sweep one sequence side by side and at any time read
+    // one contiguous stretch of it.
+    constexpr bool kStrided = S::STRIDED_;
+    const int chunk_first = kStrided ? split * kTileSlots : split * P.chunk_tiles * kTileSlots;
+    const int chunk_end = kStrided ? INT_MAX : chunk_first + P.chunk_tiles * kTileSlots;
+    const int t_step = kStrided ? P.n_split : 1;  // tiles from one tile of the chunk to the next
     int early_first = 0, early_last = 0;
     if constexpr (kEarly) {
         int vis_e = 0;
         for (int n = qwg * S::QPW; n < min(P.n_q, (qwg + 1) * S::QPW); ++n) vis_e = max(vis_e, visible_slots(P, b, n));
-        early_first = split * P.chunk_tiles * kTileSlots;
-        early_last = min(early_first + P.chunk_tiles * kTileSlots, vis_e);
+        early_first = chunk_first;
+        early_last = min(chunk_end, vis_e);
         if (early_first < early_last) {
             const uint8_t* tile = P.cache + (int64_t)b * L.n_tiles * L.tile_bytes +
                                   (int64_t)(early_first / kTileSlots) * L.tile_bytes;
@@ -618,9 +635,10 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
     for (int u = 0; u < NQW; ++u) vis[u] = n0 + u < P.n_q ? visible_slots(P, b, n0 + u) : 0;
     int vis_wg = 0;
     for (int n = qwg * S::QPW; n < min(P.n_q, (qwg + 1) * S::QPW); ++n) vis_wg = max(vis_wg, visible_slots(P, b, n));
-    const int first = split * P.chunk_tiles * kTileSlots;
-    int last = first + P.chunk_tiles * kTileSlots;
-    if (last > vis_wg) last = vis_wg;
+    const int first = chunk_first;
+    const int last = min(chunk_end, vis_wg);  // the chunk's slots lie in [first, last)
+    const int step = t_step * kTileSlots;     // slots from one tile of the chunk to the next
+    const int64_t tstep = (int64_t)t_step * L.tile_bytes;
     const uint8_t* seq = P.cache + (int64_t)b * L.n_tiles * L.tile_bytes;
 
     // Pipeline, one tile ahead for every byte:
@@ -1017,8 +1035,7 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
     }
     // Fused append (kpa_append_decode, single-query kernels; the host runs
     // the append kernel first for the others): each new token is written by
-    // the workgroup of the chunk whose slots hold it (past every chunk: the
-    // last) before it reads it.  The slot0 value arrives behind the first
+    // the workgroup of the chunk whose tiles hold it before it reads it.  The slot0 value arrives behind the first
     // tile's G blocks (loads complete in order), so workgroups owning no token
     // wait here for what the tile loop's first wait would wait for anyway.
     // The owner writes its tokens and waits for the stores, all before the
@@ -1033,7 +1050,8 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
         bool owned = false, in_first = false;
         for (int n = 0; n < P.app.n_new; ++n) {
             const int j = slot_add(app_slot0, n);
-            const int owner = j < 0 ? 0 : min(j / span, P.n_split - 1);
+            // (a slot past every contiguous chunk: the last chunk)
+            const int owner = j < 0 ? 0 : kStrided ? (j / kTileSlots) % P.n_split : min(j / span, P.n_split - 1);
             if (owner != split) continue;
             append_token<false>(P.d, L, P.cache_w, P.capacity, P.app, P.dev_status, b, n, threadIdx.x,
                                 G.waves * 64);
@@ -1049,21 +1067,21 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
             }
         }
     }
-    for (int s0 = first; s0 < last; s0 += 2 * kTileSlots) {
+    for (int s0 = first; s0 < last; s0 += 2 * step) {
         // tile s0: data in gbuf_a and fa
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the DMA and loads issued one tile ago
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         const uint8_t* tile = seq + (int64_t)(s0 / kTileSlots) * L.tile_bytes;
-        if (s0 + kTileSlots < last) issue(tile + L.tile_bytes, gbuf_b, fb);
+        if (s0 + step < last) issue(tile + tstep, gbuf_b, fb);
         process(s0, gbuf_a, fa);
-        if (s0 + kTileSlots >= last) break;
-        // tile s0 + 32: data in gbuf_b and fb
+        if (s0 + step >= last) break;
+        // the chunk's next tile: data in gbuf_b and fb
         __builtin_amdgcn_s_waitcnt(0x0f70);
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        if (s0 + 2 * kTileSlots < last) issue(tile + 2 * L.tile_bytes, gbuf_a, fa);
-        process(s0 + kTileSlots, gbuf_b, fb);
+        if (s0 + 2 * step < last) issue(tile + 2 * tstep, gbuf_a, fa);
+        process(s0 + step, gbuf_b, fb);
     }
 
     // ---- finish: full sums per row, then write --------------------------------
@@ -1126,6 +1144,7 @@ struct MfmaKernel {
     bool multi;                    // kernel for n_q > 1
     int queries_per_wave, query_subgroups;
     int waves_max;                 // waves per workgroup the kernel allows
+    int fill_pct;                  // percent of the resident-workgroup slots to fill
     hipError_t (*launch)(const DecodeParams&, hipStream_t, const KernelEvents&);
     int (*blocks_per_cu)(const kpa_dims&, int f_is_b);
     int (*lds_bytes)(const kpa_dims&, int f_is_b);
@@ -1195,6 +1214,7 @@ struct Entry {
 #define KPA_MFMA_ENTRY(p1, p2, q1, q2, rk, rv, multi, ...)                                                        \
     {false, p1, p2, q1, q2, rk, rv, 0, 0, 0, 0, multi, ::kpa::mfma::Cfg<__VA_ARGS__>::NQW_,                       \
      ::kpa::mfma::Cfg<__VA_ARGS__>::NQG_, ::kpa::mfma::Cfg<__VA_ARGS__>::WAVES_MAX,                                 \
+     ::kpa::mfma::Cfg<__VA_ARGS__>::FILL_,                                                                          \
      ::kpa::mfma::Entry<::kpa::mfma::Cfg<__VA_ARGS__>>::launch,                                                    \
      ::kpa::mfma::Entry<::kpa::mfma::Cfg<__VA_ARGS__>>::blocks_per_cu,                                             \
      ::kpa::mfma::Entry<::kpa::mfma::Cfg<__VA_ARGS__>>::lds}
@@ -1202,7 +1222,7 @@ struct Entry {
 // Generic family: QF, rank caps (key, value), row-block cap MB32, queries per
 // wave, query subgroups, waves per SIMD, waves per workgroup cap.
 #define KPA_MFMA_GENERIC(multi, QF, RKC, RVC, MB32, NQW, NQG, MW, WMAX)                                       \
-    {true, 0, 0, 0, 0, 0, 0, QF, RKC, RVC, 32 * (MB32), multi, NQW, NQG, WMAX,                                   \
+    {true, 0, 0, 0, 0, 0, 0, QF, RKC, RVC, 32 * (MB32), multi, NQW, NQG, WMAX, 100,                              \
      ::kpa::mfma::Entry<::kpa::mfma::GenCfg<QF, RKC, RVC, MB32, NQW, NQG, MW, WMAX>>::launch,                    \
      ::kpa::mfma::Entry<::kpa::mfma::GenCfg<QF, RKC, RVC, MB32, NQW, NQG, MW, WMAX>>::blocks_per_cu,             \
      ::kpa::mfma::Entry<::kpa::mfma::GenCfg<QF, RKC, RVC, MB32, NQW, NQG, MW, WMAX>>::lds}

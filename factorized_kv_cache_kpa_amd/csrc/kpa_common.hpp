@@ -215,6 +215,7 @@ hipError_t launch_stream_xor(const void* buf, int64_t bytes, uint32_t* partial, 
 hipError_t launch_decode_mfma(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);
 bool decode_mfma_supported(const kpa_dims& d, int n_q);
 int decode_mfma_blocks_per_cu(const kpa_dims& d, int n_q);
+int decode_mfma_fill_pct(const kpa_dims& d, int n_q);  // percent of the resident slots the planner fills
 int decode_valu_blocks_per_cu(const kpa_dims& d);
 int decode_mfma_query_groups(const kpa_dims& d, int n_q);
 // Multi-query decode with K and V rebuilt per tile on the matrix cores

@@ -69,7 +69,9 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
         const int64_t per_cu = rebuild ? decode_rebuild_blocks_per_cu(d)
                                : mfma  ? decode_mfma_blocks_per_cu(d, n_q)
                                        : decode_valu_blocks_per_cu(d);
-        const int64_t target = per_cu * cus;
+        // (a tuned matrix-core kernel may ask for a fraction of them)
+        const int64_t fill = mfma ? decode_mfma_fill_pct(d, n_q) : 100;
+        const int64_t target = std::max<int64_t>(1, per_cu * cus * fill / 100);
         // workgroups per chunk: one per query group (matrix cores; the
         // rebuild kernel also one per A head), one per query (VALU)
         const int64_t wg_rows = rebuild ? (int64_t)batch * d.p1 * decode_rebuild_query_groups(n_q)
