@@ -48,20 +48,39 @@ def test_decode_rank_one_kpa(gpu_lib):
     assert_close(go, gl, ro, rl, cfg.dtype, "rank one", scale=scale_of(inp))
 
 
-def test_garbage_past_the_context_is_ignored(gpu_lib):
+def _headsplit(p1, p2):
+    from workloads import headsplit_config
+    return headsplit_config(p1, p2, 2, 256)
+
+
+NAN_CASES = [
+    # config, ctx (the last tile holds ctx % 32 slots), n_q, forced chunks
+    ("kpa_32k", 100, 1, 0),
+    ("long_512k", 101, 1, 0),    # strided chunks, the weights folded on the matrix cores
+    ("long_512k", 197, 1, 2),    # ... two strided chunks: tiles 0, 2, 4 and 1, 3, 5
+    ("tpa_degenerate", 99, 1, 0),  # the weights folded on the vector ALU (G feature dimension 1)
+    ("split_5x5", 71, 1, 0),     # 8-wide F, padded rows
+    ("split_4x5", 125, 1, 3),
+    ("multiq_16", 77, 3, 0),     # several queries per workgroup (factor-space kernel)
+]
+
+
+@pytest.mark.parametrize("name,ctx,n_q,num_splits", NAN_CASES)
+def test_garbage_past_the_context_is_ignored(gpu_lib, name, ctx, n_q, num_splits):
     # slots past ctx_len hold NaN bit patterns; the result must not see them
-    cfg = CONFIGS["kpa_32k"]
-    inp = make_inputs(cfg, seed=13, batch=2, ctx=100)
+    cfg = _headsplit(*(int(x) for x in name[6:].split("x"))) if name.startswith("split_") else CONFIGS[name]
+    inp = make_inputs(cfg, seed=13, batch=2, ctx=ctx, n_q=n_q)
     dims = dims_of(cfg)
-    cap = 128
+    cap = (ctx + 31) // 32 * 32 + 32
     nan_cache = kpa.alloc_cache(dims, 2, cap)
     nan_cache.fill_(0xFF)
     kpa.kpa_cache_append(dims, nan_cache, 2, cap, inp.a_k.cuda(), inp.b_k.cuda(), inp.a_v.cuda(), inp.b_v.cuda(),
-                         inp.positions.cuda(), torch.zeros(2, dtype=torch.int32, device="cuda"), n_new=100)
+                         inp.positions.cuda(), torch.zeros(2, dtype=torch.int32, device="cuda"), n_new=ctx)
     torch.cuda.synchronize()
-    go, gl = run_decode(inp, dims, nan_cache, cap, max_ctx=cap)
+    go, gl = run_decode(inp, dims, nan_cache, cap, max_ctx=cap, num_splits=num_splits)
     ro, rl = _oracle(inp)
-    assert_close(go, gl, ro, rl, cfg.dtype, "NaN past the context", scale=scale_of(inp))
+    assert_close(go, gl, ro, rl, cfg.dtype, f"{name}: NaN past the context", scale=scale_of(inp),
+                 path=kpa.kpa_decode_path(dims, n_q))
 
 
 @pytest.mark.parametrize("name,batch,ctx,n_q,ragged,q_scale", SMALL)
