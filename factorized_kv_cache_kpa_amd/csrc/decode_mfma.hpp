@@ -1035,9 +1035,10 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
     }
     // Fused append (kpa_append_decode, single-query kernels; the host runs
     // the append kernel first for the others): each new token is written by
-    // the workgroup of the chunk whose tiles hold it before it reads it.  The slot0 value arrives behind the first
-    // tile's G blocks (loads complete in order), so workgroups owning no token
-    // wait here for what the tile loop's first wait would wait for anyway.
+    // the workgroup of the chunk whose tiles hold it before it reads it.  The
+    // slot0 value arrives behind the first tile's G blocks (loads complete in
+    // order), so workgroups owning no token wait here for what the tile
+    // loop's first wait would wait for anyway.
     // The owner writes its tokens and waits for the stores, all before the
     // next tile's loads are issued; for a token in the first tile it fetches
     // that tile again (the loop's first wait covers it).
