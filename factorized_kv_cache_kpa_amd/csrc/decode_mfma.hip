@@ -21,6 +21,15 @@ const MfmaKernel* exact_kernels(int* count) {
         // chunks (-> 128.9 us; 136.9 -> 128.5-130.3 us for the two together,
         // A/B on one box)
         KPA_MFMA_ENTRY(8, 4, 8, 16, 2, 4, false, 8, 8, 4, 16, 2, 4, true, 1, 1, 2, 1, 90, true),
+        // several queries per sequence on kpa_32k's and long_512k's shapes
+        // (the generic family they fell to runs one 2-query workgroup per CU;
+        // 8 x 16400 tokens, A/B): kpa_32k's with 4 queries per wave, 16
+        // queries 985 -> 110-119 us, 4 queries 138 -> 41 us, 2 queries 78 ->
+        // 38 us; long_512k's with 2 queries per wave and 2 query subgroups
+        // (4 sequences for 4 queries), 16 queries 2250 -> 274-283 us, 4
+        // queries 170 -> 52 us
+        KPA_MFMA_ENTRY(4, 4, 8, 16, 2, 2, true, 4, 8, 4, 16, 2, 2, true, 4, 1, 2),
+        KPA_MFMA_ENTRY(8, 4, 8, 16, 2, 4, true, 8, 8, 4, 16, 2, 4, true, 2, 2, 1),
         KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, false, 8, 8, 4, 16, 4, 4, false, 1, 1, 1),
         KPA_MFMA_ENTRY(4, 8, 16, 8, 4, 4, true, 8, 8, 4, 16, 4, 4, false, 2, 2, 2),
         // TPA split (A: h x 1, B: 1 x d_h): G = A with feature dimension 1, F = B

@@ -125,6 +125,34 @@ def test_non_causal_multi_query(gpu_lib):
     assert_close(go, gl, ro, rl, cfg.dtype, "non-causal", scale=scale_of(inp))
 
 
+MULTI_CASES = [
+    # config (its shape), batch, ctx, n_q, ragged, causal, forced chunks
+    ("kpa_32k", 3, 700, 2, True, True, 0),
+    ("kpa_32k", 2, 1000, 5, False, True, 7),
+    ("kpa_32k", 2, 530, 16, True, True, 0),
+    ("kpa_32k", 2, 300, 9, False, False, 0),
+    ("long_512k", 2, 650, 3, True, True, 0),
+    ("long_512k", 1, 1100, 16, False, True, 5),
+    ("long_512k", 2, 260, 6, True, False, 0),
+]
+
+
+@pytest.mark.parametrize("name,batch,ctx,n_q,ragged,causal,num_splits", MULTI_CASES)
+def test_multi_query_on_the_single_query_shapes(gpu_lib, name, batch, ctx, n_q, ragged, causal, num_splits):
+    """Several queries per sequence on kpa_32k's and long_512k's head and
+    feature splits (their tuned multi-query matrix-core kernels): every
+    output element against the oracle, query counts that leave a query group
+    partly filled, causal and not, automatic and forced chunk counts."""
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, seed=31, batch=batch, ctx=ctx, n_q=n_q, ragged=ragged)
+    dims = dims_of(cfg)
+    assert kpa.kpa_decode_path(dims, n_q) == "mfma_bf16"
+    cache, cap = fill_cache(inp, dims)
+    go, gl = run_decode(inp, dims, cache, cap, causal=causal, num_splits=num_splits)
+    ro, rl = _oracle(inp, causal=causal)
+    assert_close(go, gl, ro, rl, cfg.dtype, f"{name} n_q={n_q}", scale=scale_of(inp))
+
+
 def test_multi_query_row_equals_truncated_single_query(gpu_lib):
     cfg = CONFIGS["multiq_16"]
     inp = make_inputs(cfg, seed=8, batch=2, ctx=200, n_q=4)
