@@ -459,10 +459,15 @@ __global__ void __launch_bounds__(S::WAVES_MAX * 64, S::MIN_WAVES) decode_mfma_k
     const int l16 = lane & 15;
     const int g16 = lane >> 4;     // 8-slot group for the value side
     const int b = blockIdx.y;
-    // workgroup -> (chunk, query group): the query groups of a chunk share an XCD
+    // workgroup -> (chunk, query group): the query groups of a chunk share an
+    // XCD (blockIdx.x mod 8 -- the row's part of the linear index is a
+    // multiple of 8); chunk k of sequence b goes to XCD (b n_split + k) mod
+    // 8, so that when n_split is not a multiple of 8 the grid's padding
+    // spreads over the XCDs instead of idling the same ones in every row
     const int qwg_count = (P.n_q + S::QPW - 1) / S::QPW;
     const int bx = blockIdx.x;
-    const int split = (bx / (kXcds * qwg_count)) * kXcds + bx % kXcds;
+    const int xcd_off = (int)(((int64_t)b * P.n_split) % kXcds);
+    const int split = (bx / (kXcds * qwg_count)) * kXcds + (bx % kXcds - xcd_off + kXcds) % kXcds;
     const int qwg = (bx / kXcds) % qwg_count;
     if (split >= P.n_split) return;  // padding of the grid to a multiple of the XCD count
     const Layout& L = P.L;

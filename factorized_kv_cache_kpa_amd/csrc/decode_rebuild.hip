@@ -56,7 +56,14 @@
 // ranks up to 4 (missing ranks are zero rows of the inner dimension), B head
 // count p2 = 2, 4, 6 or 8 (two waves each), any A head count p1 (one
 // workgroup each), up to 16 queries per workgroup (more queries: more
-// workgroups per chunk).
+// workgroups per chunk).  Swapped (SW): q1 = 8, q2 = 16 with p1 = 8 (the
+// kernel's 16-wave layout; long_512k's split).  B (x) A is A (x) B with
+// heads and features permuted, so the
+// kernel runs with the cache's B factors in the A role and its A factors
+// in the B role: head (i1, i2) is the kernel's (i2, i1) and feature
+// (j1, j2) its (j2, j1).  Only the query's rotary pairs (now along the
+// kernel's 16-wide dimension) and the addresses of the query, the output
+// and the factor sets change.
 //
 // Precision: bf16 factors exactly; the rebuilt K and V rows, the rotated
 // query and the softmax weights are each rounded once to bf16 (relative 2^-8
@@ -95,8 +102,8 @@ struct Lds {
     static constexpr int AV = BK + kTileSlots * B_ROW;   // [j1][slot]
     static constexpr int BV = AV + kQ1 * V_ROW;          // [i2 q2 + j2][slot]
     static constexpr int TILE = BV + P2 * kQ2 * V_ROW;
-    // two tile buffers and the rotary cos/sin [16 queries][4 pairs][2]
-    static constexpr int TOTAL = 2 * TILE + kNQ * 4 * 2 * 4;
+    // two tile buffers and the rotary cos/sin [16 queries][up to 8 pairs][2]
+    static constexpr int TOTAL = 2 * TILE + kNQ * 8 * 2 * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS of one CU");
 };
 
@@ -139,9 +146,11 @@ struct Cfg {
 // chunks (one per rank, consecutive ranks a fixed stride apart; zero for
 // ranks past R) and where their 64 interleaved bytes go in LDS.  A unit's
 // kind is the same across a wave (kinds start at multiples of 64 units).
-template <int P2>
+template <int P2, bool SW>
 struct Stage {
     using C = Cfg<P2>;
+    // the cache's factor sets in the kernel's roles (A^K, B~^K, A^V, B^V)
+    static constexpr int kSetAK = SW ? 1 : 0, kSetBK = SW ? 0 : 1, kSetAV = SW ? 3 : 2, kSetBV = SW ? 2 : 3;
     enum { kBK = 0, kBV = 1, kAK = 2, kAV = 3, kNone = 4 };
     u32x4 v[C::UPT][4];
     uint32_t src[C::UPT];  // byte offset of rank 0 in the tile
@@ -159,28 +168,28 @@ struct Stage {
                 const int s = u % kTileSlots, i2 = u / kTileSlots;
                 kd = kBK;
                 slot[k] = s;
-                src[k] = (uint32_t)(L.off[1] + i2 * (kTileSlots * 16) + s * 16);
+                src[k] = (uint32_t)(L.off[kSetBK] + i2 * (kTileSlots * 16) + s * 16);
                 dst[k] = LY::BK + s * LY::B_ROW + i2 * 64;
             } else if (u < C::U_BK + C::U_BV) {  // B^V element (r P2 + i2) q2 + j2, 8 slots
                 const int x = u - C::U_BK;
                 const int sg = x & 3, e = x >> 2;
                 kd = kBV;
                 slot[k] = 8 * sg;
-                src[k] = (uint32_t)(L.off[3] + e * 64 + sg * 16);
+                src[k] = (uint32_t)(L.off[kSetBV] + e * 64 + sg * 16);
                 dst[k] = LY::BV + e * LY::V_ROW + 64 * sg;
             } else if (u < C::U_BK + C::U_BV + C::U_AK) {  // A^K chunk (r p1 + i1) 2 + hf of slot s
                 const int x = u - C::U_BK - C::U_BV;
                 const int s = x % kTileSlots, hf = x / kTileSlots;
                 kd = kAK;
                 slot[k] = s;
-                src[k] = (uint32_t)(L.off[0] + (i1 * 2 + hf) * (kTileSlots * 16) + s * 16);
+                src[k] = (uint32_t)(L.off[kSetAK] + (i1 * 2 + hf) * (kTileSlots * 16) + s * 16);
                 dst[k] = LY::AK + s * LY::A_ROW + hf * 64;
             } else if (u < C::UNITS) {  // A^V element (r p1 + i1) q1 + j1, 8 slots
                 const int x = u - C::U_BK - C::U_BV - C::U_AK;
                 const int sg = x & 3, j1 = x >> 2;
                 kd = kAV;
                 slot[k] = 8 * sg;
-                src[k] = (uint32_t)(L.off[2] + (i1 * kQ1 + j1) * 64 + sg * 16);
+                src[k] = (uint32_t)(L.off[kSetAV] + (i1 * kQ1 + j1) * 64 + sg * 16);
                 dst[k] = LY::AV + j1 * LY::V_ROW + 64 * sg;
             } else {
                 kd = kNone;
@@ -264,29 +273,33 @@ __device__ __forceinline__ s16x4 lds8(const uint8_t* p) {
     return __builtin_bit_cast(s16x4, *reinterpret_cast<const uint2*>(p));
 }
 
-template <int P2>
+template <int P2, bool SW>
 __global__ void __launch_bounds__(2 * P2 * 64, 1) decode_rebuild_kernel(DecodeParams P) {
     using LY = Lds<P2>;
+    constexpr int NP = SW ? kQ1 / 2 : kQ2 / 2;  // rotary pairs along the kernel's A (SW) or B features
     // separate LDS objects, so that the compiler can tell the rebuilt keys
     // (written per tile) from the tile factors (read around those writes)
     __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * LY::TILE];
-    __shared__ float cs[kNQ * 4 * 2];
+    __shared__ float cs[kNQ * NP * 2];
     const int lane = threadIdx.x & 63;
     const int wave = (int)(threadIdx.x >> 6);
     const int i2 = wave % P2;   // this wave's B head
     const int hh = wave / P2;   // and its half of every tile: slots 16 hh .. 16 hh + 15
-    const int p1 = P.d.p1;
+    const int p1 = SW ? P.d.p2 : P.d.p1;  // the kernel's A heads: one workgroup each
     const int H = p1 * P2;
-    // workgroup -> (chunk, A head): the head groups of a chunk share an XCD,
-    // so the B factors they all read come from HBM once
+    // workgroup -> (chunk, A head): the head groups (and query groups) of a
+    // chunk share an XCD, so the B factors they all read come from HBM once;
+    // chunk k of sequence b goes to XCD (b n_split + k) mod 8, so the grid's
+    // padding (n_split not a multiple of 8) spreads over the XCDs
     const int bx = blockIdx.x;
-    const int split = (bx / (kXcds * p1)) * kXcds + bx % kXcds;
-    const int i1 = (bx / kXcds) % p1;
     const int b = blockIdx.y;
+    const int xcd_off = (int)(((int64_t)b * P.n_split) % kXcds);
+    const int split = (bx / (kXcds * p1)) * kXcds + (bx % kXcds - xcd_off + kXcds) % kXcds;
+    const int i1 = (bx / kXcds) % p1;
     const int qg = blockIdx.z;  // group of 16 queries
     if (split >= P.n_split) return;
     const Layout& L = P.L;
-    const int head = i1 * P2 + i2;
+    const int head = SW ? i2 * p1 + i1 : i1 * P2 + i2;  // in the cache's head order
 
     // queries of this workgroup: n = 16 qg + (lane & 15)
     const int ql = lane & 15;
@@ -299,19 +312,19 @@ __global__ void __launch_bounds__(2 * P2 * 64, 1) decode_rebuild_kernel(DecodePa
     const int last = min(first + P.chunk_tiles * kTileSlots, vis_max);
     const uint8_t* seq = P.cache + (int64_t)b * L.n_tiles * L.tile_bytes;
 
-    Stage<P2> stage;
+    Stage<P2, SW> stage;
     stage.init(L, i1, p1);
     if (first < last) stage.load(seq + (int64_t)(first / kTileSlots) * L.tile_bytes, p1, P.d.r_k, P.d.r_v);
 
     // ---- rotated, scaled query as the score MFMA's B operand (bf16) --------
-    if (threadIdx.x < kNQ * 4) {
-        const int nq = threadIdx.x >> 2, m = threadIdx.x & 3;
+    if (threadIdx.x < kNQ * NP) {
+        const int nq = threadIdx.x / NP, m = threadIdx.x % NP;
         const int nn = min(qg * kNQ + nq, P.n_q - 1);
-        const double theta = exp2(-(2.0 * m / kQ2) * log2((double)P.d.rope_base));
+        const double theta = exp2(-(2.0 * m / (2 * NP)) * log2((double)P.d.rope_base));
         double sn, c;
         sincos((double)P.q_pos[(int64_t)b * P.n_q + nn] * theta, &sn, &c);
-        cs[(nq * 4 + m) * 2] = (float)c;
-        cs[(nq * 4 + m) * 2 + 1] = (float)sn;
+        cs[(nq * NP + m) * 2] = (float)c;
+        cs[(nq * NP + m) * 2 + 1] = (float)sn;
     }
     if (i1 == 0)
         for (int k = 0; k < kNQ; ++k)
@@ -324,26 +337,51 @@ __global__ void __launch_bounds__(2 * P2 * 64, 1) decode_rebuild_kernel(DecodePa
         for (int ks = 0; ks < 4; ++ks) {
             const int j1 = 4 * ks + (lane >> 4);
             float x[8];
-            if (P.a_q == nullptr) {
-                const float* src = P.q + (row * H + head) * kDH + j1 * kQ2;
-                const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-                const f32x4 c = *reinterpret_cast<const f32x4*>(src + 4);
+            float v[8];
+            if constexpr (!SW) {
+                // features j1 q2 + 0 .. 7: contiguous, the rotary pairs inside
+                if (P.a_q == nullptr) {
+                    const float* src = P.q + (row * H + head) * kDH + j1 * kQ2;
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+                    const f32x4 c = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    x[k] = a[k];
-                    x[4 + k] = c[k];
+                    for (int k = 0; k < 4; ++k) {
+                        x[k] = a[k];
+                        x[4 + k] = c[k];
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) x[k] = query_elem(P, row, head, j1 * kQ2 + k);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float c = cs[(ql * NP + m) * 2], sn = cs[(ql * NP + m) * 2 + 1];
+                    const float x0 = x[2 * m], x1 = x[2 * m + 1];
+                    v[2 * m] = q_ok ? (x0 * c - x1 * sn) * P.q_scale : 0.f;
+                    v[2 * m + 1] = q_ok ? (x1 * c + x0 * sn) * P.q_scale : 0.f;
                 }
             } else {
+                // features k q2 + j1 (k = 0 .. 7) of the cache's order, q2 = 16;
+                // the rotary partner of each is k q2 + (j1 ^ 1)
+                float y[8];
 #pragma unroll
-                for (int k = 0; k < 8; ++k) x[k] = query_elem(P, row, head, j1 * kQ2 + k);
-            }
-            float v[8];
+                for (int k = 0; k < 8; ++k) {
+                    const int f = k * kQ1 + j1, g = k * kQ1 + (j1 ^ 1);
+                    if (P.a_q == nullptr) {
+                        x[k] = P.q[(row * H + head) * kDH + f];
+                        y[k] = P.q[(row * H + head) * kDH + g];
+                    } else {
+                        x[k] = query_elem(P, row, head, f);
+                        y[k] = query_elem(P, row, head, g);
+                    }
+                }
+                const float c = cs[(ql * NP + (j1 >> 1)) * 2], sn = cs[(ql * NP + (j1 >> 1)) * 2 + 1];
+                const bool first_of_pair = (j1 & 1) == 0;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float c = cs[(ql * 4 + m) * 2], sn = cs[(ql * 4 + m) * 2 + 1];
-                const float x0 = x[2 * m], x1 = x[2 * m + 1];
-                v[2 * m] = q_ok ? (x0 * c - x1 * sn) * P.q_scale : 0.f;
-                v[2 * m + 1] = q_ok ? (x1 * c + x0 * sn) * P.q_scale : 0.f;
+                for (int k = 0; k < 8; ++k) {
+                    const float r = first_of_pair ? (x[k] * c - y[k] * sn) : (x[k] * c + y[k] * sn);
+                    v[k] = q_ok ? r * P.q_scale : 0.f;
+                }
             }
             q_hi[ks] = pack_bf16x8(v);
         }
@@ -542,12 +580,17 @@ __global__ void __launch_bounds__(2 * P2 * 64, 1) decode_rebuild_kernel(DecodePa
             const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
             for (int j = 0; j < kQ2; ++j) v[j] = l_run > 0.f ? v[j] * inv : 0.f;
-            dst = P.out + (row * H + head) * kDH + j1 * kQ2;
+            dst = P.out + (row * H + head) * kDH;
         } else {
-            dst = P.part_o + ((row * P.n_split + split) * H + head) * kDH + j1 * kQ2;
+            dst = P.part_o + ((row * P.n_split + split) * H + head) * kDH;
         }
-        *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        if constexpr (!SW) {
+            *reinterpret_cast<f32x4*>(dst + j1 * kQ2) = f32x4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4*>(dst + j1 * kQ2 + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        } else {
+#pragma unroll
+            for (int j = 0; j < kQ2; ++j) dst[j * kQ1 + j1] = v[j];  // feature (j, j1) of the cache's order
+        }
     }
     if (t8 == 0) {
         if (P.n_split == 1) {
@@ -564,18 +607,19 @@ __global__ void __launch_bounds__(2 * P2 * 64, 1) decode_rebuild_kernel(DecodePa
 // Host side
 // ---------------------------------------------------------------------------
 struct Kernel {
-    int p2;
+    int p2;   // the kernel's B heads
+    bool sw;  // the factors' roles swapped
     hipError_t (*launch)(const DecodeParams&, hipStream_t, const KernelEvents&);
     int (*blocks_per_cu)();
 };
 
-template <int P2>
+template <int P2, bool SW>
 struct Entry {
     static hipError_t launch(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
         const int split_pad = (P.n_split + kXcds - 1) / kXcds * kXcds;
         const int qgroups = (P.n_q + kNQ - 1) / kNQ;
-        dim3 grid(split_pad * P.d.p1, P.batch, qgroups);
-        hipExtLaunchKernelGGL(decode_rebuild_kernel<P2>, grid, dim3(2 * P2 * 64), 0, s, ev.start,
+        dim3 grid(split_pad * (SW ? P.d.p2 : P.d.p1), P.batch, qgroups);
+        hipExtLaunchKernelGGL((decode_rebuild_kernel<P2, SW>), grid, dim3(2 * P2 * 64), 0, s, ev.start,
                               ev.stop, 0, P);
         return hipGetLastError();
     }
@@ -584,7 +628,7 @@ struct Entry {
         int v = cached.load(std::memory_order_relaxed);
         if (v > 0) return v;
         int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_rebuild_kernel<P2>, 2 * P2 * 64, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, decode_rebuild_kernel<P2, SW>, 2 * P2 * 64, 0) != hipSuccess ||
             nb <= 0)
             nb = 1;
         cached.store(nb, std::memory_order_relaxed);
@@ -592,26 +636,40 @@ struct Entry {
     }
 };
 
-#define KPA_REBUILD_ENTRY(p2) {p2, Entry<p2>::launch, Entry<p2>::blocks_per_cu}
+#define KPA_REBUILD_ENTRY(p2, sw) {p2, sw, Entry<p2, sw>::launch, Entry<p2, sw>::blocks_per_cu}
 
+// The kernel for a shape: q1 = 16, q2 = 8 as they are (B heads p2), or q1 =
+// 8, q2 = 16 with the factors' roles swapped (the kernel's B heads are p1).
+// Swapped, only p1 = 8 is instantiated: with fewer heads in the kernel's B
+// role a workgroup has fewer than 16 waves, and the factor-space kernel was
+// as fast or faster on kpa_32k's split (p1 = 4; 8 x 16400 tokens, 16
+// queries: 99.7 against 103.8 us, 8 queries 92.1 against 60.9, 32
+// sequences x 4096 tokens 370.7 against 188.3).
 const Kernel* find(const kpa_dims& d) {
     static const Kernel tab[] = {
-        KPA_REBUILD_ENTRY(2), KPA_REBUILD_ENTRY(4), KPA_REBUILD_ENTRY(6), KPA_REBUILD_ENTRY(8),
+        KPA_REBUILD_ENTRY(2, false), KPA_REBUILD_ENTRY(4, false), KPA_REBUILD_ENTRY(6, false),
+        KPA_REBUILD_ENTRY(8, false), KPA_REBUILD_ENTRY(8, true),
     };
     if (d.r_k > 4 || d.r_v > 4) return nullptr;
+    bool sw;
+    if (d.q1 == kQ1 && d.q2 == kQ2) sw = false;
+    else if (d.q1 == kQ2 && d.q2 == kQ1) sw = true;
+    else return nullptr;
+    const int p2 = sw ? d.p1 : d.p2;
     for (const Kernel& k : tab)
-        if (k.p2 == d.p2) return &k;
+        if (k.sw == sw && k.p2 == p2) return &k;
     return nullptr;
 }
 
 }  // namespace rebuild
 
-// The rebuild kernel serves bf16 caches with q1 = 16, q2 = 8, p2 = 2, 4, 6
-// or 8, ranks up to 4 and at least kRebuildMinQ queries per sequence.
+// The rebuild kernel serves bf16 caches with ranks up to 4 and either q1 =
+// 16, q2 = 8, p2 = 2, 4, 6 or 8 and at least kRebuildMinQ queries per
+// sequence, or q1 = 8, q2 = 16, p1 = 8 and at least kRebuildMinQSwapped.
 bool decode_rebuild_supported(const kpa_dims& d, int n_q) {
-    if (d.dtype != KPA_BF16 || n_q < kRebuildMinQ) return false;
-    if (d.q1 != rebuild::kQ1 || d.q2 != rebuild::kQ2) return false;
-    return rebuild::find(d) != nullptr;
+    if (d.dtype != KPA_BF16) return false;
+    const rebuild::Kernel* k = rebuild::find(d);
+    return k != nullptr && n_q >= (k->sw ? kRebuildMinQSwapped : kRebuildMinQ);
 }
 
 int decode_rebuild_blocks_per_cu(const kpa_dims& d) {
@@ -621,9 +679,16 @@ int decode_rebuild_blocks_per_cu(const kpa_dims& d) {
 
 int decode_rebuild_query_groups(int n_q) { return (n_q + rebuild::kNQ - 1) / rebuild::kNQ; }
 
+// Workgroups per chunk and query group: one per head of the factor in the
+// kernel's A role.
+int decode_rebuild_head_groups(const kpa_dims& d) {
+    const rebuild::Kernel* k = rebuild::find(d);
+    return k && k->sw ? d.p2 : d.p1;
+}
+
 hipError_t launch_decode_rebuild(const DecodeParams& P, hipStream_t s, const KernelEvents& ev) {
     const rebuild::Kernel* k = rebuild::find(P.d);
-    if (!k || P.d.q1 != rebuild::kQ1 || P.d.q2 != rebuild::kQ2) return hipErrorInvalidValue;
+    if (!k) return hipErrorInvalidValue;
     return k->launch(P, s, ev);
 }
 

@@ -221,9 +221,16 @@ int decode_mfma_query_groups(const kpa_dims& d, int n_q);
 // Multi-query decode with K and V rebuilt per tile on the matrix cores
 // (decode_rebuild.hip): taken from kRebuildMinQ queries per sequence.
 constexpr int kRebuildMinQ = 8;
+// With the factors' roles swapped (q1 = 8, q2 = 16, p1 = 8): from 12.  A
+// query group is 16 wide, so the rebuild costs about the same from 8 to 16
+// queries while the factor-space kernel's time grows with them: on
+// long_512k's split (8 x 16400 tokens) 8 queries take 137.0 us there
+// against 160.9 rebuilt, 16 queries 250.4 against 175.3.
+constexpr int kRebuildMinQSwapped = 12;
 hipError_t launch_decode_rebuild(const DecodeParams& P, hipStream_t s, const KernelEvents& ev);
 bool decode_rebuild_supported(const kpa_dims& d, int n_q);
 int decode_rebuild_blocks_per_cu(const kpa_dims& d);
+int decode_rebuild_head_groups(const kpa_dims& d);  // workgroups per chunk and query group
 int decode_rebuild_query_groups(int n_q);
 
 }  // namespace kpa

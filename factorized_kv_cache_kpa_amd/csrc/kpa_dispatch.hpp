@@ -74,7 +74,7 @@ inline Plan plan_decode(const kpa_dims& d, int32_t batch, int32_t max_ctx, int32
         const int64_t target = std::max<int64_t>(1, per_cu * cus * fill / 100);
         // workgroups per chunk: one per query group (matrix cores; the
         // rebuild kernel also one per A head), one per query (VALU)
-        const int64_t wg_rows = rebuild ? (int64_t)batch * d.p1 * decode_rebuild_query_groups(n_q)
+        const int64_t wg_rows = rebuild ? (int64_t)batch * decode_rebuild_head_groups(d) * decode_rebuild_query_groups(n_q)
                                 : mfma  ? (int64_t)batch * decode_mfma_query_groups(d, n_q)
                                         : rows;
         s = wg_rows > 0 ? (target + wg_rows - 1) / wg_rows : 1;

@@ -357,9 +357,10 @@ const char* kpa_status_string(int status);
  *       and head a sum of R outer products, formed by matrix instructions)
  *       and plain attention over the rebuilt rows (the rebuilt rows, the
  *       rotated query and the softmax weights each rounded once to bf16;
- *       float32 sums).  Taken for bf16 caches with n_q >= 8, q1 = 16,
- *       q2 = 8, p2 = 2, 4, 6 or 8, any p1, R_K <= 4 and R_V <= 4; every
- *       rebuilt row then serves 8-16 queries.
+ *       float32 sums).  Taken for bf16 caches with R_K <= 4, R_V <= 4 and
+ *       either n_q >= 8, q1 = 16, q2 = 8, p2 = 2, 4, 6 or 8, any p1, or
+ *       n_q >= 12, q1 = 8, q2 = 16, p1 = 8, any p2 (the factors' roles
+ *       swapped); every rebuilt row then serves 8-16 queries.
  *   "mfma_bf16": the bf16 matrix cores.  Taken by every other bf16 cache where
  *       one factor -- call it F -- has a feature dimension of 8, 16, 32 or 64
  *       (contracted on the matrix cores) and

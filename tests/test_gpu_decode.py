@@ -134,23 +134,27 @@ MULTI_CASES = [
     ("long_512k", 2, 650, 3, True, True, 0),
     ("long_512k", 1, 1100, 16, False, True, 5),
     ("long_512k", 2, 260, 6, True, False, 0),
+    ("long_512k", 2, 400, 9, True, True, 0),
+    ("long_512k", 2, 480, 12, True, False, 3),
 ]
 
 
 @pytest.mark.parametrize("name,batch,ctx,n_q,ragged,causal,num_splits", MULTI_CASES)
 def test_multi_query_on_the_single_query_shapes(gpu_lib, name, batch, ctx, n_q, ragged, causal, num_splits):
     """Several queries per sequence on kpa_32k's and long_512k's head and
-    feature splits (their tuned multi-query matrix-core kernels): every
-    output element against the oracle, query counts that leave a query group
-    partly filled, causal and not, automatic and forced chunk counts."""
+    feature splits (tuned multi-query matrix-core kernels; on long_512k's
+    split K and V rebuilt per tile from 12 queries): every output element
+    against the oracle, query counts that leave a query group partly filled,
+    causal and not, automatic and forced chunk counts."""
     cfg = CONFIGS[name]
     inp = make_inputs(cfg, seed=31, batch=batch, ctx=ctx, n_q=n_q, ragged=ragged)
     dims = dims_of(cfg)
-    assert kpa.kpa_decode_path(dims, n_q) == "mfma_bf16"
+    path = kpa.kpa_decode_path(dims, n_q)
+    assert path == ("mfma_rebuild" if name == "long_512k" and n_q >= 12 else "mfma_bf16")
     cache, cap = fill_cache(inp, dims)
     go, gl = run_decode(inp, dims, cache, cap, causal=causal, num_splits=num_splits)
     ro, rl = _oracle(inp, causal=causal)
-    assert_close(go, gl, ro, rl, cfg.dtype, f"{name} n_q={n_q}", scale=scale_of(inp))
+    assert_close(go, gl, ro, rl, cfg.dtype, f"{name} n_q={n_q}", scale=scale_of(inp), path=path)
 
 
 def test_multi_query_row_equals_truncated_single_query(gpu_lib):

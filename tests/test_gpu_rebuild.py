@@ -9,8 +9,10 @@ workgroup each), ranks 1..4 for keys and values independently, 8..64
 queries (one or several groups of 16 per sequence), causal and non-causal,
 ragged contexts over several tiles with a ragged tail, one chunk (direct
 output) and several (the merge), sharp softmaxes, a factored query, NaN
-bytes past the context, and an empty sequence.  Every output element is
-compared.
+bytes past the context, and an empty sequence.  The same kernel with the
+factors' roles swapped serves q1 = 8, q2 = 16 with p1 = 8 (long_512k's
+split): its cases span B head counts 1 / 3 / 4 (the kernel's A role) and
+12..40 queries.  Every output element is compared.
 """
 import numpy as np
 import pytest
@@ -24,10 +26,11 @@ from workloads import CONFIGS, make_inputs, make_query_factors
 pytestmark = pytest.mark.gpu
 
 BASE = CONFIGS["multiq_16"]
+SWAPPED = CONFIGS["long_512k"]  # q1 = 8, q2 = 16, p1 = 8
 
 
-def _cfg(p1, p2, r_k, r_v):
-    return BASE.scaled(name=f"rebuild_{p1}x{p2}_r{r_k}{r_v}", p1=p1, p2=p2, r_k=r_k, r_v=r_v)
+def _cfg(p1, p2, r_k, r_v, base=BASE):
+    return base.scaled(name=f"rebuild_{p1}x{p2}_q{base.q1}x{base.q2}_r{r_k}{r_v}", p1=p1, p2=p2, r_k=r_k, r_v=r_v)
 
 
 def _oracle(inp, causal=True, q=None):
@@ -51,10 +54,19 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "p{}x{}_r{}{}_b{}_s{}_q{}_{}_{}_x{}_ns{}".format(*c))
-def test_rebuild_matches_oracle(gpu_lib, case):
+SWAPPED_CASES = [
+    # p1, p2, r_k, r_v, batch, ctx, n_q, ragged, causal, q_scale, num_splits  (q1 = 8, q2 = 16)
+    (8, 4, 2, 4, 2, 520, 16, True, True, 1.0, 0),     # long_512k's split
+    (8, 4, 2, 4, 2, 520, 16, True, True, 1.0, 1),     # one chunk: the kernel writes the output
+    (8, 4, 2, 4, 1, 300, 40, False, True, 2.0, 3),    # three query groups, the last 8 wide
+    (8, 3, 1, 3, 2, 333, 12, True, True, 4.0, 5),     # three B heads, sharp softmax
+    (8, 1, 4, 1, 2, 410, 13, True, False, 1.0, 0),    # one B head, non-causal
+]
+
+
+def _check_rebuild(case, base):
     p1, p2, r_k, r_v, batch, ctx, n_q, ragged, causal, q_scale, ns = case
-    cfg = _cfg(p1, p2, r_k, r_v)
+    cfg = _cfg(p1, p2, r_k, r_v, base)
     dims = dims_of(cfg)
     assert kpa.kpa_decode_path(dims, n_q) == "mfma_rebuild"
     inp = make_inputs(cfg, seed=41, batch=batch, ctx=ctx, n_q=n_q, ragged=ragged, q_scale=q_scale)
@@ -64,9 +76,24 @@ def test_rebuild_matches_oracle(gpu_lib, case):
     assert_close(go, gl, ro, rl, cfg.dtype, cfg.name, scale=scale_of(inp), path="mfma_rebuild")
 
 
-def test_rebuild_factored_query(gpu_lib):
-    cfg = BASE
+_IDS = lambda c: "p{}x{}_r{}{}_b{}_s{}_q{}_{}_{}_x{}_ns{}".format(*c)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_IDS)
+def test_rebuild_matches_oracle(gpu_lib, case):
+    _check_rebuild(case, BASE)
+
+
+@pytest.mark.parametrize("case", SWAPPED_CASES, ids=_IDS)
+def test_rebuild_swapped_matches_oracle(gpu_lib, case):
+    _check_rebuild(case, SWAPPED)
+
+
+@pytest.mark.parametrize("base", [BASE, SWAPPED], ids=["q16x8", "q8x16"])
+def test_rebuild_factored_query(gpu_lib, base):
+    cfg = base
     dims = dims_of(cfg)
+    assert kpa.kpa_decode_path(dims, 16) == "mfma_rebuild"
     inp = make_inputs(cfg, seed=42, batch=2, ctx=480, n_q=16, ragged=True)
     a_q, b_q = make_query_factors(cfg, 6, seed=42, batch=2, n_q=16)
     cache, cap = fill_cache(inp, dims)
@@ -84,9 +111,11 @@ def test_rebuild_factored_query(gpu_lib):
                  "factored query", scale=scale_of(inp, q=q), path="mfma_rebuild")
 
 
-def test_rebuild_ignores_nan_bytes_past_the_context(gpu_lib):
-    cfg = BASE
+@pytest.mark.parametrize("base", [BASE, SWAPPED], ids=["q16x8", "q8x16"])
+def test_rebuild_ignores_nan_bytes_past_the_context(gpu_lib, base):
+    cfg = base
     dims = dims_of(cfg)
+    assert kpa.kpa_decode_path(dims, 16) == "mfma_rebuild"
     inp = make_inputs(cfg, seed=43, batch=2, ctx=150, n_q=16)
     inp.ctx_len[1] = 90                       # a ragged tail inside a tile
     inp.q_pos[1] = 90 - 16 + torch.arange(16, dtype=torch.int32)

@@ -8,8 +8,9 @@ tuned shapes, or when one factor F has a contracted feature dimension of 8,
 16, 32 or 64 and the other factor G meets the row, rank, head-count and LDS
 conditions of a generic family; everything else (and every float32 cache)
 runs on the vector ALUs.  Several queries per sequence (8 or more) on
-shapes with q1 = 16, q2 = 8, an even p2 up to 8 and ranks up to 4 rebuild K
-and V per tile on the matrix cores instead.
+shapes with q1 = 16, q2 = 8, an even p2 up to 8 and ranks up to 4 -- or,
+from 12 queries, q1 = 8, q2 = 16 and p1 = 8 -- rebuild K and V per tile on
+the matrix cores instead.
 """
 import random
 
@@ -27,7 +28,7 @@ TUNED = {
     (2, 6, 8, 8, 2, 2),
 }
 # tuned shapes with a multi-query kernel of their own
-TUNED_MULTI = {(4, 8, 16, 8, 4, 4)}
+TUNED_MULTI = {(4, 8, 16, 8, 4, 4), (4, 4, 8, 16, 2, 2), (8, 4, 8, 16, 2, 4)}
 
 LDS_BYTES = 160 * 1024
 
@@ -81,7 +82,9 @@ def _generic_ok(pf, qf, pg, qg, r_k, r_v, multi):
 def documented_path(p1, p2, q1, q2, r_k, r_v, n_q):
     multi = n_q > 1
     shape = (p1, p2, q1, q2, r_k, r_v)
-    if n_q >= 8 and q1 == 16 and q2 == 8 and p2 in (2, 4, 6, 8) and r_k <= 4 and r_v <= 4:
+    if r_k <= 4 and r_v <= 4 and (
+            (n_q >= 8 and q1 == 16 and q2 == 8 and p2 in (2, 4, 6, 8))
+            or (n_q >= 12 and q1 == 8 and q2 == 16 and p1 == 8)):
         return "mfma_rebuild"
     if shape in TUNED and (not multi or shape in TUNED_MULTI):
         return "mfma_bf16"
@@ -126,12 +129,14 @@ def test_library_path_matches_the_documented_rule(n_q):
     assert paths == ({"mfma_bf16", "valu", "mfma_rebuild"} if n_q >= 8 else {"mfma_bf16", "valu"})
 
 
-# shapes of the rebuild family and its edges (q1 = 16, q2 = 8)
+# shapes of the rebuild family and its edges (q1 = 16, q2 = 8, and swapped)
 REBUILD_SHAPES = [(p1, p2, 16, 8, rk, rv) for p1 in (1, 3, 4) for p2 in (1, 2, 3, 4, 6, 8, 10)
                   for rk, rv in ((1, 1), (4, 4), (2, 3), (5, 2))]
+REBUILD_SHAPES += [(p1, p2, 8, 16, rk, rv) for p1 in (1, 2, 3, 4, 6, 8, 10) for p2 in (1, 3, 4)
+                   for rk, rv in ((1, 1), (4, 4), (2, 3), (2, 5))]
 
 
-@pytest.mark.parametrize("n_q", [1, 7, 8, 16, 64])
+@pytest.mark.parametrize("n_q", [1, 7, 8, 11, 12, 16, 64])
 def test_rebuild_family_matches_the_documented_rule(n_q):
     for shape in REBUILD_SHAPES:
         assert kpa.kpa_decode_path(kpa.make_dims(*shape), n_q) == documented_path(*shape, n_q), shape
