@@ -44,8 +44,7 @@ const MfmaKernel* exact_kernels(int* count) {
         // factor with fewer heads (fewer waves, more rows per wave), except for
         // 4 x 5, where four waves per workgroup (F = A) spread evenly over a
         // CU's four SIMDs (five waves: 46% -> 62% of 8 TB/s measured), with
-        // registers for three waves per SIMD (61.6 -> 59.6 us) and strided
-        // chunks (54.6-54.8 -> 54.2-54.4 us, A/B twice).  10 x 2, 2 x 10
+        // registers for three waves per SIMD (61.6 -> 59.6 us).  10 x 2, 2 x 10
         // and 6 x 2 split each F head's G heads over two waves, so a CU runs 8
         // (10 x 2: LDS held it to three 2-wave workgroups) and 12 waves instead
         // of 6 and 8 (75.2 -> 69.4, 75.9 -> 72.2, 48.1 -> 47.0 us at 16 x 32768
@@ -54,7 +53,7 @@ const MfmaKernel* exact_kernels(int* count) {
         KPA_MFMA_ENTRY(4, 4, 8, 8, 2, 2, false, 4, 8, 4, 8, 2, 2, true, 1, 1, 3),
         KPA_MFMA_ENTRY(2, 8, 8, 8, 2, 2, false, 8, 8, 2, 8, 2, 2, false, 1, 1, 2),
         KPA_MFMA_ENTRY(10, 2, 8, 8, 2, 2, false, 10, 8, 2, 8, 2, 2, true, 1, 1, 2, 2),
-        KPA_MFMA_ENTRY(4, 5, 8, 8, 2, 2, false, 5, 8, 4, 8, 2, 2, false, 1, 1, 3, 1, 100, true),
+        KPA_MFMA_ENTRY(4, 5, 8, 8, 2, 2, false, 5, 8, 4, 8, 2, 2, false, 1, 1, 3),
         KPA_MFMA_ENTRY(2, 10, 8, 8, 2, 2, false, 10, 8, 2, 8, 2, 2, false, 1, 1, 2, 2),
         KPA_MFMA_ENTRY(5, 5, 8, 8, 2, 2, false, 5, 8, 5, 8, 2, 2, true, 1, 1, 3),
         KPA_MFMA_ENTRY(6, 2, 8, 8, 2, 2, false, 6, 8, 2, 8, 2, 2, true, 1, 1, 3, 2),
