@@ -19,7 +19,7 @@ _lib = None
 def build(force: bool = True) -> str:
     """Compile kpa_oracle.c with gcc (-O2, OpenMP) into oracle/libkpa_oracle.so."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+        tmp = f"{_LIB}.{os.getpid()}.tmp"  # per process: concurrent builds do not collide
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
                                "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
